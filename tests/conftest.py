@@ -1,0 +1,18 @@
+"""Test configuration: the ``gpu`` marker and import paths.
+
+CPU tests (``-m "not gpu"``) cover the oracle against its pins, the host
+logic of the C ABI and the library's exported symbols. GPU tests
+(``-m gpu``) compare the HIP path with the oracle through the C ABI.
+"""
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+TESTS = os.path.dirname(os.path.abspath(__file__))
+for p in (ROOT, TESTS):
+    if p not in sys.path:
+        sys.path.insert(0, p)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")

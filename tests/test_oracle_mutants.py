@@ -1,0 +1,74 @@
+"""Plant plausible mistakes in copies of the oracle and check that the pins
+catch each one (CPU only; the planted copies live in a temporary directory).
+
+A pin set that lets a dropped term, a swapped index or a reversed chain
+through would not be worth trusting; every mutant below must fail at least
+one pin.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "ks_oracle.c")
+
+# (name, exact text in ks_oracle.c, replacement)
+MUTANTS = [
+    ("swap_beta_gamma_in_K",
+     "* b + beta) * c + gamma]", "* c + gamma) * b + beta]"),
+    ("swap_alpha_delta_in_K",
+     "K[(((long long)alpha * d + delta) * b", "K[(((long long)delta * a + alpha) * b"),
+    ("transpose_x_block",
+     "x[((long long)alpha * c + gamma) * d + delta]", "x[((long long)alpha * d + delta) * c + gamma]"),
+    ("transpose_y_block",
+     "y[((long long)alpha * b + beta) * d + delta]", "y[((long long)alpha * d + delta) * b + beta]"),
+    ("drop_last_gamma",
+     "gamma < c; ++gamma", "gamma < c - 1; ++gamma"),
+    ("skip_first_gamma",
+     "int gamma = 0;", "int gamma = 1;"),
+    ("wrong_sign",
+     "acc += k * v;", "acc += (gamma == 1 ? -k : k) * v;"),
+    ("reverse_chain",
+     "ks_factor_row(pat[4 * k], pat[4 * k + 1], pat[4 * k + 2], pat[4 * k + 3],\n                      Ks[k], cur, out);",
+     "ks_factor_row(pat[4 * (nf - 1 - k)], pat[4 * (nf - 1 - k) + 1], pat[4 * (nf - 1 - k) + 2], pat[4 * (nf - 1 - k) + 3],\n                      Ks[nf - 1 - k], cur, out);"),
+]
+
+
+_RUNNER = r"""
+import sys
+sys.path[:0] = [%r, %r]
+import oracle, oracle_pins
+lib = oracle.load(sys.argv[1])
+failed = []
+for pin in oracle_pins.ALL_PINS:
+    try:
+        pin(lib)
+    except (AssertionError, ValueError):
+        failed.append(pin.__name__)
+print("FAILED_PINS", ",".join(failed))
+"""
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    with open(SRC) as f:
+        text = f.read()
+    assert text.count(old) == 1, "mutation site not found: %s" % name
+    src = tmp_path / ("ks_oracle_%s.c" % name)
+    src.write_text(text.replace(old, new))
+    so = str(tmp_path / ("libks_oracle_%s.so" % name))
+    oracle.build(force=True, out=so, src=str(src), extra_flags=["-w"])
+    # A mutant may read or write out of bounds; run it in its own process so
+    # that a corrupted heap cannot reach this one. A crash counts as caught.
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    tests = os.path.dirname(os.path.abspath(__file__))
+    proc = subprocess.run([sys.executable, "-c", _RUNNER % (root, tests), so],
+                          capture_output=True, text=True, timeout=300)
+    if proc.returncode != 0:
+        return
+    line = [l for l in proc.stdout.splitlines() if l.startswith("FAILED_PINS")][-1]
+    failed = [x for x in line.split(" ", 1)[1].split(",") if x] if " " in line else []
+    assert failed, "mutant %s passed every pin" % name
