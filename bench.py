@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Benchmark of libks, the KS matmul path, on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the hot path over one batch: plan + launch of the KS
+kernel(s) for the workload (ks_matmul for a single factor, ks_chain_matmul
+for a chain) on synthetic seeded inputs already resident in HBM. K steps are
+timed between two device synchronisations; several copies of the inputs and
+outputs rotate so that each step reads data that is not in the 256 MB
+Infinity Cache or the L2 (the working set of a step is re-read only after
+more than 288 MB of other traffic).
+
+Default workload: the ViT-S/16 MLP up-projection as one KS factor, pattern
+(4, 64, 16, 6) mapping 384 -> 1536, 25,216 rows (128 images x 197 tokens),
+fp32.
+
+Printed: one JSON line with the throughput (algorithmic GB/s), TFLOP/s, the
+roofline of the dominant kernel (measured per launch with HIP events on the
+launch stream) and the fp64 oracle timed on this host's cores on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+FP32_PEAK_TFLOPS = 157.3         # MI355X fp32 (vector and matrix), published
+BF16_PEAK_TFLOPS = 2516.6        # MI355X bf16 dense MFMA, published
+CACHE_BYTES = (256 + 32) * 2 ** 20   # Infinity Cache + 8 x 4 MB L2
+METRIC = "KS matmul achieved GB/s & TFLOP/s as % of roofline, fp32, 1×MI355X"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "kronecker_sparse_structured_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".cpp", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode())
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="vit_mlp")
+    ap.add_argument("--dtype", default="f32", choices=["f32", "bf16"])
+    ap.add_argument("--kernel", default="auto", choices=["auto", "generic", "valu", "mfma"])
+    ap.add_argument("--no-fuse", action="store_true", help="chains: one launch per factor")
+    ap.add_argument("--no-rotate", action="store_true", help="reuse one input/output set (warm caches)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle leg")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain device copy of known size (for counter calibration)")
+    return ap.parse_args()
+
+
+def factor_bytes(p, x_bytes, w_bytes, batch):
+    a, b, c, d = p
+    return x_bytes * batch * a * c * d + 4 * batch * a * b * d + w_bytes * a * b * c * d
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(rows would shard across GPUs with no exchange); run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from kronecker_sparse_structured_amd import datagen, libks
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = datagen.get(args.workload)
+    bf16 = args.dtype == "bf16"
+    chain = len(wl.patterns) > 1
+    X, Ws = datagen.draw(wl)
+
+    def put(a, as_bf16):
+        if as_bf16:
+            return torch.from_numpy(datagen.bf16_bits(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    xb = 2 if bf16 else 4
+    wbytes = 2 if bf16 else 4
+    batch = wl.batch
+    n_out = wl.n_out
+    step_bytes = xb * batch * wl.n_in + 4 * batch * n_out
+    Wt = [put(W, bf16) for W in Ws]
+    ws_bytes = 0
+    flags = libks.CHAIN_NO_FUSE if args.no_fuse else libks.CHAIN_AUTO
+    dt = libks.DTYPE_BF16 if bf16 else libks.DTYPE_F32
+    if chain:
+        ws_bytes = libks.ks_chain_workspace_size(wl.patterns, batch, dt, flags)
+    working = step_bytes + 2 * ws_bytes
+    nset = 1 if args.no_rotate else max(2, int(np.ceil(CACHE_BYTES / working)) + 1)
+    Xt = [put(X, bf16)]
+    for _ in range(nset - 1):
+        Xt.append(Xt[0].clone())
+    Yt = [torch.empty((batch, n_out), dtype=torch.float32, device=dev) for _ in range(nset)]
+    wst = [torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None for _ in range(nset)]
+    del X
+
+    # algorithmic bytes and flops of one step, as run
+    flops = sum(2 * batch * datagen.nnz(p) for p in wl.patterns)
+    if chain:
+        # as run: each launch group reads its input and writes its output
+        # once (fp32 between groups) and reads its weights once.
+        bytes_run = 0
+        x_sz = xb
+        for grp in libks.ks_chain_groups(wl.patterns, batch, dt, flags):
+            bytes_run += x_sz * batch * datagen.n_in(wl.patterns[grp[0]])
+            bytes_run += 4 * batch * datagen.n_out(wl.patterns[grp[-1]])
+            bytes_run += sum(wbytes * datagen.nnz(wl.patterns[k]) for k in grp)
+            x_sz = 4
+        bytes_min = step_bytes + sum(wbytes * datagen.nnz(p) for p in wl.patterns)
+    else:
+        bytes_run = factor_bytes(wl.patterns[0], xb, wbytes, batch)
+        bytes_min = bytes_run
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        k = i % nset
+        if chain:
+            libks.ks_chain_matmul(wl.patterns, Wt, Xt[k], Yt[k], batch, dt, wst[k], ws_bytes, flags, stream)
+        else:
+            libks.ks_matmul_ex(wl.patterns[0], Wt[0], Xt[k], Yt[k], batch, dt, stream, kernel=args.kernel)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    mean_ms = float(np.mean(kern_ms))
+    med_ms = float(np.median(kern_ms))
+
+    value = bytes_run * args.steps / wall / 1e9
+    achieved = bytes_run / (mean_ms * 1e-3) / 1e9
+    peak_flops = BF16_PEAK_TFLOPS if bf16 else FP32_PEAK_TFLOPS
+    tflops = flops / (mean_ms * 1e-3) / 1e12
+    t_roof = max(bytes_run / (HBM_PEAK_GBS * 1e9), flops / (peak_flops * 1e12))
+    bound = "hbm" if bytes_run / (HBM_PEAK_GBS * 1e9) >= flops / (peak_flops * 1e12) else "mfma"
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            rec = json.load(open(TRAFFIC_FILE)).get(args.workload + ":" + args.dtype)
+            if rec and rec.get("source_hash") == kernel_source_hash():
+                traffic = rec.get("bytes_per_launch")
+        except (ValueError, OSError):
+            traffic = None
+
+    if args.calib_copy:
+        src = torch.empty(256 * 2 ** 20 // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    roofline = {
+        "bound": bound,
+        "achieved": round(achieved if bound == "hbm" else tflops, 2),
+        "peak": HBM_PEAK_GBS if bound == "hbm" else peak_flops,
+        "unit": "GB/s" if bound == "hbm" else "TFLOP/s",
+        "frac": round((achieved / HBM_PEAK_GBS) if bound == "hbm" else (tflops / peak_flops), 4),
+        "traffic": traffic,
+        "roofline_time_frac": round(t_roof / (mean_ms * 1e-3), 4),
+    }
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(wl, bf16, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "kernel_ms_mean": round(mean_ms, 5),
+        "kernel_ms_median": round(med_ms, 5),
+        "tflops": round(tflops, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "patterns": [list(p) for p in wl.patterns],
+            "batch": batch,
+            "n_in": wl.n_in,
+            "n_out": n_out,
+            "bytes_per_step": bytes_run,
+            "bytes_min": bytes_min,
+            "flops_per_step": flops,
+            "chain_fused": bool(chain and not args.no_fuse),
+            "kernel": args.kernel if not chain else "chain",
+            "plan": "; ".join(libks.ks_plan_describe(p, batch, libks.DTYPE_F32 if not bf16 else
+                                                     (libks.DTYPE_BF16 if i == 0 else libks.DTYPE_BF16W))
+                              for i, p in enumerate(wl.patterns)),
+            "rotating_sets": nset,
+            "parallelism": "single GPU",
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline(wl, bf16, target_s):
+    """The fp64 oracle as it stands, timed on this host on a bounded number
+    of rows of the same workload; reported in the same unit (GB/s of the
+    workload's algorithmic bytes per row)."""
+    import numpy as np
+    sys.path.insert(0, ROOT)
+    import oracle
+    from kronecker_sparse_structured_amd import datagen
+
+    lib = oracle.load()
+    xw = "bf16" if bf16 else "f32"
+    small = datagen.scaled(wl, min(wl.batch, 4096))
+    X, Ws = datagen.draw(small)
+    Wd = [oracle.widen(datagen.bf16_bits(W), "bf16") if bf16 else oracle.widen(W) for W in Ws]
+    Xd_all = oracle.widen(datagen.bf16_bits(X), "bf16") if bf16 else oracle.widen(X)
+
+    def run(rows):
+        t0 = time.perf_counter()
+        if len(wl.patterns) == 1:
+            oracle.ks_matmul(wl.patterns[0], Wd[0], Xd_all[:rows], lib=lib)
+        else:
+            oracle.ks_chain_matmul(wl.patterns, Wd, Xd_all[:rows], lib=lib)
+        return time.perf_counter() - t0
+
+    rows = min(16, small.batch)
+    t = run(rows)
+    while t < 0.2 and rows < small.batch:
+        rows = min(small.batch, rows * 4)
+        t = run(rows)
+    per_row = t / rows
+    want = int(max(1, min(small.batch, target_s / per_row)))
+    reps = max(1, int(target_s / (per_row * want)))
+    total_t = 0.0
+    for _ in range(reps):
+        total_t += run(want)
+    rows_done = want * reps
+    xb = 2 if bf16 else 4
+    row_bytes = xb * wl.n_in + 4 * wl.n_out
+    gbs = row_bytes * rows_done / total_t / 1e9
+    return {
+        "value": round(gbs, 4),
+        "unit": "GB/s",
+        "cores": oracle.num_threads(lib),
+        "kind": "oracle",
+        "sample": "%d rows of %s (%d of %d rows, %d repeat(s)), %.1f s" % (
+            rows_done, wl.name, want, wl.batch, reps, total_t),
+    }
+
+
+if __name__ == "__main__":
+    sys.exit(main())

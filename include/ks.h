@@ -1,0 +1,193 @@
+/*
+ * ks.h -- C ABI of libks: Kronecker-sparse (KS) matrix multiplication on
+ * AMD MI355X (gfx950).
+ *
+ * The operation. A KS matrix has a support that is a Kronecker product of
+ * identity and all-ones blocks (KS abstract page, taxoreview.com
+ * "dblp:303/4794", first paragraph, first sentence). libks handles the
+ * support I_a (x) 1_{b x c} (x) I_d: W is (a*b*d) x (a*c*d) and holds
+ * a*b*c*d nonzeros, stored densely as a 4-D tensor K of shape (a, d, b, c),
+ * gamma fastest, with
+ *     W[alpha*b*d + beta*d + delta][alpha*c*d + gamma*d + delta]
+ *         = K[alpha][delta][beta][gamma].
+ * Every entry point computes Y = X * W^T for a batch of rows:
+ *     Y[n][alpha][beta][delta] = sum_gamma K[alpha][delta][beta][gamma]
+ *                                        * X[n][alpha][gamma][delta],
+ * X is batch x (a*c*d) and Y is batch x (a*b*d), both row-major, batch first.
+ * The same page's third paragraph factorises matrices into products of
+ * butterfly-support factors, and its first sentence ties KS matrices to
+ * Butterfly and Monarch matrices, which are such products: ks_chain_matmul
+ * applies a list of factors in order. The page's third sentence describes
+ * the kernel principle followed here: one fused pass, output-stationary,
+ * with no separate permutation of X or Y through global memory.
+ *
+ * Conventions for every entry point.
+ *  - All tensor pointers (W, X, Y, workspace) are DEVICE pointers owned by
+ *    the caller. libks never allocates or frees device memory and keeps no
+ *    per-call state; it is safe to call from several host threads.
+ *  - Calls are asynchronous on `stream` (0 = the null stream). Argument
+ *    errors are detected on the host before any HIP call and returned as a
+ *    status; nothing is launched then. Launch failures are returned as
+ *    KS_ERR_HIP. Faults during execution surface at the caller's next
+ *    synchronisation, as for any HIP kernel.
+ *  - batch == 0 is a valid no-op.
+ *  - Results are deterministic: the same call on the same inputs gives
+ *    bit-identical outputs (no atomics, fixed summation order per kernel).
+ *  - No exception crosses the ABI.
+ */
+#ifndef KS_H_
+#define KS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The KS pattern (a, b, c, d): support I_a (x) 1_{b x c} (x) I_d.
+ * Each field must be >= 1 (powers of two are not required). n_in = a*c*d,
+ * n_out = a*b*d and nnz = a*b*c*d must each be below 2^31. */
+typedef struct ks_pattern_t {
+    int32_t a, b, c, d;
+} ks_pattern_t;
+
+/* Element types. Accumulation is always fp32 and Y is always fp32.
+ *  KS_DTYPE_F32   X fp32,  W fp32.
+ *  KS_DTYPE_BF16  X bf16,  W bf16 (products of two bf16 values are exact
+ *                 in fp32, so only the fp32 accumulation rounds).
+ *  KS_DTYPE_BF16W X fp32,  W bf16 (the later factors of a bf16 chain, whose
+ *                 inputs are fp32 intermediates).
+ * bf16 is the upper 16 bits of an IEEE fp32 word. */
+typedef enum ks_dtype_t {
+    KS_DTYPE_F32 = 0,
+    KS_DTYPE_BF16 = 1,
+    KS_DTYPE_BF16W = 2
+} ks_dtype_t;
+
+typedef enum ks_status_t {
+    KS_OK = 0,
+    KS_ERR_NULL = 1,            /* a required pointer is NULL (batch > 0)      */
+    KS_ERR_PATTERN = 2,         /* a field < 1, or n_in/n_out/nnz >= 2^31      */
+    KS_ERR_BATCH = 3,           /* batch < 0 or batch >= 2^31                  */
+    KS_ERR_DTYPE = 4,           /* unknown dtype (or BF16W as a chain dtype)   */
+    KS_ERR_CHAIN_MISMATCH = 5,  /* n < 1, or n_out(p[k]) != n_in(p[k+1])       */
+    KS_ERR_WORKSPACE = 6,       /* workspace NULL or smaller than required     */
+    KS_ERR_ALIGN = 7,           /* pointer not aligned to its element size     */
+    KS_ERR_OVERLAP = 8,         /* Y (or workspace) overlaps an input          */
+    KS_ERR_HIP = 9,             /* a HIP call failed (launch, device query)    */
+    KS_ERR_UNSUPPORTED = 10,    /* a forced kernel cannot run this pattern     */
+    KS_ERR_INVALID = 11         /* other invalid argument (flags, options)     */
+} ks_status_t;
+
+/* Kernel families, for ks_matmul_ex (tests and benchmarks only). */
+typedef enum ks_kernel_t {
+    KS_KERNEL_AUTO = 0,     /* the planner's choice (what ks_matmul runs)        */
+    KS_KERNEL_GENERIC = 1,  /* one thread per output, any pattern                */
+    KS_KERNEL_VALU = 2,     /* weights in registers, fp32 FMA (b, c <= 16)       */
+    KS_KERNEL_MFMA = 3      /* LDS-staged tiles on matrix cores (b, c >= 16)     */
+} ks_kernel_t;
+
+typedef struct ks_options_t {
+    int32_t kernel;         /* a ks_kernel_t value                               */
+    int32_t rows_per_block; /* 0 = planner default; else rows per workgroup step */
+    int32_t reserved[6];    /* must be zero                                      */
+} ks_options_t;
+
+/* Chain flags. */
+#define KS_CHAIN_AUTO 0u      /* fuse consecutive factors where the planner can */
+#define KS_CHAIN_NO_FUSE 1u   /* one launch per factor, through the workspace   */
+
+/* Human-readable name of a status; never NULL. */
+const char* ks_status_string(ks_status_t status);
+
+/* Library version string, e.g. "libks 0.1.0 gfx950". */
+const char* ks_version(void);
+
+/*
+ * ks_matmul: Y = X * W^T for one KS factor p.
+ *   W      device, K tensor of shape (p.a, p.d, p.b, p.c), contiguous,
+ *          element type per dt.
+ *   X      device, batch x (a*c*d) row-major, element type per dt.
+ *   Y      device, batch x (a*b*d) row-major fp32; fully overwritten.
+ *   batch  number of rows, 0 <= batch < 2^31.
+ *   dt     KS_DTYPE_F32, KS_DTYPE_BF16 or KS_DTYPE_BF16W.
+ *   stream HIP stream for the launch.
+ * Pointers must be aligned to their element size (4 bytes fp32, 2 bytes
+ * bf16); 16-byte alignment enables wider loads but is not required.
+ * Y must not overlap X or W (KS_ERR_OVERLAP).
+ */
+ks_status_t ks_matmul(ks_pattern_t p, const void* W, const void* X, void* Y,
+                      int64_t batch, ks_dtype_t dt, hipStream_t stream);
+
+/*
+ * ks_matmul_ex: ks_matmul with options; opt may be NULL (same as ks_matmul).
+ * opt->kernel forces a kernel family; KS_ERR_UNSUPPORTED if that family
+ * cannot run p with dt. For tests and benchmarks that compare kernels on
+ * the same input; results of every family agree within fp32 rounding.
+ */
+ks_status_t ks_matmul_ex(ks_pattern_t p, const void* W, const void* X, void* Y,
+                         int64_t batch, ks_dtype_t dt, hipStream_t stream,
+                         const ks_options_t* opt);
+
+/*
+ * ks_chain_workspace_size: bytes of device workspace ks_chain_matmul needs
+ * for these arguments (0 if none), written to *bytes.
+ *   p, n   the factors in application order (p[0] is applied to X first).
+ *   dt     KS_DTYPE_F32 or KS_DTYPE_BF16 (chain dtype; intermediates are
+ *          always fp32).
+ *   flags  KS_CHAIN_AUTO or KS_CHAIN_NO_FUSE.
+ * Returns the same validation statuses as ks_chain_matmul for p, n, batch,
+ * dt and flags; KS_ERR_NULL if bytes is NULL.
+ */
+ks_status_t ks_chain_workspace_size(const ks_pattern_t* p, int n, int64_t batch,
+                                    ks_dtype_t dt, unsigned flags, size_t* bytes);
+
+/*
+ * ks_chain_matmul: Y = X * (W_{n-1} ... W_1 W_0)^T, factor 0 applied first.
+ *   p      host array of n patterns; n_out(p[k]) must equal n_in(p[k+1]).
+ *   W      host array of n device pointers; W[k] holds factor k's K tensor
+ *          (p[k].a, p[k].d, p[k].b, p[k].c).
+ *   X      device, batch x n_in(p[0]); Y device fp32, batch x n_out(p[n-1]).
+ *   dt     KS_DTYPE_F32: everything fp32. KS_DTYPE_BF16: X and every W are
+ *          bf16; intermediates and Y are fp32, so factors after the first
+ *          read fp32 inputs with bf16 weights.
+ *   ws     device workspace of ws_bytes >= ks_chain_workspace_size(...);
+ *          may be NULL when that size is 0. 16-byte aligned. Must not
+ *          overlap X, Y or any W.
+ *   flags  KS_CHAIN_AUTO: consecutive factors whose joint tile fits on chip
+ *          run as one fused launch with the intermediate kept in LDS.
+ *          KS_CHAIN_NO_FUSE: one launch per factor.
+ * All launches go to `stream` in order; there is no host synchronisation.
+ */
+ks_status_t ks_chain_matmul(const ks_pattern_t* p, int n, const void* const* W,
+                            const void* X, void* Y, int64_t batch, ks_dtype_t dt,
+                            void* ws, size_t ws_bytes, unsigned flags,
+                            hipStream_t stream);
+
+/*
+ * ks_chain_plan: the launch groups ks_chain_matmul uses for these arguments.
+ * Writes the number of groups to *groups and, for each group in order, the
+ * number of consecutive factors it runs (1, or 2 for a fused pair) to
+ * group_len[0 .. min(*groups, cap) - 1]. Pure host code; no HIP call. Same
+ * validation statuses as ks_chain_workspace_size; KS_ERR_NULL if groups is
+ * NULL (group_len may be NULL when cap is 0).
+ */
+ks_status_t ks_chain_plan(const ks_pattern_t* p, int n, int64_t batch, ks_dtype_t dt,
+                          unsigned flags, int* group_len, int cap, int* groups);
+
+/*
+ * ks_plan_describe: write a one-line description of the kernel and tile the
+ * planner picks for (p, batch, dt) into buf (NUL-terminated, truncated to
+ * len). Pure host code; no HIP call. For tests and benchmark labels.
+ */
+ks_status_t ks_plan_describe(ks_pattern_t p, int64_t batch, ks_dtype_t dt,
+                             char* buf, size_t len);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif  /* KS_H_ */

@@ -1,0 +1,321 @@
+// ks_api.cpp -- the C ABI of libks: argument validation, planning and
+// dispatch. Validation is pure host code and returns before any HIP call, so
+// every argument error can be produced without a GPU.
+//
+// The operation is Y = X * W^T for W with support I_a (x) 1_{b x c} (x) I_d
+// (KS abstract page, taxoreview.com "dblp:303/4794", first paragraph); see
+// include/ks.h for the layouts.
+
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "ks_internal.h"
+
+namespace {
+
+using ks::Shape;
+
+constexpr int64_t kLimit = int64_t(1) << 31;
+
+ks_status_t shape_of(ks_pattern_t p, Shape* s) {
+    if (p.a < 1 || p.b < 1 || p.c < 1 || p.d < 1) return KS_ERR_PATTERN;
+    const int64_t a = p.a, b = p.b, c = p.c, d = p.d;
+    const int64_t n_in = a * c * d, n_out = a * b * d;
+    if (n_in >= kLimit || n_out >= kLimit) return KS_ERR_PATTERN;
+    // a*b*c*d can overflow int64 only if the factors are huge; each partial
+    // product is checked against 2^31 first.
+    if (a * b >= kLimit || a * b * c >= kLimit || a * b * c * d >= kLimit) return KS_ERR_PATTERN;
+    s->a = p.a; s->b = p.b; s->c = p.c; s->d = p.d;
+    s->n_in = n_in; s->n_out = n_out; s->nnz = a * b * c * d;
+    return KS_OK;
+}
+
+ks_status_t check_batch(int64_t batch) {
+    return (batch < 0 || batch >= kLimit) ? KS_ERR_BATCH : KS_OK;
+}
+
+ks_status_t factor_types(ks_dtype_t dt, int* xt, int* wt) {
+    switch (dt) {
+        case KS_DTYPE_F32: *xt = ks::kF32; *wt = ks::kF32; return KS_OK;
+        case KS_DTYPE_BF16: *xt = ks::kBF16; *wt = ks::kBF16; return KS_OK;
+        case KS_DTYPE_BF16W: *xt = ks::kF32; *wt = ks::kBF16; return KS_OK;
+        default: return KS_ERR_DTYPE;
+    }
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Half-open byte ranges [p, p+pb) and [q, q+qb) intersect.
+bool overlap(const void* p, uint64_t pb, const void* q, uint64_t qb) {
+    if (pb == 0 || qb == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), b0 = reinterpret_cast<uintptr_t>(q);
+    return a0 < b0 + qb && b0 < a0 + pb;
+}
+
+ks_status_t check_options(const ks_options_t* opt) {
+    if (!opt) return KS_OK;
+    if (opt->kernel < KS_KERNEL_AUTO || opt->kernel > KS_KERNEL_MFMA) return KS_ERR_INVALID;
+    if (opt->rows_per_block < 0 || opt->rows_per_block > 4096) return KS_ERR_INVALID;
+    for (int i = 0; i < 6; ++i)
+        if (opt->reserved[i] != 0) return KS_ERR_INVALID;
+    return KS_OK;
+}
+
+// Compute units of the current device, cached per device id.
+ks_status_t current_cus(int* cus) {
+    static std::mutex mu;
+    static std::vector<int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return KS_ERR_HIP;
+    std::lock_guard<std::mutex> lock(mu);
+    if (dev >= 0 && dev < static_cast<int>(cache.size()) && cache[dev] > 0) {
+        *cus = cache[dev];
+        return KS_OK;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        return KS_ERR_HIP;
+    if (dev >= static_cast<int>(cache.size())) cache.resize(dev + 1, 0);
+    cache[dev] = n;
+    *cus = n;
+    return KS_OK;
+}
+
+// The planner's kernel family for one factor.
+int choose_kernel(const Shape& s, int xt, int wt) {
+    if (ks::mfma_supports(s, xt, wt) && (s.b >= 32 || s.c >= 32)) return KS_KERNEL_MFMA;
+    if (ks::valu_supports(s, xt, wt)) return KS_KERNEL_VALU;
+    if (ks::mfma_supports(s, xt, wt)) return KS_KERNEL_MFMA;
+    return KS_KERNEL_GENERIC;
+}
+
+ks_status_t launch_family(int kernel, const ks::FactorCall& f) {
+    switch (kernel) {
+        case KS_KERNEL_GENERIC: return ks::launch_generic(f);
+        case KS_KERNEL_VALU: return ks::launch_valu(f);
+        case KS_KERNEL_MFMA: return ks::launch_mfma(f);
+        default: return KS_ERR_INVALID;
+    }
+}
+
+// A forced family runs or refuses; the planner's choice falls back to the
+// generic kernel when its family refuses the call (for instance pointers
+// that are not 16-byte aligned).
+ks_status_t run_factor(int kernel, const ks::FactorCall& f) {
+    if (kernel != KS_KERNEL_AUTO) return launch_family(kernel, f);
+    const int chosen = choose_kernel(f.s, f.xt, f.wt);
+    ks_status_t st = launch_family(chosen, f);
+    if (st == KS_ERR_UNSUPPORTED && chosen != KS_KERNEL_GENERIC) st = ks::launch_generic(f);
+    return st;
+}
+
+// Validated chain: shapes, element types and the fusion grouping.
+struct ChainPlan {
+    std::vector<Shape> shapes;
+    std::vector<int> group_start;  // first factor of each launch group
+    std::vector<int> group_len;    // 1 (single factor) or 2 (fused pair)
+    int xt0 = ks::kF32, wt = ks::kF32;
+    int64_t max_mid = 0;           // widest intermediate between groups
+    int nbuf = 0;                  // workspace buffers (0, 1 or 2)
+    size_t buf_bytes = 0;          // bytes per workspace buffer
+};
+
+ks_status_t plan_chain(const ks_pattern_t* p, int n, int64_t batch, ks_dtype_t dt,
+                       unsigned flags, ChainPlan* plan) {
+    if (!p) return KS_ERR_NULL;
+    if (n < 1) return KS_ERR_CHAIN_MISMATCH;
+    if (flags != KS_CHAIN_AUTO && flags != KS_CHAIN_NO_FUSE) return KS_ERR_INVALID;
+    ks_status_t st = check_batch(batch);
+    if (st != KS_OK) return st;
+    if (dt == KS_DTYPE_F32) { plan->xt0 = ks::kF32; plan->wt = ks::kF32; }
+    else if (dt == KS_DTYPE_BF16) { plan->xt0 = ks::kBF16; plan->wt = ks::kBF16; }
+    else return KS_ERR_DTYPE;
+    plan->shapes.resize(n);
+    for (int k = 0; k < n; ++k) {
+        st = shape_of(p[k], &plan->shapes[k]);
+        if (st != KS_OK) return st;
+        if (k > 0 && plan->shapes[k - 1].n_out != plan->shapes[k].n_in) return KS_ERR_CHAIN_MISMATCH;
+    }
+    for (int k = 0; k < n;) {
+        const int xt = (k == 0) ? plan->xt0 : ks::kF32;
+        int len = 1;
+        if (flags == KS_CHAIN_AUTO && k + 1 < n &&
+            ks::fused_pair_supports(plan->shapes[k], plan->shapes[k + 1], xt, plan->wt, plan->wt))
+            len = 2;
+        plan->group_start.push_back(k);
+        plan->group_len.push_back(len);
+        k += len;
+    }
+    const int groups = static_cast<int>(plan->group_start.size());
+    for (int g = 0; g + 1 < groups; ++g) {
+        const Shape& last = plan->shapes[plan->group_start[g] + plan->group_len[g] - 1];
+        if (last.n_out > plan->max_mid) plan->max_mid = last.n_out;
+    }
+    plan->nbuf = groups <= 1 ? 0 : (groups == 2 ? 1 : 2);
+    const uint64_t raw = static_cast<uint64_t>(batch) * static_cast<uint64_t>(plan->max_mid) * 4u;
+    plan->buf_bytes = static_cast<size_t>((raw + 255u) / 256u * 256u);
+    return KS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ks_status_string(ks_status_t status) {
+    switch (status) {
+        case KS_OK: return "KS_OK";
+        case KS_ERR_NULL: return "KS_ERR_NULL: a required pointer is NULL";
+        case KS_ERR_PATTERN: return "KS_ERR_PATTERN: pattern field < 1 or size >= 2^31";
+        case KS_ERR_BATCH: return "KS_ERR_BATCH: batch < 0 or >= 2^31";
+        case KS_ERR_DTYPE: return "KS_ERR_DTYPE: unsupported dtype";
+        case KS_ERR_CHAIN_MISMATCH: return "KS_ERR_CHAIN_MISMATCH: chain is empty or widths do not match";
+        case KS_ERR_WORKSPACE: return "KS_ERR_WORKSPACE: workspace missing or too small";
+        case KS_ERR_ALIGN: return "KS_ERR_ALIGN: pointer not aligned to its element size";
+        case KS_ERR_OVERLAP: return "KS_ERR_OVERLAP: output or workspace overlaps an input";
+        case KS_ERR_HIP: return "KS_ERR_HIP: a HIP call failed";
+        case KS_ERR_UNSUPPORTED: return "KS_ERR_UNSUPPORTED: the forced kernel cannot run this pattern";
+        case KS_ERR_INVALID: return "KS_ERR_INVALID: invalid flags or options";
+    }
+    return "KS_ERR_UNKNOWN";
+}
+
+const char* ks_version(void) { return "libks 0.1.0 gfx950"; }
+
+ks_status_t ks_matmul_ex(ks_pattern_t p, const void* W, const void* X, void* Y,
+                         int64_t batch, ks_dtype_t dt, hipStream_t stream,
+                         const ks_options_t* opt) {
+    ks_status_t st = check_options(opt);
+    if (st != KS_OK) return st;
+    Shape s;
+    st = shape_of(p, &s);
+    if (st != KS_OK) return st;
+    st = check_batch(batch);
+    if (st != KS_OK) return st;
+    int xt = 0, wt = 0;
+    st = factor_types(dt, &xt, &wt);
+    if (st != KS_OK) return st;
+    if (batch == 0) return KS_OK;
+    if (!W || !X || !Y) return KS_ERR_NULL;
+    if (!aligned(X, ks::elem_bytes(xt)) || !aligned(W, ks::elem_bytes(wt)) || !aligned(Y, 4))
+        return KS_ERR_ALIGN;
+    const uint64_t xb = static_cast<uint64_t>(batch) * s.n_in * ks::elem_bytes(xt);
+    const uint64_t yb = static_cast<uint64_t>(batch) * s.n_out * 4u;
+    const uint64_t wb = static_cast<uint64_t>(s.nnz) * ks::elem_bytes(wt);
+    if (overlap(Y, yb, X, xb) || overlap(Y, yb, W, wb)) return KS_ERR_OVERLAP;
+
+    const int kernel = opt ? opt->kernel : KS_KERNEL_AUTO;
+    if (kernel == KS_KERNEL_VALU && !ks::valu_supports(s, xt, wt)) return KS_ERR_UNSUPPORTED;
+    if (kernel == KS_KERNEL_MFMA && !ks::mfma_supports(s, xt, wt)) return KS_ERR_UNSUPPORTED;
+
+    ks::FactorCall f;
+    f.s = s; f.xt = xt; f.wt = wt; f.W = W; f.X = X; f.Y = static_cast<float*>(Y);
+    f.batch = batch; f.stream = stream;
+    f.rows_per_block = opt ? opt->rows_per_block : 0;
+    st = current_cus(&f.num_cus);
+    if (st != KS_OK) return st;
+    return run_factor(kernel, f);
+}
+
+ks_status_t ks_matmul(ks_pattern_t p, const void* W, const void* X, void* Y,
+                      int64_t batch, ks_dtype_t dt, hipStream_t stream) {
+    return ks_matmul_ex(p, W, X, Y, batch, dt, stream, nullptr);
+}
+
+ks_status_t ks_chain_workspace_size(const ks_pattern_t* p, int n, int64_t batch,
+                                    ks_dtype_t dt, unsigned flags, size_t* bytes) {
+    if (!bytes) return KS_ERR_NULL;
+    ChainPlan plan;
+    ks_status_t st = plan_chain(p, n, batch, dt, flags, &plan);
+    if (st != KS_OK) return st;
+    *bytes = (batch == 0) ? 0 : static_cast<size_t>(plan.nbuf) * plan.buf_bytes;
+    return KS_OK;
+}
+
+ks_status_t ks_chain_plan(const ks_pattern_t* p, int n, int64_t batch, ks_dtype_t dt,
+                          unsigned flags, int* group_len, int cap, int* groups) {
+    if (!groups || (cap > 0 && !group_len)) return KS_ERR_NULL;
+    ChainPlan plan;
+    ks_status_t st = plan_chain(p, n, batch, dt, flags, &plan);
+    if (st != KS_OK) return st;
+    const int ng = static_cast<int>(plan.group_len.size());
+    *groups = ng;
+    for (int g = 0; g < ng && g < cap; ++g) group_len[g] = plan.group_len[g];
+    return KS_OK;
+}
+
+ks_status_t ks_chain_matmul(const ks_pattern_t* p, int n, const void* const* W,
+                            const void* X, void* Y, int64_t batch, ks_dtype_t dt,
+                            void* ws, size_t ws_bytes, unsigned flags,
+                            hipStream_t stream) {
+    ChainPlan plan;
+    ks_status_t st = plan_chain(p, n, batch, dt, flags, &plan);
+    if (st != KS_OK) return st;
+    if (batch == 0) return KS_OK;
+    if (!W || !X || !Y) return KS_ERR_NULL;
+    for (int k = 0; k < n; ++k)
+        if (!W[k]) return KS_ERR_NULL;
+    const size_t need = static_cast<size_t>(plan.nbuf) * plan.buf_bytes;
+    if (need > 0 && (!ws || ws_bytes < need)) return KS_ERR_WORKSPACE;
+    const int xe = ks::elem_bytes(plan.xt0), we = ks::elem_bytes(plan.wt);
+    if (!aligned(X, xe) || !aligned(Y, 4)) return KS_ERR_ALIGN;
+    for (int k = 0; k < n; ++k)
+        if (!aligned(W[k], we)) return KS_ERR_ALIGN;
+    if (need > 0 && !aligned(ws, 16)) return KS_ERR_ALIGN;
+    const uint64_t xb = static_cast<uint64_t>(batch) * plan.shapes[0].n_in * xe;
+    const uint64_t yb = static_cast<uint64_t>(batch) * plan.shapes[n - 1].n_out * 4u;
+    if (overlap(Y, yb, X, xb)) return KS_ERR_OVERLAP;
+    if (need > 0 && (overlap(ws, need, X, xb) || overlap(ws, need, Y, yb))) return KS_ERR_OVERLAP;
+    for (int k = 0; k < n; ++k) {
+        const uint64_t wb = static_cast<uint64_t>(plan.shapes[k].nnz) * we;
+        if (overlap(Y, yb, W[k], wb)) return KS_ERR_OVERLAP;
+        if (need > 0 && overlap(ws, need, W[k], wb)) return KS_ERR_OVERLAP;
+    }
+
+    int cus = 0;
+    st = current_cus(&cus);
+    if (st != KS_OK) return st;
+    char* bufs[2] = {static_cast<char*>(ws), static_cast<char*>(ws) + plan.buf_bytes};
+    const void* cur = X;
+    int cur_t = plan.xt0;
+    const int groups = static_cast<int>(plan.group_start.size());
+    for (int g = 0; g < groups; ++g) {
+        const int k = plan.group_start[g];
+        float* out = (g == groups - 1) ? static_cast<float*>(Y)
+                                       : reinterpret_cast<float*>(bufs[g % 2]);
+        if (plan.group_len[g] == 2) {
+            st = ks::launch_fused_pair(plan.shapes[k], plan.shapes[k + 1], cur_t, plan.wt, plan.wt,
+                                       W[k], W[k + 1], cur, out, batch, stream, cus);
+        } else {
+            ks::FactorCall f;
+            f.s = plan.shapes[k]; f.xt = cur_t; f.wt = plan.wt; f.W = W[k]; f.X = cur; f.Y = out;
+            f.batch = batch; f.stream = stream; f.num_cus = cus; f.rows_per_block = 0;
+            st = run_factor(KS_KERNEL_AUTO, f);
+        }
+        if (st != KS_OK) return st;
+        cur = out;
+        cur_t = ks::kF32;
+    }
+    return KS_OK;
+}
+
+ks_status_t ks_plan_describe(ks_pattern_t p, int64_t batch, ks_dtype_t dt, char* buf, size_t len) {
+    if (!buf || len == 0) return KS_ERR_NULL;
+    Shape s;
+    ks_status_t st = shape_of(p, &s);
+    if (st != KS_OK) return st;
+    st = check_batch(batch);
+    if (st != KS_OK) return st;
+    int xt = 0, wt = 0;
+    st = factor_types(dt, &xt, &wt);
+    if (st != KS_OK) return st;
+    const int kernel = choose_kernel(s, xt, wt);
+    const int cus = 256;  // description only; launches use the device's count
+    if (kernel == KS_KERNEL_VALU) ks::valu_describe(s, xt, wt, batch, cus, buf, len);
+    else if (kernel == KS_KERNEL_MFMA) ks::mfma_describe(s, xt, wt, batch, cus, buf, len);
+    else std::snprintf(buf, len, "generic: one thread per output");
+    return KS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// ks_internal.h -- shared declarations between the libks host code and its
+// HIP kernels. Not part of the public ABI (include/ks.h is).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+#include "ks.h"
+
+namespace ks {
+
+// Element type codes for X and W.
+enum ElemType : int { kF32 = 0, kBF16 = 1 };
+
+inline int elem_bytes(int t) { return t == kBF16 ? 2 : 4; }
+
+// Shape of one factor with its derived sizes (all below 2^31 after
+// validation).
+struct Shape {
+    int a, b, c, d;
+    int64_t n_in, n_out, nnz;
+};
+
+// Everything a launcher needs for one factor.
+struct FactorCall {
+    Shape s;
+    int xt, wt;            // ElemType of X and W; Y is fp32
+    const void* W;
+    const void* X;
+    float* Y;
+    int64_t batch;
+    hipStream_t stream;
+    int num_cus;           // compute units of the current device
+    int rows_per_block;    // 0 = default
+};
+
+// Kernel launchers. Each returns KS_OK, KS_ERR_UNSUPPORTED when the family
+// cannot run this factor, or KS_ERR_HIP when the launch fails.
+ks_status_t launch_generic(const FactorCall& f);
+ks_status_t launch_valu(const FactorCall& f);
+ks_status_t launch_mfma(const FactorCall& f);
+
+// Whether a family can run a factor (pure host; no HIP call).
+bool valu_supports(const Shape& s, int xt, int wt);
+bool mfma_supports(const Shape& s, int xt, int wt);
+
+// Planner description of the VALU / MFMA tiles (pure host).
+int valu_describe(const Shape& s, int xt, int wt, int64_t batch, int num_cus, char* buf, size_t len);
+int mfma_describe(const Shape& s, int xt, int wt, int64_t batch, int num_cus, char* buf, size_t len);
+
+// Fused pair of factors (intermediate kept in LDS). Returns KS_ERR_UNSUPPORTED
+// when the pair does not fit the fused kernel.
+bool fused_pair_supports(const Shape& s0, const Shape& s1, int xt, int wt0, int wt1);
+ks_status_t launch_fused_pair(const Shape& s0, const Shape& s1, int xt, int wt0, int wt1,
+                              const void* W0, const void* W1, const void* X, float* Y,
+                              int64_t batch, hipStream_t stream, int num_cus);
+
+}  // namespace ks

@@ -1,0 +1,158 @@
+"""libks host logic without a GPU: the library loads, exports every entry
+point include/ks.h declares, and rejects bad arguments with the documented
+status before any HIP call (these calls never reach the device)."""
+import os
+import re
+import subprocess
+
+import pytest
+
+from kronecker_sparse_structured_amd import libks
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ks.h")
+
+# Fake, well-aligned device addresses far apart; validation never dereferences.
+XP, WP, YP, WSP = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ks_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return libks.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"ks_matmul", "ks_chain_matmul", "ks_chain_workspace_size"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", libks.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (ks_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        getattr(lib, n)
+
+
+def test_status_strings_and_version():
+    for i, name in enumerate(libks.STATUS):
+        assert libks.ks_status_string(i).startswith(name)
+    assert libks.ks_status_string(999) == "KS_ERR_UNKNOWN"
+    assert "gfx950" in libks.ks_version()
+
+
+def st(p, W=WP, X=XP, Y=YP, batch=4, dtype=libks.DTYPE_F32, **kw):
+    return libks.ks_matmul_ex(p, W, X, Y, batch, dtype, stream=0, check=False, **kw)
+
+
+@pytest.mark.parametrize("p", [(0, 1, 1, 1), (1, 0, 1, 1), (1, 1, -3, 1), (1, 1, 1, 0),
+                               (1 << 16, 1, 1 << 15, 1), (2, 1 << 30, 2, 1), (1, 46341, 46341, 1)])
+def test_bad_pattern(p):
+    assert st(p) == libks.KS_ERR_PATTERN
+
+
+def test_bad_batch():
+    assert st((2, 2, 2, 2), batch=-1) == libks.KS_ERR_BATCH
+    assert st((2, 2, 2, 2), batch=1 << 31) == libks.KS_ERR_BATCH
+
+
+def test_bad_dtype():
+    assert st((2, 2, 2, 2), dtype=3) == libks.KS_ERR_DTYPE
+    assert st((2, 2, 2, 2), dtype=-1) == libks.KS_ERR_DTYPE
+
+
+def test_empty_batch_is_noop_even_with_null_pointers():
+    assert st((2, 3, 4, 5), W=None, X=None, Y=None, batch=0) == libks.KS_OK
+    assert libks.ks_matmul((2, 3, 4, 5), None, None, None, 0, libks.DTYPE_F32, stream=0, check=False) == 0
+
+
+def test_null_pointers():
+    for kw in ({"W": None}, {"X": None}, {"Y": None}):
+        assert st((2, 2, 2, 2), **kw) == libks.KS_ERR_NULL
+
+
+def test_alignment():
+    assert st((2, 2, 2, 2), X=XP + 2) == libks.KS_ERR_ALIGN
+    assert st((2, 2, 2, 2), Y=YP + 1) == libks.KS_ERR_ALIGN
+    assert st((2, 2, 2, 2), W=WP + 3, dtype=libks.DTYPE_BF16) == libks.KS_ERR_ALIGN
+    assert st((2, 2, 2, 2), X=XP + 1, dtype=libks.DTYPE_BF16) == libks.KS_ERR_ALIGN
+    # bf16 X on a 2-byte boundary and fp32 Y on a 4-byte boundary are fine for
+    # validation; the call then proceeds to the device, which is not tested here.
+
+
+def test_overlap():
+    p = (2, 4, 4, 2)  # n_in = n_out = 16, batch 4 -> 256 bytes each
+    assert st(p, Y=XP) == libks.KS_ERR_OVERLAP
+    assert st(p, Y=XP + 252) == libks.KS_ERR_OVERLAP      # last 4 bytes of X
+    assert st(p, Y=WP + 4) == libks.KS_ERR_OVERLAP
+    assert st(p, Y=XP - 256 + 4) == libks.KS_ERR_OVERLAP  # Y tail reaches X head
+
+
+def test_options():
+    assert st((2, 2, 2, 2), kernel=99) == libks.KS_ERR_INVALID
+    assert st((2, 2, 2, 2), rows_per_block=-1) == libks.KS_ERR_INVALID
+    assert st((2, 2, 2, 2), reserved=[1]) == libks.KS_ERR_INVALID
+    # a forced family that cannot run the pattern is refused on the host
+    assert st((2, 3, 5, 2), kernel="valu") == libks.KS_ERR_UNSUPPORTED
+    assert st((2, 3, 5, 2), kernel="mfma") == libks.KS_ERR_UNSUPPORTED
+
+
+def cst(ps, batch=4, dtype=libks.DTYPE_F32, ws=WSP, ws_bytes=1 << 30, flags=0, Ws=None, X=XP, Y=YP, n=None):
+    Ws = Ws if Ws is not None else [WP + 0x100000 * i for i in range(len(ps))]
+    return libks.ks_chain_matmul(ps, Ws, X, Y, batch, dtype, ws, ws_bytes, flags, stream=0, n=n, check=False)
+
+
+def test_chain_validation():
+    ok = [(1, 4, 2, 4), (4, 2, 2, 2)]
+    assert cst(ok, n=0) == libks.KS_ERR_CHAIN_MISMATCH
+    assert cst([(1, 4, 2, 4), (4, 2, 3, 2)]) == libks.KS_ERR_CHAIN_MISMATCH
+    assert cst(ok, dtype=libks.DTYPE_BF16W) == libks.KS_ERR_DTYPE
+    assert cst(ok, flags=7) == libks.KS_ERR_INVALID
+    assert cst(ok, batch=-2) == libks.KS_ERR_BATCH
+    assert cst([(1, 4, 0, 4)]) == libks.KS_ERR_PATTERN
+    assert cst(ok, batch=0, X=None, Y=None, ws=None, ws_bytes=0) == libks.KS_OK
+    assert cst(ok, X=None) == libks.KS_ERR_NULL
+    assert cst(ok, Ws=[WP, None]) == libks.KS_ERR_NULL
+    need = libks.ks_chain_workspace_size(ok, 4, libks.DTYPE_F32, libks.CHAIN_NO_FUSE)
+    assert cst(ok, flags=libks.CHAIN_NO_FUSE, ws=None, ws_bytes=need) == libks.KS_ERR_WORKSPACE
+    assert cst(ok, flags=libks.CHAIN_NO_FUSE, ws_bytes=need - 1) == libks.KS_ERR_WORKSPACE
+    assert cst(ok, flags=libks.CHAIN_NO_FUSE, ws=WSP + 8, ws_bytes=need) == libks.KS_ERR_ALIGN
+    assert cst(ok, flags=libks.CHAIN_NO_FUSE, ws=XP, ws_bytes=need) == libks.KS_ERR_OVERLAP
+    assert cst(ok, Y=XP) == libks.KS_ERR_OVERLAP
+    assert cst(ok, Y=WP + 0x100000) == libks.KS_ERR_OVERLAP
+    assert cst(ok, X=XP + 2) == libks.KS_ERR_ALIGN
+
+
+def test_chain_workspace_sizes():
+    f32, nf = libks.DTYPE_F32, libks.CHAIN_NO_FUSE
+    assert libks.ks_chain_workspace_size([(2, 3, 4, 5)], 10, f32, nf) == 0
+    # two factors: one fp32 intermediate of batch x 16, rounded up to 256 bytes
+    two = [(1, 4, 2, 4), (4, 2, 2, 2)]
+    assert libks.ks_chain_workspace_size(two, 10, f32, nf) == 768
+    assert libks.ks_chain_workspace_size(two, 0, f32, nf) == 0
+    # three or more: two ping-pong buffers of the widest intermediate
+    three = [(1, 6, 2, 3), (3, 2, 3, 2), (2, 2, 3, 2)]   # 6 -> 18 -> 12 -> 8
+    assert libks.ks_chain_workspace_size(three, 100, f32, nf) == 2 * 7424
+    # bf16 chains keep fp32 intermediates
+    assert libks.ks_chain_workspace_size(two, 10, libks.DTYPE_BF16, nf) == 768
+    st_, _ = libks.ks_chain_workspace_size(two, 10, libks.DTYPE_BF16W, nf, check=False)
+    assert st_ == libks.KS_ERR_DTYPE
+
+
+def test_plan_describe():
+    assert libks.ks_plan_describe((1, 16, 16, 4096), 4096, libks.DTYPE_F32).startswith("valu lane")
+    assert libks.ks_plan_describe((4096, 16, 16, 1), 4096, libks.DTYPE_F32).startswith("valu slab")
+    assert libks.ks_plan_describe((2, 3, 5, 7), 10, libks.DTYPE_F32).startswith("generic")
+
+
+def test_chain_plan():
+    three = [(1, 6, 2, 3), (3, 2, 3, 2), (2, 2, 3, 2)]
+    assert libks.ks_chain_plan(three, 10, libks.DTYPE_F32, libks.CHAIN_NO_FUSE) == [1, 1, 1]
+    assert libks.ks_chain_groups(three, 10, libks.DTYPE_F32, libks.CHAIN_NO_FUSE) == [[0], [1], [2]]
+    groups = libks.ks_chain_groups(three, 10, libks.DTYPE_F32, libks.CHAIN_AUTO)
+    assert sum(len(g) for g in groups) == 3 and all(len(g) in (1, 2) for g in groups)

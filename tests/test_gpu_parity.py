@@ -1,0 +1,325 @@
+"""HIP path vs the fp64 oracle, through the C ABI (needs an MI355X).
+
+Small cases are compared on every output; the full-size workloads (the
+sizes and launch configuration the benchmark uses) on sampled rows that the
+oracle recomputes one by one. Every kernel family that supports a pattern is
+run on the same input.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import (DEV, FP32_REL_TOL, chain_check, check_factor, host_values, rel_err,
+                         require_gpu, run_factor, sample_rows, to_dev)
+from kronecker_sparse_structured_amd import datagen, libks
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    print("device:", torch.cuda.get_device_name(0), flush=True)
+
+
+def try_family(p, Xt, Wt, kernel):
+    """Run with a forced family; None if the family refuses the pattern."""
+    a, b, c, d = p
+    Y = torch.empty((Xt.shape[0], a * b * d), dtype=torch.float32, device=DEV)
+    st = libks.ks_matmul_ex(p, Wt, Xt, Y, Xt.shape[0], libks.dtype_code(Xt.dtype, Wt.dtype),
+                            kernel=kernel, check=False)
+    if st == libks.KS_ERR_UNSUPPORTED:
+        return None
+    assert st == libks.KS_OK, libks.ks_status_string(st)
+    return Y
+
+
+ALL_FAMILIES = ["auto", "generic", "valu", "mfma"]
+
+# ---------------------------------------------------------------- small workloads
+
+
+def test_tiny_factor_all_families():
+    wl = datagen.get("tiny")
+    X, (W,) = datagen.draw(wl)
+    p = wl.patterns[0]
+    Xt, Wt = to_dev(X), to_dev(W)
+    ran = []
+    for k in ALL_FAMILIES:
+        Y = try_family(p, Xt, Wt, k)
+        if Y is None:
+            continue
+        torch.cuda.synchronize()
+        check_factor(p, X, W, Y.cpu().numpy())
+        ran.append(k)
+    assert "generic" in ran and "auto" in ran
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("fuse", [True, False])
+def test_hadamard_chain_exact(bf16, fuse):
+    """Integer X in [-8, 8] through the four (2^k,2,2,2^(3-k)) factors equals
+    X H16 exactly (the oracle equals X H16; pinned by scipy's Hadamard)."""
+    wl = datagen.get("hadamard16")
+    X, Ws = datagen.draw(wl)
+    Xt = to_dev(X, bf16)
+    Wts = [to_dev(W, bf16) for W in Ws]
+    Y = libks.chain_matmul(Xt, Wts, wl.patterns, fuse=fuse)
+    torch.cuda.synchronize()
+    ref = oracle.ks_chain_matmul(wl.patterns, [host_values(W, bf16) for W in Ws], host_values(X, bf16))
+    assert np.array_equal(Y.cpu().numpy().astype(np.float64), ref)
+    import scipy.linalg
+    assert np.array_equal(ref, X.astype(np.float64) @ scipy.linalg.hadamard(16))
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_integer_exact_all_families(bf16):
+    """Integer data keeps every partial sum exact in fp32: all families must
+    agree with the oracle bit for bit."""
+    for p in [(2, 4, 4, 2), (8, 16, 16, 1), (4, 8, 8, 4), (1, 16, 16, 64), (2, 64, 16, 6),
+              (4, 32, 32, 2), (1, 64, 64, 4), (2, 128, 128, 1), (16, 4, 4, 16)]:
+        X, W = datagen.random_pattern_inputs(p, 37, seed=sum(p), kind="int8range")
+        W = np.clip(W, -4, 4)
+        Xt, Wt = to_dev(X, bf16), to_dev(W, bf16)
+        ref = oracle.ks_matmul(p, host_values(W, bf16), host_values(X, bf16))
+        assert np.max(np.abs(ref)) < 2 ** 24
+        for k in ALL_FAMILIES:
+            Y = try_family(p, Xt, Wt, k)
+            if Y is None:
+                continue
+            torch.cuda.synchronize()
+            assert np.array_equal(Y.cpu().numpy().astype(np.float64), ref), (p, k)
+
+
+# ---------------------------------------------------------------- fuzz over patterns
+
+FUZZ = [
+    (1, 1, 1, 1), (3, 2, 5, 7), (2, 3, 3, 9), (5, 4, 4, 3), (1, 16, 16, 3), (7, 8, 8, 1),
+    (3, 4, 8, 2), (2, 8, 4, 4), (4, 16, 8, 8), (2, 8, 16, 12), (3, 4, 4, 40), (1, 4, 4, 200),
+    (9, 16, 16, 16), (5, 8, 8, 24), (1, 32, 32, 5), (3, 64, 16, 6), (2, 16, 64, 8),
+    (1, 48, 32, 4), (6, 32, 32, 1), (1, 128, 128, 2), (2, 64, 64, 3), (1, 16, 32, 130),
+    (129, 4, 4, 1), (1, 4, 4, 1024), (33, 8, 8, 2),
+]
+
+
+@pytest.mark.parametrize("p", FUZZ, ids=lambda p: "%d_%d_%d_%d" % p)
+@pytest.mark.parametrize("batch", [1, 131])
+def test_fuzz_patterns_all_families(p, batch):
+    X, W = datagen.random_pattern_inputs(p, batch, seed=1000 + sum(p) * batch)
+    Xt, Wt = to_dev(X), to_dev(W)
+    for k in ALL_FAMILIES:
+        Y = try_family(p, Xt, Wt, k)
+        if Y is None:
+            continue
+        torch.cuda.synchronize()
+        check_factor(p, X, W, Y.cpu().numpy())
+
+
+@pytest.mark.parametrize("p", [(2, 16, 16, 8), (64, 8, 8, 8), (256, 16, 16, 16), (2, 64, 16, 6)],
+                         ids=lambda p: "%d_%d_%d_%d" % p)
+def test_bf16_and_mixed_inputs(p):
+    X, W = datagen.random_pattern_inputs(p, 70, seed=99)
+    for xb, wb in [(True, True), (False, True)]:
+        Xt, Wt = to_dev(X, xb), to_dev(W, wb)
+        for k in ALL_FAMILIES:
+            Y = try_family(p, Xt, Wt, k)
+            if Y is None:
+                continue
+            torch.cuda.synchronize()
+            check_factor(p, X, W, Y.cpu().numpy(), bf16=xb, w_bf16=wb)
+
+
+# ---------------------------------------------------------------- edges
+
+
+def test_batch_zero_and_one():
+    p = (4, 16, 16, 4)
+    X, W = datagen.random_pattern_inputs(p, 1, seed=5)
+    Xt, Wt = to_dev(X), to_dev(W)
+    Y = run_factor(p, Xt, Wt)
+    torch.cuda.synchronize()
+    check_factor(p, X, W, Y.cpu().numpy())
+    Y0 = torch.full((0, 256), 7.0, device=DEV)
+    libks.ks_matmul(p, Wt, Xt[:0], Y0, 0, libks.DTYPE_F32)
+
+
+def test_guard_bands_untouched():
+    """Canaries before and after Y stay intact for every family."""
+    for p, batch in [((3, 16, 16, 8), 67), ((5, 8, 8, 2), 33), ((2, 64, 16, 6), 45), ((1, 32, 32, 16), 19)]:
+        a, b, c, d = p
+        X, W = datagen.random_pattern_inputs(p, batch, seed=3)
+        Xt, Wt = to_dev(X), to_dev(W)
+        n_out = a * b * d
+        for k in ALL_FAMILIES:
+            guard = 4096
+            buf = torch.full((guard + batch * n_out + guard,), 12345.0, device=DEV)
+            Y = buf[guard:guard + batch * n_out].view(batch, n_out)
+            st = libks.ks_matmul_ex(p, Wt, Xt, Y, batch, libks.DTYPE_F32, kernel=k, check=False)
+            if st == libks.KS_ERR_UNSUPPORTED:
+                continue
+            assert st == 0
+            torch.cuda.synchronize()
+            h = buf.cpu().numpy()
+            assert np.all(h[:guard] == 12345.0) and np.all(h[-guard:] == 12345.0), (p, k)
+            check_factor(p, X, W, Y.cpu().numpy())
+
+
+def test_deterministic_repeat():
+    for p in [(1, 16, 16, 256), (256, 16, 16, 1), (4, 64, 16, 6), (2, 32, 32, 16)]:
+        X, W = datagen.random_pattern_inputs(p, 300, seed=8)
+        Xt, Wt = to_dev(X), to_dev(W)
+        y1 = run_factor(p, Xt, Wt).cpu()
+        y2 = run_factor(p, Xt, Wt).cpu()
+        assert torch.equal(y1, y2), p
+
+
+def test_non_default_stream():
+    p = (16, 16, 16, 16)
+    X, W = datagen.random_pattern_inputs(p, 200, seed=9)
+    Xt, Wt = to_dev(X), to_dev(W)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        Y = run_factor(p, Xt, Wt)
+    s.synchronize()
+    check_factor(p, X, W, Y.cpu().numpy())
+
+
+def test_unaligned_pointers_fall_back():
+    """X and Y offset by one element from 16-byte alignment still give the
+    right answer (the planner picks a kernel that needs no 16-byte loads)."""
+    p = (4, 16, 16, 4)
+    batch = 50
+    a, b, c, d = p
+    X, W = datagen.random_pattern_inputs(p, batch, seed=10)
+    xb = torch.empty(batch * a * c * d + 1, device=DEV)
+    xb[1:] = torch.from_numpy(X.reshape(-1)).to(DEV)
+    yb = torch.empty(batch * a * b * d + 1, device=DEV)
+    Xt = xb[1:].view(batch, -1)
+    Y = yb[1:].view(batch, -1)
+    libks.ks_matmul(p, to_dev(W), Xt, Y, batch, libks.DTYPE_F32)
+    torch.cuda.synchronize()
+    check_factor(p, X, W, Y.cpu().numpy())
+
+
+def test_nan_propagates_to_its_support():
+    p = (3, 16, 16, 8)
+    a, b, c, d = p
+    X, W = datagen.random_pattern_inputs(p, 4, seed=11)
+    al, ga, de = 1, 5, 6
+    X[2, (al * c + ga) * d + de] = np.nan
+    for k in ALL_FAMILIES:
+        Y = try_family(p, to_dev(X), to_dev(W), k)
+        if Y is None:
+            continue
+        bad = np.isnan(Y.cpu().numpy())
+        expect = np.zeros_like(bad)
+        expect[2].reshape(a, b, d)[al, :, de] = True
+        assert np.array_equal(bad, expect), k
+
+
+# ---------------------------------------------------------------- the named workloads
+
+
+def _factor_workload(name, batch=None, rows=None, kernel="auto"):
+    wl = datagen.get(name)
+    if batch is not None:
+        wl = datagen.scaled(wl, batch)
+    X, Ws = datagen.draw(wl)
+    p = wl.patterns[0]
+    Xt, Wt = to_dev(X), to_dev(Ws[0])
+    Y = run_factor(p, Xt, Wt, kernel=kernel)
+    torch.cuda.synchronize()
+    if rows is None:
+        return check_factor(p, X, Ws[0], Y.cpu().numpy())
+    r = torch.from_numpy(rows).to(DEV)
+    return check_factor(p, X, Ws[0], Y.index_select(0, r).cpu().numpy(), rows=rows)
+
+
+@pytest.mark.parametrize("batch", [1, 197, 1003])
+def test_vit_mlp_small(batch):
+    _factor_workload("vit_mlp", batch=batch)
+
+
+def test_vit_mlp_full_size_sampled():
+    wl = datagen.get("vit_mlp")
+    _factor_workload("vit_mlp", rows=sample_rows(wl.batch))
+
+
+SWEEP = datagen.square_sweep_patterns()
+
+
+@pytest.mark.parametrize("p", SWEEP, ids=lambda p: "%d_%d_%d_%d" % p)
+def test_square_sweep_small(p):
+    _factor_workload("square_%d_%d_%d_%d" % p, batch=70)
+
+
+@pytest.mark.parametrize("p", SWEEP, ids=lambda p: "%d_%d_%d_%d" % p)
+def test_square_sweep_full_size_sampled(p):
+    _factor_workload("square_%d_%d_%d_%d" % p, rows=sample_rows(16384, n=24))
+
+
+def _chain_workload(name, bf16, fuse, batch=None, rows=None):
+    wl = datagen.get(name)
+    if batch is not None:
+        wl = datagen.scaled(wl, batch)
+    X, Ws = datagen.draw(wl)
+    Xt = to_dev(X, bf16)
+    Wts = [to_dev(W, bf16) for W in Ws]
+    Y = libks.chain_matmul(Xt, Wts, wl.patterns, fuse=fuse)
+    torch.cuda.synchronize()
+    if rows is None:
+        Yh = Y.cpu().numpy()
+    else:
+        Yh = Y.index_select(0, torch.from_numpy(rows).to(DEV)).cpu().numpy()
+    return chain_check(wl.patterns, X, Ws, Yh, bf16, rows=rows)
+
+
+@pytest.mark.parametrize("fuse", [True, False])
+@pytest.mark.parametrize("batch", [5, 333])
+def test_gpt2_chain_small(fuse, batch):
+    _chain_workload("gpt2_mlp", False, fuse, batch=batch)
+
+
+@pytest.mark.parametrize("fuse", [True, False])
+def test_gpt2_chain_full_size_sampled(fuse):
+    _chain_workload("gpt2_mlp", False, fuse, rows=sample_rows(16384))
+
+
+def test_gpt2_factors_single():
+    wl = datagen.get("gpt2_mlp")
+    wl = datagen.scaled(wl, 257)
+    X, Ws = datagen.draw(wl)
+    Z = oracle.ks_matmul(wl.patterns[0], host_values(Ws[0], False), host_values(X, False)).astype(np.float32)
+    for p, W, inp in [(wl.patterns[0], Ws[0], X), (wl.patterns[1], Ws[1], Z)]:
+        Y = run_factor(p, to_dev(inp), to_dev(W))
+        torch.cuda.synchronize()
+        check_factor(p, inp, W, Y.cpu().numpy())
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("fuse", [True, False])
+def test_butterfly_chain_small(bf16, fuse):
+    _chain_workload("butterfly65536", bf16, fuse, batch=9)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_butterfly_chain_full_size_sampled(bf16):
+    _chain_workload("butterfly65536", bf16, True, rows=sample_rows(4096, n=12))
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("k", [0, 1, 2, 3])
+def test_butterfly_single_factor(bf16, k):
+    """Each factor alone, as the chain runs it: bf16 X for k = 0, fp32 X with
+    bf16 weights after that."""
+    wl = datagen.scaled(datagen.get("butterfly65536"), 40)
+    X, Ws = datagen.draw(wl)
+    p = wl.patterns[k]
+    xb = bf16 and k == 0
+    Y = run_factor(p, to_dev(X, xb), to_dev(Ws[k], bf16))
+    torch.cuda.synchronize()
+    check_factor(p, X, Ws[k], Y.cpu().numpy(), bf16=xb, w_bf16=bf16)
