@@ -58,7 +58,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="vit_mlp")
     ap.add_argument("--dtype", default="f32", choices=["f32", "bf16"])
-    ap.add_argument("--kernel", default="auto", choices=["auto", "generic", "valu", "mfma"])
+    ap.add_argument("--kernel", default="auto", choices=["auto", "generic", "valu", "mfma", "mfma_lds"])
     ap.add_argument("--no-fuse", action="store_true", help="chains: one launch per factor")
     ap.add_argument("--no-rotate", action="store_true", help="reuse one input/output set (warm caches)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle leg")

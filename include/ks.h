@@ -87,7 +87,9 @@ typedef enum ks_kernel_t {
     KS_KERNEL_AUTO = 0,     /* the planner's choice (what ks_matmul runs)        */
     KS_KERNEL_GENERIC = 1,  /* one thread per output, any pattern                */
     KS_KERNEL_VALU = 2,     /* weights in registers, fp32 FMA (b, c <= 16)       */
-    KS_KERNEL_MFMA = 3      /* LDS-staged tiles on matrix cores (b, c >= 16)     */
+    KS_KERNEL_MFMA = 3,     /* matrix cores (b, c >= 16): the register-direct
+                               variant for small d, else LDS-staged tiles        */
+    KS_KERNEL_MFMA_LDS = 4  /* matrix cores, LDS-staged tiles only               */
 } ks_kernel_t;
 
 typedef struct ks_options_t {

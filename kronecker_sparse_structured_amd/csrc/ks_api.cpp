@@ -56,7 +56,7 @@ bool overlap(const void* p, uint64_t pb, const void* q, uint64_t qb) {
 
 ks_status_t check_options(const ks_options_t* opt) {
     if (!opt) return KS_OK;
-    if (opt->kernel < KS_KERNEL_AUTO || opt->kernel > KS_KERNEL_MFMA) return KS_ERR_INVALID;
+    if (opt->kernel < KS_KERNEL_AUTO || opt->kernel > KS_KERNEL_MFMA_LDS) return KS_ERR_INVALID;
     if (opt->rows_per_block < 0 || opt->rows_per_block > 4096) return KS_ERR_INVALID;
     for (int i = 0; i < 6; ++i)
         if (opt->reserved[i] != 0) return KS_ERR_INVALID;
@@ -96,6 +96,7 @@ ks_status_t launch_family(int kernel, const ks::FactorCall& f) {
         case KS_KERNEL_GENERIC: return ks::launch_generic(f);
         case KS_KERNEL_VALU: return ks::launch_valu(f);
         case KS_KERNEL_MFMA: return ks::launch_mfma(f);
+        case KS_KERNEL_MFMA_LDS: return ks::launch_mfma_lds(f);
         default: return KS_ERR_INVALID;
     }
 }
@@ -208,6 +209,7 @@ ks_status_t ks_matmul_ex(ks_pattern_t p, const void* W, const void* X, void* Y,
     const int kernel = opt ? opt->kernel : KS_KERNEL_AUTO;
     if (kernel == KS_KERNEL_VALU && !ks::valu_supports(s, xt, wt)) return KS_ERR_UNSUPPORTED;
     if (kernel == KS_KERNEL_MFMA && !ks::mfma_supports(s, xt, wt)) return KS_ERR_UNSUPPORTED;
+    if (kernel == KS_KERNEL_MFMA_LDS && !ks::mfma_lds_supports(s, xt, wt)) return KS_ERR_UNSUPPORTED;
 
     ks::FactorCall f;
     f.s = s; f.xt = xt; f.wt = wt; f.W = W; f.X = X; f.Y = static_cast<float*>(Y);

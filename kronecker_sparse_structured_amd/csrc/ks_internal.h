@@ -40,11 +40,13 @@ struct FactorCall {
 // cannot run this factor, or KS_ERR_HIP when the launch fails.
 ks_status_t launch_generic(const FactorCall& f);
 ks_status_t launch_valu(const FactorCall& f);
-ks_status_t launch_mfma(const FactorCall& f);
+ks_status_t launch_mfma(const FactorCall& f);       // direct variant, else LDS-staged
+ks_status_t launch_mfma_lds(const FactorCall& f);   // LDS-staged variant only
 
 // Whether a family can run a factor (pure host; no HIP call).
 bool valu_supports(const Shape& s, int xt, int wt);
 bool mfma_supports(const Shape& s, int xt, int wt);
+bool mfma_lds_supports(const Shape& s, int xt, int wt);
 
 // Planner description of the VALU / MFMA tiles (pure host).
 int valu_describe(const Shape& s, int xt, int wt, int64_t batch, int num_cus, char* buf, size_t len);

@@ -1,22 +1,435 @@
-// ks_mfma.hip -- placeholder until the matrix-core kernel lands.
+// ks_mfma.hip -- KS matmul on the matrix cores for blocks with b, c >= 16.
+//
+// Y[n][alpha][beta][delta] = sum_gamma K[alpha][delta][beta][gamma]
+//                                    * X[n][alpha][gamma][delta]
+// (KS abstract page, taxoreview.com "dblp:303/4794", first paragraph). For a
+// fixed (alpha, delta) pair this is a dense product of the rows' c-vectors
+// with the b x c block K[alpha][delta]: M = rows, N = b, K = c. With b and c
+// of 16 or more that product fills v_mfma_f32_16x16x4_f32 tiles exactly, so
+// the contraction runs on the matrix cores and the vector ALUs only move
+// data. The op stays bound by HBM traffic for most such shapes (about 6 flop
+// per byte at b = 64, c = 16), so the kernel is built around moving X and Y
+// once, in whole 16-byte vectors, with no permutation pass through global
+// memory (the same page, third sentence: a fused, output-stationary kernel).
+//
+// Workgroup: a tile of (alpha, delta) pairs and a range of rows; one loader
+// wave streams X into a 4-stage LDS ring (ks_stream.h), four consumer waves:
+//  * hold the B operands of their N tiles, for every pair of the tile, in
+//    VGPRs for the whole kernel (waves split the b outputs);
+//  * per stage and pair, read A operands (16 rows x 4 gammas) from LDS,
+//    accumulate c/4 MFMAs in fp32 and write the 16 x 16 results into a Y
+//    tile in LDS laid out like the rows of Y;
+//  * after an LDS barrier, store the Y tile with 16-byte vectors that cover
+//    whole segments of Y.
+
+#include <algorithm>
 #include <cstdio>
 
+#include "ks_device.h"
 #include "ks_internal.h"
+#include "ks_stream.h"
+#include "ks_tile.h"
 
 namespace ks {
+namespace {
 
-bool mfma_supports(const Shape&, int, int) { return false; }
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-int mfma_describe(const Shape&, int, int, int64_t, int, char* buf, size_t len) {
-    return std::snprintf(buf, len, "mfma: unsupported");
+constexpr int kLdsPerGroup = 80 * 1024;   // two workgroups per compute unit
+
+// Tile shape of one (b, c) instantiation.
+template <int B, int C>
+struct MfmaShape {
+    static constexpr int NT = B / 16;                  // 16-wide N tiles
+    static constexpr int WN = NT < 4 ? NT : 4;         // waves along N
+    static constexpr int NTW = NT / WN;                // N tiles per wave
+    static constexpr int WR = 4 / WN;                  // waves along rows
+    static constexpr int KS = C / 4;                   // MFMA K steps
+    static constexpr int R = 16 * WR;                  // rows per stage
+    // Pairs per tile: the B operands take TP * NTW * KS VGPRs, at most 64.
+    static constexpr int TP = (256 / (NTW * C)) < 1 ? 1 : 256 / (NTW * C);
+};
+
+// MfmaShape<b, c>::TP for runtime b, c.
+__host__ __device__ constexpr int mfma_tp(int b, int c) {
+    return (256 / ((b / 16 < 4 ? 1 : b / 64) * c)) < 1 ? 1 : 256 / ((b / 16 < 4 ? 1 : b / 64) * c);
 }
 
-ks_status_t launch_mfma(const FactorCall&) { return KS_ERR_UNSUPPORTED; }
+// Loader instructions (KB) per X stage: R rows of at most TP * c elements,
+// plus one pad vector per row.
+__host__ __device__ constexpr int mfma_stage_insts(int b, int c, int eb) {
+    return ((16 * (4 / (b / 16 < 4 ? b / 16 : 4))) * (mfma_tp(b, c) * c * eb / 16 + 1) + 63) / 64;
+}
 
-bool fused_pair_supports(const Shape&, const Shape&, int, int, int) { return false; }
+struct MfmaArgs {
+    int a, d;
+    int64_t n_in, n_out, batch;
+    int at, dt;
+    int tiles_delta, n_tiles;
+    int rows_per_split;      // a multiple of the stage rows
+    int contiguous;
+    int qy;                  // Y vectors in one row chunk of the tile
+    int insts;               // loader instructions per stage (stage = insts KB of LDS)
+    int stages;              // LDS ring depth
+    int xcd_remap;           // 1: renumber workgroups so neighbouring tiles share an XCD
+    StageMap xmap;           // LDS layout of an X stage
+    RowChunk yc;             // LDS layout of the Y tile and its global stores
+};
 
-ks_status_t launch_fused_pair(const Shape&, const Shape&, int, int, int, const void*, const void*,
-                              const void*, float*, int64_t, hipStream_t, int) {
+template <typename TX, typename TW, int B, int C>
+__global__ __launch_bounds__(kStreamThreads) void mfma_kernel(const TX* __restrict__ X,
+                                                              const TW* __restrict__ K,
+                                                              float* __restrict__ Y, MfmaArgs args) {
+    using S = MfmaShape<B, C>;
+    constexpr int TP = S::TP, NTW = S::NTW, WN = S::WN, KS = S::KS, R = S::R;
+    constexpr int EB = int(sizeof(TX));
+    constexpr int VWX = 16 / EB;
+    constexpr int kMaxInsts = mfma_stage_insts(B, C, EB);
+    static_assert(kMaxInsts <= 63, "vmcnt is six bits");
+    const int kStageBytes = args.insts * 1024;
+    const int kStages = args.stages;
+
+    extern __shared__ __align__(16) unsigned char lds[];
+    unsigned char* const ys = lds + kStages * kStageBytes;
+
+    const int t = threadIdx.x;
+    const int blk = args.xcd_remap ? xcd_logical_block(blockIdx.x, gridDim.x) : int(blockIdx.x);
+    const int tile = blk % args.n_tiles;
+    const int split = blk / args.n_tiles;
+    const int ta = tile / args.tiles_delta;
+    const int td = tile - ta * args.tiles_delta;
+    const int alpha0 = ta * args.at;
+    const int delta0 = td * args.dt;
+    const int d = args.d;
+    const int at_eff = min(args.at, args.a - alpha0);
+    const int dt_eff = min(args.dt, d - delta0);
+    const bool contig = args.contiguous != 0;
+    const int64_t xg0 = int64_t(alpha0) * C * d + (contig ? 0 : delta0);
+    const int64_t yg0 = int64_t(alpha0) * B * d + (contig ? 0 : delta0);
+
+    const int64_t row_begin = int64_t(split) * args.rows_per_split;
+    if (row_begin >= args.batch) return;
+    const int64_t row_end = min(args.batch, row_begin + int64_t(args.rows_per_split));
+    const int nsteps = static_cast<int>((row_end - row_begin + R - 1) / R);
+    const int xrow_bytes = args.xmap.row_vec * 16;
+    const int xblk_bytes = args.xmap.blk_vec * 16;   // no per-block padding in X stages
+
+    if (t >= kConsumerThreads) {
+        // ------------------------------------------------------ loader wave
+        LoaderPlan<kMaxInsts> lp;
+        const int valid_blocks = contig ? at_eff : args.xmap.blocks;
+        const int valid_vec = contig ? args.xmap.blk_vec : dt_eff / VWX;
+        make_loader_plan<kMaxInsts>(args.xmap, args.insts, VWX, EB, args.n_in, valid_blocks, valid_vec,
+                                    t - kConsumerThreads, &lp);
+        auto issue = [&](int s) {
+            const int64_t n0 = row_begin + int64_t(s) * R;
+            issue_stage<kMaxInsts>(lp, args.insts, X + n0 * args.n_in + xg0,
+                                   stage_limit(n0, row_end, args.n_in, EB), lds + (s % kStages) * kStageBytes);
+        };
+        for (int s = 0; s < kStages - 1 && s < nsteps; ++s) issue(s);
+        for (int s = 0; s < nsteps; ++s) {
+            // stage s has landed once only the stages issued after it remain
+            wait_vmcnt_upto(min(kStages - 2, nsteps - 1 - s) * args.insts);
+            lds_barrier();                                   // stage s ready
+            if (s + kStages - 1 < nsteps) issue(s + kStages - 1);
+            lds_barrier();                                   // Y tile written
+        }
+        return;
+    }
+
+    // ---------------------------------------------------------- consumers
+    const int wave = t >> 6;
+    const int lane = t & 63;
+    const int wn = wave % WN;
+    const int wr = wave / WN;
+
+    const int gsx = contig ? d * EB : xblk_bytes;          // X: gamma stride in LDS
+    const int bsy = contig ? d * 4 : args.yc.seg_lds;      // Y: beta stride in LDS
+    int xoff[TP], yoff[TP];
+    bool pv[TP];
+    float breg[TP][NTW][KS];
+#pragma unroll
+    for (int p = 0; p < TP; ++p) {
+        const int al = p / args.dt;
+        const int de = p - al * args.dt;
+        pv[p] = p < args.at * args.dt && al < at_eff && de < dt_eff;
+        xoff[p] = contig ? al * xblk_bytes + de * EB : de * EB;
+        yoff[p] = contig ? al * args.yc.lds_slab + de * 4 : de * 4;
+        const TW* kp = K + ((int64_t(alpha0 + al) * d + delta0 + de) * B) * C;
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+            const int beta = (wn * NTW + nt) * 16 + (lane & 15);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int gamma = ks * 4 + (lane >> 4);
+                breg[p][nt][ks] = pv[p] ? to_f32(kp[beta * C + gamma]) : 0.0f;
+            }
+        }
+    }
+
+
+    const int arow = wr * 16 + (lane & 15);       // A operand row of this lane
+    const int akk = lane >> 4;                    // A operand k (gamma within a step)
+    for (int s = 0; s < nsteps; ++s) {
+        lds_barrier();                                                   // stage s ready
+        const unsigned char* xcur = lds + (s % kStages) * kStageBytes;
+#pragma unroll
+        for (int p = 0; p < TP; ++p) {
+            if (!pv[p]) continue;
+            floatx4 acc[NTW];
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) acc[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+            const unsigned char* xa = xcur + arow * xrow_bytes + xoff[p] + akk * gsx;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const float av = to_f32(*reinterpret_cast<const TX*>(xa + ks * 4 * gsx));
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt)
+                    acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, breg[p][nt][ks], acc[nt], 0, 0, 0);
+            }
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) {
+                const int beta = (wn * NTW + nt) * 16 + (lane & 15);
+                unsigned char* yb = ys + yoff[p] + beta * bsy;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int row = wr * 16 + 4 * (lane >> 4) + v;
+                    *reinterpret_cast<float*>(yb + row * args.yc.lds_row) = acc[nt][v];
+                }
+            }
+        }
+        lds_barrier();                                                   // Y tile written
+        // store the Y tile: flat vector f of the stage is vector f % qy of row f / qy
+        const int64_t n0 = row_begin + int64_t(s) * R;
+        const int nvec = static_cast<int>(min(int64_t(R), row_end - n0)) * args.qy;
+#pragma unroll 2
+        for (int f = t; f < nvec; f += kConsumerThreads) {
+            const int r = f / args.qy;
+            int gy, ly;
+            bool ok;
+            chunk_vector(args.yc, f - r * args.qy, 4, at_eff, dt_eff, &gy, &ly, &ok);
+            if (ok)
+                __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(ys + r * args.yc.lds_row + ly),
+                                            reinterpret_cast<u32x4*>(Y + (n0 + r) * args.n_out + yg0 + gy));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+
+struct MfmaGeom {
+    int tp, r, at, dt, tiles_delta, n_tiles, contiguous, qy, insts, stages;
+    StageMap xmap;
+    RowChunk yc;
+    size_t lds;
+};
+
+bool supported_bc(int b, int c) {
+    return (b == 16 || b == 32 || b == 64 || b == 128) && (c == 16 || c == 32 || c == 64 || c == 128);
+}
+
+// Smallest pad (in 16-byte vectors) making a row pitch of `vec` vectors an
+// odd multiple of 16 bytes modulo 256, so 16 consecutive rows start in
+// distinct 16-byte bank groups.
+int row_pad(int vec) {
+    int pad = 0;
+    while (((vec + pad) % 16) % 2 == 0) ++pad;
+    return pad;
+}
+
+bool geom_for(const Shape& s, int xt, MfmaGeom* g) {
+    if (!supported_bc(s.b, s.c)) return false;
+    const int eb = elem_bytes(xt);
+    const int vwx = 16 / eb;
+    const int b = s.b, c = s.c, d = s.d;
+    const int nt = b / 16;
+    const int wn = nt < 4 ? nt : 4;
+    g->tp = mfma_tp(b, c);
+    g->r = 16 * (4 / wn);
+    const int kStageInsts = mfma_stage_insts(b, c, eb);
+    if (kStageInsts > 63) return false;
+    // the loader addresses a stage with 32-bit byte offsets
+    if (int64_t(g->r) * s.n_in * eb >= (int64_t(1) << 31)) return false;
+    StageMap& xm = g->xmap;
+    RowChunk& yc = g->yc;
+    xm.rows = g->r;
+    xm.pad_vec = 0;
+    if (d <= g->tp) {
+        if ((c * d) % vwx != 0) return false;
+        // as many alphas as the pairs allow, while the X stage fits and the
+        // whole workgroup stays within about 80 KB of LDS (two per CU)
+        const int blk = c * d / vwx;
+        g->at = 0;
+        for (int at = std::max(1, g->tp / d); at >= 1; --at) {
+            const int xv = at * blk;
+            const int insts = (g->r * (xv + row_pad(xv)) + 63) / 64;
+            const size_t lds = size_t(3) * insts * 1024 + size_t(g->r) * (size_t(at) * b * d * 4 + 16);
+            if (g->r * (xv + row_pad(xv)) <= kStageInsts * 64 && (lds <= kLdsPerGroup || at == 1)) {
+                g->at = at;
+                break;
+            }
+        }
+        if (g->at == 0) return false;
+        g->dt = d;
+        g->contiguous = 1;
+        xm.blocks = g->at;
+        xm.blk_vec = blk;
+        xm.gstride = c * d;
+        xm.row_vec = g->at * xm.blk_vec;
+        yc.contiguous = 1;
+        yc.slab = b * d;
+        yc.lds_slab = b * d * 4;
+        yc.lds_row = g->at * yc.lds_slab + 16;
+        yc.nseg = yc.seg_global = yc.seg_lds = yc.seg_cap = 0;
+    } else {
+        // one alpha, tp deltas: segments of tp elements, d apart
+        if (g->tp % vwx != 0 || d % vwx != 0 || g->tp % 4 != 0 || d % 4 != 0) return false;
+        g->at = 1;
+        g->dt = g->tp;
+        g->contiguous = 0;
+        xm.blocks = c;
+        xm.blk_vec = g->tp / vwx;
+        xm.gstride = d;
+        xm.row_vec = c * xm.blk_vec;
+        yc.contiguous = 0;
+        yc.slab = yc.lds_slab = 0;
+        yc.nseg = b;
+        yc.seg_global = d;
+        yc.seg_cap = g->tp;
+        yc.seg_lds = g->tp * 4;
+        yc.lds_row = b * g->tp * 4 + 16;
+    }
+    xm.row_vec += row_pad(xm.row_vec);
+    if (xm.rows * xm.row_vec > kStageInsts * 64) return false;
+    const int64_t tiles_alpha = (s.a + g->at - 1) / g->at;
+    g->tiles_delta = g->contiguous ? 1 : (d + g->dt - 1) / g->dt;
+    const int64_t nt_all = tiles_alpha * g->tiles_delta;
+    if (nt_all > (int64_t(1) << 30)) return false;
+    g->n_tiles = static_cast<int>(nt_all);
+    g->qy = g->contiguous ? g->at * b * d / 4 : b * g->dt / 4;
+    g->insts = (xm.rows * xm.row_vec + 63) / 64;
+    // ring depth: as many stages as fit next to the Y tile in the
+    // per-workgroup LDS budget, 3..8, with the loader's wait count
+    // (stages - 2) * insts within vmcnt's range
+    const int64_t ytile = int64_t(g->r) * yc.lds_row;
+    g->stages = static_cast<int>(std::max<int64_t>(3, std::min<int64_t>(8, (kLdsPerGroup - ytile) / (g->insts * 1024))));
+    while (g->stages > 3 && (g->stages - 2) * g->insts > 63) --g->stages;
+    if ((g->stages - 2) * g->insts > 63) return false;
+    g->lds = size_t(g->stages) * g->insts * 1024 + size_t(ytile);
+    return g->lds <= 160 * 1024;
+}
+
+// Rows per workgroup: a multiple of the stage rows, so that the grid is about
+// one resident wave of workgroups with equal shares.
+int64_t rows_per_split(const MfmaGeom& g, int64_t batch, int num_cus, int rows_per_block) {
+    const int64_t steps_total = (batch + g.r - 1) / g.r;
+    int64_t steps;
+    if (rows_per_block > 0) {
+        steps = std::max<int64_t>(1, (rows_per_block + g.r - 1) / g.r);
+    } else {
+        const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(4, (160 * 1024) / int64_t(g.lds)));
+        const int64_t resident = int64_t(std::max(num_cus, 1)) * per_cu;
+        const int64_t splits = std::max<int64_t>(1, resident / std::max(g.n_tiles, 1));
+        steps = (steps_total + splits - 1) / splits;
+    }
+    steps = std::max<int64_t>(1, std::min(steps, steps_total));
+    return steps * g.r;
+}
+
+template <typename TX, typename TW, int B, int C>
+ks_status_t launch_bc(const FactorCall& f, const MfmaGeom& g, const MfmaArgs& args, dim3 grid) {
+    if constexpr (mfma_stage_insts(B, C, int(sizeof(TX))) <= 63) {
+        hipLaunchKernelGGL((mfma_kernel<TX, TW, B, C>), grid, dim3(kStreamThreads), g.lds, f.stream,
+                           static_cast<const TX*>(f.X), static_cast<const TW*>(f.W), f.Y, args);
+        return hipGetLastError() == hipSuccess ? KS_OK : KS_ERR_HIP;
+    } else {
+        return KS_ERR_UNSUPPORTED;
+    }
+}
+
+template <typename TX, typename TW, int B>
+ks_status_t launch_b(const FactorCall& f, const MfmaGeom& g, const MfmaArgs& args, dim3 grid) {
+    switch (f.s.c) {
+        case 16: return launch_bc<TX, TW, B, 16>(f, g, args, grid);
+        case 32: return launch_bc<TX, TW, B, 32>(f, g, args, grid);
+        case 64: return launch_bc<TX, TW, B, 64>(f, g, args, grid);
+        case 128: return launch_bc<TX, TW, B, 128>(f, g, args, grid);
+    }
+    return KS_ERR_UNSUPPORTED;
+}
+
+template <typename TX, typename TW>
+ks_status_t launch_types(const FactorCall& f, const MfmaGeom& g, const MfmaArgs& args, dim3 grid) {
+    switch (f.s.b) {
+        case 16: return launch_b<TX, TW, 16>(f, g, args, grid);
+        case 32: return launch_b<TX, TW, 32>(f, g, args, grid);
+        case 64: return launch_b<TX, TW, 64>(f, g, args, grid);
+        case 128: return launch_b<TX, TW, 128>(f, g, args, grid);
+    }
+    return KS_ERR_UNSUPPORTED;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+bool mfma_supports(const Shape& s, int xt, int wt) {
+    (void)wt;
+    MfmaGeom g;
+    return geom_for(s, xt, &g);
+}
+
+bool mfma_lds_supports(const Shape& s, int xt, int wt) { return mfma_supports(s, xt, wt); }
+
+int mfma_describe(const Shape& s, int xt, int wt, int64_t batch, int num_cus, char* buf, size_t len) {
+    (void)wt;
+    MfmaGeom g;
+    if (!geom_for(s, xt, &g)) return std::snprintf(buf, len, "mfma: unsupported");
+    const int64_t rps = rows_per_split(g, batch, num_cus, 0);
+    return std::snprintf(buf, len,
+                         "mfma 16x16x4f32: pairs/tile=%d (alphas=%d deltas=%d %s) rows/stage=%d tiles=%d "
+                         "rows/wg=%lld wgs=%lld stages=%d x %d KB lds=%zu",
+                         g.tp, g.at, g.dt, g.contiguous ? "contiguous" : "segmented", g.r, g.n_tiles,
+                         static_cast<long long>(rps),
+                         static_cast<long long>(g.n_tiles * ((batch + rps - 1) / std::max<int64_t>(rps, 1))),
+                         g.stages, g.insts, g.lds);
+}
+
+ks_status_t launch_mfma(const FactorCall& f) { return launch_mfma_lds(f); }
+
+ks_status_t launch_mfma_lds(const FactorCall& f) {
+    MfmaGeom g;
+    if (!geom_for(f.s, f.xt, &g)) return KS_ERR_UNSUPPORTED;
+    if (!aligned16(f.X) || !aligned16(f.Y)) return KS_ERR_UNSUPPORTED;
+    if ((f.s.n_in * elem_bytes(f.xt)) % 16 != 0 || (f.s.n_out * 4) % 16 != 0) return KS_ERR_UNSUPPORTED;
+    const int64_t rps = rows_per_split(g, f.batch, f.num_cus, f.rows_per_block);
+    const int64_t splits = (f.batch + rps - 1) / rps;
+    const int64_t blocks = int64_t(g.n_tiles) * splits;
+    if (blocks > 0x7fffffff || rps > 0x7fffffff) return KS_ERR_UNSUPPORTED;
+    MfmaArgs args;
+    args.a = f.s.a;
+    args.d = f.s.d;
+    args.n_in = f.s.n_in;
+    args.n_out = f.s.n_out;
+    args.batch = f.batch;
+    args.at = g.at;
+    args.dt = g.dt;
+    args.tiles_delta = g.tiles_delta;
+    args.n_tiles = g.n_tiles;
+    args.rows_per_split = static_cast<int>(rps);
+    args.contiguous = g.contiguous;
+    args.qy = g.qy;
+    args.insts = g.insts;
+    args.stages = g.stages;
+    args.xcd_remap = g.contiguous ? 0 : 1;
+    args.xmap = g.xmap;
+    args.yc = g.yc;
+    const dim3 grid(static_cast<unsigned>(blocks));
+    if (f.xt == kF32 && f.wt == kF32) return launch_types<float, float>(f, g, args, grid);
+    if (f.xt == kBF16 && f.wt == kBF16) return launch_types<bf16_t, bf16_t>(f, g, args, grid);
+    if (f.xt == kF32 && f.wt == kBF16) return launch_types<float, bf16_t>(f, g, args, grid);
     return KS_ERR_UNSUPPORTED;
 }
 

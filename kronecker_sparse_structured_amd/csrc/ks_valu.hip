@@ -5,103 +5,137 @@
 //                                    * X[n][alpha][gamma][delta]
 // (KS abstract page, taxoreview.com "dblp:303/4794", first paragraph). With
 // b, c <= 16 the contraction is a few fp32 FMAs per output and the op is
-// bound by HBM traffic, so the design goal is to move X and Y exactly once,
-// in full cache lines, with no permutation pass (the same page, third
+// bound by HBM traffic, so the kernel is built to move X and Y exactly once,
+// in whole 16-byte vectors, with no permutation pass (the same page, third
 // sentence: a fused, output-stationary kernel).
 //
-// Workgroup tile: a set of (alpha, delta) pairs (all beta) and a range of
-// rows. Every thread owns NB outputs of each row for a FIXED (alpha, delta)
-// set, so its NB x c weights are loaded into registers once and reused for
-// every row the workgroup streams (weight-stationary, output-stationary).
+// Workgroup: a tile of (alpha, delta) pairs (all beta) and a range of rows.
+// One loader wave streams the tile's part of each row of X into a 4-stage
+// LDS ring (ks_stream.h); four consumer waves compute and store Y.
 //
-// X: the tile's part of each row is copied global -> LDS with 16-byte loads
-// that cover whole segments, double-buffered across row steps (the global
-// loads of step s+1 are in flight while step s computes). Threads then read
-// X from LDS in whatever order the contraction wants.
-//
-// Two thread mappings:
-//  * lane mode (d >= 8): lanes run over consecutive (alpha, delta) pairs,
-//    delta fastest; a thread reads one X value per gamma and writes NB
-//    outputs, each store coalesced across lanes along delta.
-//  * slab mode (d in {1, 2, 4}): a thread owns an alpha' and all d deltas;
-//    it reads the contiguous c*d slab of its alpha with 16-byte LDS reads and
-//    writes NB*d contiguous outputs.
+// Every consumer thread owns NB betas of a FIXED set of (alpha, delta)
+// pairs, so its NB x DV x c weights are loaded into registers once and
+// reused for every row (weight-stationary, output-stationary). Mappings:
+//  * lane mode (d >= 8): lanes run over consecutive delta runs of DV = 4
+//    deltas (DV = 1 when d is not a multiple of 4); a thread reads DV
+//    consecutive X values per gamma from LDS and stores DV consecutive
+//    outputs per beta, so both sides move 16-byte vectors across lanes.
+//  * slab mode (d in {1, 2, 4}): a thread owns one alpha and all d deltas;
+//    it reads the contiguous c*d slab of X with 16-byte LDS reads and stores
+//    NB*d contiguous outputs.
 
 #include <algorithm>
 #include <cstdio>
 
 #include "ks_device.h"
 #include "ks_internal.h"
+#include "ks_stream.h"
 
 namespace ks {
 namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kRows = 2;   // rows per double-buffered step
+constexpr int kMaxInsts = 31;       // loader instructions (KB) per stage, at most
+constexpr int kTargetVec = 16 * 64; // aim for about 16 KB per stage
+constexpr int kLdsPerGroup = 80 * 1024;   // two workgroups per compute unit
+
+// Betas per thread: the largest power of two dividing b whose weights
+// (NB * dv * c values) fit in 128 registers for c = 16, 64 otherwise, which
+// keeps a thread near 168 VGPRs (three waves per SIMD, two workgroups per
+// compute unit). The host planner uses the same rule.
+__host__ __device__ constexpr int nb_rule(int b, int c, int dv) {
+    const int budget = c == 16 ? 128 : 64;
+    int nb = b;
+    while (nb > 1 && nb * c * dv > budget) nb /= 2;
+    return nb;
+}
 
 struct ValuArgs {
     int a, d;
     int64_t n_in, n_out;
     int64_t batch;
     int at;              // alphas per tile
-    int dt;              // deltas per tile (lane mode), d in slab mode
+    int dt;              // deltas per tile
     int tiles_delta;     // delta tiles per alpha tile
     int n_tiles;         // alpha tiles * delta tiles
-    int steps_per_split; // row steps per workgroup
-    int lds_row_bytes;   // LDS bytes per staged row
-    int lds_alpha_bytes; // LDS bytes between alpha' slabs (contiguous chunks)
-    int contiguous;      // 1: the tile's row chunk is one contiguous run
+    int rows_per_split;  // rows per workgroup (a multiple of map.rows)
+    int contiguous;      // 1: the tile spans every delta (alpha slabs); 0: gamma segments
+    int insts;           // loader instructions per stage (stage = insts KB of LDS)
+    int stages;          // LDS ring depth
+    int xcd_remap;       // 1: renumber workgroups so neighbouring tiles share an XCD
+    StageMap map;        // LDS layout of one stage
 };
 
-// Betas per thread. A thread holds NB*c*dv weights and prefetches kRows rows
-// of its share of X (c*dv*G/... per row, see VPT), which together must stay
-// near 176 registers so two waves fit per SIMD: the smallest power-of-two
-// number of beta groups G with (b + kRows) * c * dv / G <= 176. The host
-// planner uses the same rule.
-__host__ __device__ constexpr int nb_rule(int b, int c, int dv) {
-    int g = 1;
-    while (g < b && (b + kRows) * c * dv > 176 * g) g *= 2;
-    return b / g;
-}
-
 template <typename TX, typename TW, int B, int C, int DV, bool LANE>
-__global__ __launch_bounds__(kThreads, 2) void valu_kernel(const TX* __restrict__ X,
-                                                          const TW* __restrict__ K,
-                                                          float* __restrict__ Y,
-                                                          ValuArgs args) {
-    constexpr int VW = 16 / int(sizeof(TX));                    // elements per 16-byte vector
-    constexpr int NB = nb_rule(B, C, LANE ? 1 : DV);
-    constexpr int G = B / NB;                                   // beta groups
-    constexpr int P = kThreads / G;                             // pairs (lane) or alphas (slab)
-    constexpr int R = kRows;                                    // rows per step
-    constexpr int DVX = LANE ? 1 : DV;                          // deltas per thread
-    // 16-byte vectors of X per row that each thread copies.
-    constexpr int VPT = LANE ? (P * C / VW + kThreads - 1) / kThreads
-                             : (P * C * DV / VW + kThreads - 1) / kThreads;
+__global__ __launch_bounds__(kStreamThreads) void valu_kernel(const TX* __restrict__ X,
+                                                              const TW* __restrict__ K,
+                                                              float* __restrict__ Y,
+                                                              ValuArgs args) {
+    constexpr int EB = int(sizeof(TX));
+    constexpr int VW = 16 / EB;                 // elements per 16-byte vector
+    constexpr int NB = nb_rule(B, C, DV);
+    constexpr int G = B / NB;                   // beta groups
+    constexpr int P = kConsumerThreads / G;     // delta runs (lane) or alphas (slab) per group
     static_assert(B % NB == 0, "beta groups must divide b");
-    static_assert(VPT >= 1, "at least one vector per thread");
 
     extern __shared__ __align__(16) unsigned char lds[];
+    const int kStageBytes = args.insts * 1024;
+    const int kStages = args.stages;
 
     const int t = threadIdx.x;
-    const int tile = blockIdx.x % args.n_tiles;
-    const int split = blockIdx.x / args.n_tiles;
+    const int blk = args.xcd_remap ? xcd_logical_block(blockIdx.x, gridDim.x) : int(blockIdx.x);
+    const int tile = blk % args.n_tiles;
+    const int split = blk / args.n_tiles;
     const int ta = tile / args.tiles_delta;
     const int td = tile - ta * args.tiles_delta;
     const int alpha0 = ta * args.at;
     const int delta0 = td * args.dt;
     const int d = args.d;
+    const int at_eff = min(args.at, args.a - alpha0);
+    const int dt_eff = min(args.dt, d - delta0);
+    const int64_t chunk_base = int64_t(alpha0) * C * d + (args.contiguous ? 0 : delta0);
 
-    // ---- thread -> (alpha', delta', beta group) -------------------------
-    int g, al_l, de_l;
+    const int64_t row_begin = int64_t(split) * args.rows_per_split;
+    if (row_begin >= args.batch) return;
+    const int64_t row_end = min(args.batch, row_begin + int64_t(args.rows_per_split));
+    const int R = args.map.rows;
+    const int nsteps = static_cast<int>((row_end - row_begin + R - 1) / R);
+    const int row_bytes = args.map.row_vec * 16;
+    const int pitch_bytes = (args.map.blk_vec + args.map.pad_vec) * 16;
+
+    if (t >= kConsumerThreads) {
+        // ------------------------------------------------------ loader wave
+        LoaderPlan<kMaxInsts> lp;
+        const int valid_blocks = args.contiguous ? at_eff : args.map.blocks;
+        const int valid_vec = args.contiguous ? args.map.blk_vec : dt_eff / VW;
+        make_loader_plan<kMaxInsts>(args.map, args.insts, VW, EB, args.n_in, valid_blocks, valid_vec,
+                                    t - kConsumerThreads, &lp);
+        auto issue = [&](int s) {
+            const int64_t n0 = row_begin + int64_t(s) * R;
+            issue_stage<kMaxInsts>(lp, args.insts, X + n0 * args.n_in + chunk_base,
+                                   stage_limit(n0, row_end, args.n_in, EB), lds + (s % kStages) * kStageBytes);
+        };
+        for (int s = 0; s < kStages - 1 && s < nsteps; ++s) issue(s);
+        for (int s = 0; s < nsteps; ++s) {
+            // stage s has landed once only the stages issued after it remain
+            wait_vmcnt_upto(min(kStages - 2, nsteps - 1 - s) * args.insts);
+            lds_barrier();
+            if (s + kStages - 1 < nsteps) issue(s + kStages - 1);
+        }
+        return;
+    }
+
+    // ---------------------------------------------------------- consumers
+    int g, al_l, de_l;   // beta group, alpha within the tile, first delta within the tile
     if (LANE) {
         g = t / P;
         const int p = t - g * P;
-        al_l = p / args.dt;
-        de_l = p - al_l * args.dt;
-        if (al_l >= args.at) al_l = args.at;  // marks the thread idle below
+        const int runs = args.dt / DV;              // delta runs per alpha
+        al_l = p / runs;
+        de_l = (p - al_l * runs) * DV;
     } else {
         g = t % G;
         al_l = t / G;
@@ -109,136 +143,71 @@ __global__ __launch_bounds__(kThreads, 2) void valu_kernel(const TX* __restrict_
     }
     const int alpha = alpha0 + al_l;
     const int delta = delta0 + de_l;
-    const bool active = (al_l < args.at) && alpha < args.a && (LANE ? (delta < d) : true);
+    const bool active = al_l < at_eff && (LANE ? (de_l < dt_eff) : true);
 
-    // ---- weights into registers: kr[j][dv][gamma] ------------------------
-    float kr[NB][DVX][C];
-    if (active) {
+    // weights: kr[j][dv][gamma] = K[alpha][delta + dv][g*NB + j][gamma]
+    float kr[NB][DV][C];
 #pragma unroll
-        for (int dv = 0; dv < DVX; ++dv) {
+    for (int dv = 0; dv < DV; ++dv)
 #pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                const TW* kp = K + ((int64_t(alpha) * d + delta + dv) * B + g * NB + j) * C;
+        for (int j = 0; j < NB; ++j) {
+            const TW* kp = K + ((int64_t(alpha) * d + delta + dv) * B + g * NB + j) * C;
 #pragma unroll
-                for (int gm = 0; gm < C; ++gm) kr[j][dv][gm] = to_f32(kp[gm]);
-            }
+            for (int gm = 0; gm < C; ++gm) kr[j][dv][gm] = active ? to_f32(kp[gm]) : 0.0f;
         }
-    } else {
-#pragma unroll
-        for (int dv = 0; dv < DVX; ++dv)
-#pragma unroll
-            for (int j = 0; j < NB; ++j)
-#pragma unroll
-                for (int gm = 0; gm < C; ++gm) kr[j][dv][gm] = 0.0f;
-    }
 
-    // ---- the copy plan: which 16-byte vectors of each row this thread moves
-    int64_t chunk_base;   // element offset of the tile's chunk within a row
-    int at_eff = min(args.at, args.a - alpha0);
-    int dt_eff = LANE ? min(args.dt, d - delta0) : DV;
-    if (args.contiguous) chunk_base = int64_t(alpha0) * C * d;
-    else chunk_base = int64_t(alpha0) * C * d + delta0;
-    int gofs[VPT];
-    int lofs[VPT];
-    bool vok[VPT];
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-        const int q = t + i * kThreads;
-        if (args.contiguous) {
-            const int per_alpha = C * d / VW;       // vectors per alpha slab
-            const int al = q / per_alpha;
-            const int rem = q - al * per_alpha;
-            gofs[i] = q * VW;
-            lofs[i] = al * args.lds_alpha_bytes + rem * 16;
-            vok[i] = al < at_eff && al < args.at;
-        } else {
-            const int per_seg = args.dt / VW;       // vectors per gamma segment
-            const int gm = q / per_seg;
-            const int e = q - gm * per_seg;
-            gofs[i] = gm * d + e * VW;
-            lofs[i] = (gm * args.dt + e * VW) * int(sizeof(TX));
-            vok[i] = gm < C && e * VW < dt_eff;
-        }
-    }
-
-    // ---- rows of this workgroup -------------------------------------------
-    const int64_t row_begin = int64_t(split) * args.steps_per_split * R;
-    if (row_begin >= args.batch) return;
-    const int64_t row_end = min(args.batch, row_begin + int64_t(args.steps_per_split) * R);
-    const int nsteps = static_cast<int>((row_end - row_begin + R - 1) / R);
-
-    const int buf_bytes = R * args.lds_row_bytes;
-    u32x4 pre[R][VPT];
-
-    auto load_step = [&](int s) {
-        const int64_t n0 = row_begin + int64_t(s) * R;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const bool row_ok = n0 + r < row_end;
-            const TX* xrow = X + (n0 + r) * args.n_in + chunk_base;
-#pragma unroll
-            for (int i = 0; i < VPT; ++i) {
-                if (row_ok && vok[i]) pre[r][i] = *reinterpret_cast<const u32x4*>(xrow + gofs[i]);
-            }
-        }
-    };
-    auto store_lds = [&](int buf) {
-        unsigned char* base = lds + buf * buf_bytes;
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int i = 0; i < VPT; ++i)
-                if (vok[i]) *reinterpret_cast<u32x4*>(base + r * args.lds_row_bytes + lofs[i]) = pre[r][i];
-    };
-
-    load_step(0);
-    store_lds(0);
-    __syncthreads();
-
-    // Output and LDS read offsets of this thread.
+    // LDS offset of this thread's X within a staged row, and the gamma stride.
+    const int xl_off = !active ? 0
+                     : LANE ? (args.contiguous ? al_l * pitch_bytes + de_l * EB : de_l * EB)
+                            : al_l * pitch_bytes;
+    const int gstride = LANE ? (args.contiguous ? d : args.dt) * EB : 0;
     const int64_t yoff = LANE ? (int64_t(alpha) * B + g * NB) * d + delta
                               : (int64_t(alpha) * B + g * NB) * DV;
-    // Idle threads read a valid LDS address (their result is never stored).
-    const int xl_off = !active ? 0
-                     : LANE ? (args.contiguous ? al_l * args.lds_alpha_bytes + de_l * int(sizeof(TX))
-                                               : de_l * int(sizeof(TX)))
-                            : al_l * args.lds_alpha_bytes;
-    const int gstride = LANE ? (args.contiguous ? d : args.dt) * int(sizeof(TX)) : 0;
 
     for (int s = 0; s < nsteps; ++s) {
-        if (s + 1 < nsteps) load_step(s + 1);
-        const unsigned char* base = lds + (s & 1) * buf_bytes;
+        lds_barrier();
+        const unsigned char* base = lds + (s % kStages) * kStageBytes;
         const int64_t n0 = row_begin + int64_t(s) * R;
+        const int rows = static_cast<int>(min(int64_t(R), row_end - n0));
 #pragma unroll 1
-        for (int r = 0; r < R; ++r) {
-            const unsigned char* xr = base + r * args.lds_row_bytes + xl_off;
-            float acc[NB][DVX];
+        for (int r = 0; r < rows; ++r) {
+            const unsigned char* xr = base + r * row_bytes + xl_off;
+            float acc[NB][DV];
 #pragma unroll
             for (int j = 0; j < NB; ++j)
 #pragma unroll
-                for (int dv = 0; dv < DVX; ++dv) acc[j][dv] = 0.0f;
+                for (int dv = 0; dv < DV; ++dv) acc[j][dv] = 0.0f;
             if (LANE) {
 #pragma unroll
                 for (int gm = 0; gm < C; ++gm) {
-                    const float x = to_f32(*reinterpret_cast<const TX*>(xr + gm * gstride));
+                    float x[DV];
+                    const unsigned char* xp = xr + gm * gstride;
+                    if constexpr (DV == 4 && EB == 4) {
+                        const floatx4 w = *reinterpret_cast<const floatx4*>(xp);
+                        x[0] = w[0]; x[1] = w[1]; x[2] = w[2]; x[3] = w[3];
+                    } else if constexpr (DV == 4) {
+                        const u32x2 w = *reinterpret_cast<const u32x2*>(xp);
+                        x[0] = bf16_lo(w[0]); x[1] = bf16_hi(w[0]); x[2] = bf16_lo(w[1]); x[3] = bf16_hi(w[1]);
+                    } else {
+                        x[0] = to_f32(*reinterpret_cast<const TX*>(xp));
+                    }
 #pragma unroll
-                    for (int j = 0; j < NB; ++j) acc[j][0] = fmaf(kr[j][0][gm], x, acc[j][0]);
+                    for (int j = 0; j < NB; ++j)
+#pragma unroll
+                        for (int dv = 0; dv < DV; ++dv) acc[j][dv] = fmaf(kr[j][dv][gm], x[dv], acc[j][dv]);
                 }
             } else {
-                // The slab holds c*DV elements, element e = gamma*DV + delta.
+                // the slab holds c*DV elements, element e = gamma*DV + delta
 #pragma unroll
                 for (int v = 0; v < C * DV / VW; ++v) {
                     const u32x4 w = *reinterpret_cast<const u32x4*>(xr + v * 16);
                     float xv[VW];
-                    if (sizeof(TX) == 4) {
+                    if constexpr (EB == 4) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) xv[e] = __uint_as_float(w[e]);
                     } else {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            xv[2 * e] = bf16_lo(w[e]);
-                            xv[2 * e + 1] = bf16_hi(w[e]);
-                        }
+                        for (int e = 0; e < 4; ++e) { xv[2 * e] = bf16_lo(w[e]); xv[2 * e + 1] = bf16_hi(w[e]); }
                     }
 #pragma unroll
                     for (int e = 0; e < VW; ++e) {
@@ -250,33 +219,33 @@ __global__ __launch_bounds__(kThreads, 2) void valu_kernel(const TX* __restrict_
                     }
                 }
             }
-            const int64_t n = n0 + r;
-            if (active && n < row_end) {
-                float* yrow = Y + n * args.n_out + yoff;
+            if (active) {
+                float* yrow = Y + (n0 + r) * args.n_out + yoff;
                 if (LANE) {
 #pragma unroll
-                    for (int j = 0; j < NB; ++j) yrow[int64_t(j) * d] = acc[j][0];
+                    for (int j = 0; j < NB; ++j) {
+                        if constexpr (DV == 4)
+                            __builtin_nontemporal_store(floatx4{acc[j][0], acc[j][1], acc[j][2], acc[j][3]},
+                                                        reinterpret_cast<floatx4*>(yrow + int64_t(j) * d));
+                        else
+                            __builtin_nontemporal_store(acc[j][0], yrow + int64_t(j) * d);
+                    }
                 } else {
-                    constexpr int NOUT = NB * DVX;
-                    if (NOUT % 4 == 0) {
+                    constexpr int NOUT = NB * DV;
+                    if constexpr (NOUT % 4 == 0) {
 #pragma unroll
-                        for (int v = 0; v < NOUT / 4; ++v) {
-                            float4 o;
-                            o.x = acc[(4 * v + 0) / DVX][(4 * v + 0) % DVX];
-                            o.y = acc[(4 * v + 1) / DVX][(4 * v + 1) % DVX];
-                            o.z = acc[(4 * v + 2) / DVX][(4 * v + 2) % DVX];
-                            o.w = acc[(4 * v + 3) / DVX][(4 * v + 3) % DVX];
-                            reinterpret_cast<float4*>(yrow)[v] = o;
-                        }
+                        for (int v = 0; v < NOUT / 4; ++v)
+                            __builtin_nontemporal_store(
+                                floatx4{acc[(4 * v + 0) / DV][(4 * v + 0) % DV], acc[(4 * v + 1) / DV][(4 * v + 1) % DV],
+                                        acc[(4 * v + 2) / DV][(4 * v + 2) % DV], acc[(4 * v + 3) / DV][(4 * v + 3) % DV]},
+                                reinterpret_cast<floatx4*>(yrow) + v);
                     } else {
 #pragma unroll
-                        for (int e = 0; e < NOUT; ++e) yrow[e] = acc[e / DVX][e % DVX];
+                        for (int e = 0; e < NOUT; ++e) __builtin_nontemporal_store(acc[e / DV][e % DV], yrow + e);
                     }
                 }
             }
         }
-        if (s + 1 < nsteps) store_lds((s + 1) & 1);
-        __syncthreads();
     }
 }
 
@@ -285,11 +254,17 @@ __global__ __launch_bounds__(kThreads, 2) void valu_kernel(const TX* __restrict_
 
 struct ValuGeom {
     bool lane;
-    int nb, g, p, at, dt, tiles_delta, n_tiles, contiguous;
-    int lds_row_bytes, lds_alpha_bytes, vw, r;
+    int dv, nb, g, p, at, dt, tiles_delta, n_tiles, contiguous, vw, insts, stages;
+    StageMap map;
 };
 
-int nb_for(int b, int c, int dv) { return nb_rule(b, c, dv); }
+// The largest tile width <= cap that splits n into equal tiles (as equal as
+// the tile count allows), so no tile is left nearly empty.
+int balanced(int n, int cap) {
+    if (cap < 1) return 0;
+    const int tiles = (n + cap - 1) / cap;
+    return (n + tiles - 1) / tiles;
+}
 
 bool geom_for(const Shape& s, int xt, ValuGeom* gm) {
     const int eb = elem_bytes(xt);
@@ -297,71 +272,116 @@ bool geom_for(const Shape& s, int xt, ValuGeom* gm) {
     const int b = s.b, c = s.c, d = s.d;
     if (!((b == 4 || b == 8 || b == 16) && (c == 4 || c == 8 || c == 16))) return false;
     gm->vw = vw;
-    gm->r = kRows;
+    StageMap& m = gm->map;
     if (d >= 8) {
         if (d % vw != 0) return false;
         gm->lane = true;
-        gm->nb = nb_for(b, c, 1);
+        gm->dv = (d % 4 == 0) ? 4 : 1;
+        gm->nb = nb_rule(b, c, gm->dv);
         gm->g = b / gm->nb;
-        gm->p = kThreads / gm->g;
-        if (d >= gm->p) {
-            gm->dt = gm->p;
+        gm->p = kConsumerThreads / gm->g;
+        const int span = gm->p * gm->dv;            // deltas one group covers
+        if (d >= span) {
+            gm->dt = span;
             gm->at = 1;
             gm->contiguous = 0;
-            gm->lds_row_bytes = c * gm->dt * eb;
-            gm->lds_alpha_bytes = gm->lds_row_bytes;
+            m.blocks = c;
+            m.blk_vec = span / vw;
+            m.pad_vec = 0;
+            m.gstride = d;
+            m.row_vec = c * m.blk_vec;
         } else {
             gm->dt = d;
-            gm->at = gm->p / d;
             gm->contiguous = 1;
-            // alpha' stride congruent to d words mod 64 banks (lanes reading
-            // consecutive (alpha', delta) then hit distinct banks), rounded to
-            // keep 16-byte alignment.
+            m.blk_vec = c * d / vw;
+            // alpha-slab pitch congruent to d elements modulo 256 bytes, so
+            // lanes reading consecutive (alpha, delta) hit consecutive banks
             const int slab = c * d * eb;
-            int stride = slab;
             const int want = (d * eb) % 256;
-            while ((stride % 256) != want || stride % 16 != 0) stride += 16;
-            gm->lds_alpha_bytes = stride;
-            gm->lds_row_bytes = gm->at * stride;
+            const int pad = ((want - slab) % 256 + 256) % 256;
+            if (pad % 16 != 0) return false;
+            m.pad_vec = pad / 16;
+            // as many alphas as the threads cover and one stage row holds
+            gm->at = balanced(s.a, std::min(span / d, kMaxInsts * 64 / (m.blk_vec + m.pad_vec)));
+            if (gm->at < 1) return false;
+            m.blocks = gm->at;
+            m.gstride = c * d;
+            m.row_vec = gm->at * (m.blk_vec + m.pad_vec);
         }
     } else {
         if (d != 1 && d != 2 && d != 4) return false;
         if ((c * d) % vw != 0) return false;
         gm->lane = false;
-        gm->nb = nb_for(b, c, d);
+        gm->dv = d;
+        gm->nb = nb_rule(b, c, d);
         gm->g = b / gm->nb;
-        gm->p = kThreads / gm->g;
-        gm->at = gm->p;
+        gm->p = kConsumerThreads / gm->g;
         gm->dt = d;
         gm->contiguous = 1;
+        m.blk_vec = c * d / vw;
         const int slab = c * d * eb;
-        // odd multiple of 16 bytes: 16 consecutive alpha' slabs start in
-        // distinct 16-byte bank groups.
-        gm->lds_alpha_bytes = (slab % 32 == 0) ? slab + 16 : slab;
-        gm->lds_row_bytes = gm->at * gm->lds_alpha_bytes;
+        // odd multiple of 16 bytes: 16 consecutive alpha slabs start in
+        // distinct 16-byte bank groups
+        m.pad_vec = (slab % 32 == 0) ? 1 : 0;
+        gm->at = balanced(s.a, std::min(gm->p, kMaxInsts * 64 / (m.blk_vec + m.pad_vec)));
+        if (gm->at < 1) return false;
+        m.blocks = gm->at;
+        m.gstride = c * d;
+        m.row_vec = gm->at * (m.blk_vec + m.pad_vec);
     }
-    const int tiles_alpha = (s.a + gm->at - 1) / gm->at;
-    gm->tiles_delta = gm->lane ? (d + gm->dt - 1) / gm->dt : 1;
-    if (gm->contiguous) gm->tiles_delta = 1;
-    const int64_t nt = int64_t(tiles_alpha) * gm->tiles_delta;
+    if (m.row_vec > kMaxInsts * 64) return false;
+    m.rows = std::max(1, std::min(16, kTargetVec / m.row_vec));
+    // the loader addresses a stage with 32-bit byte offsets
+    while (m.rows > 1 && int64_t(m.rows) * s.n_in * eb >= (int64_t(1) << 31)) --m.rows;
+    if (int64_t(m.rows) * s.n_in * eb >= (int64_t(1) << 31)) return false;
+    gm->insts = (m.rows * m.row_vec + 63) / 64;
+    // ring depth: as many stages as fit the per-workgroup LDS budget, 3..8,
+    // with the loader's wait count (stages - 2) * insts within vmcnt's range
+    gm->stages = std::max(3, std::min(8, kLdsPerGroup / (gm->insts * 1024)));
+    while (gm->stages > 3 && (gm->stages - 2) * gm->insts > 63) --gm->stages;
+    if ((gm->stages - 2) * gm->insts > 63) return false;
+    const int64_t tiles_alpha = (s.a + gm->at - 1) / gm->at;
+    gm->tiles_delta = gm->contiguous ? 1 : (d + gm->dt - 1) / gm->dt;
+    const int64_t nt = tiles_alpha * gm->tiles_delta;
     if (nt > (int64_t(1) << 30)) return false;
     gm->n_tiles = static_cast<int>(nt);
     return true;
 }
 
+// Rows per workgroup: a multiple of the stage rows, chosen so that the grid
+// is about one resident wave of workgroups (two per compute unit) with
+// equal shares, unless the tiles alone already fill it.
+int64_t rows_per_split(const ValuGeom& gm, int64_t batch, int num_cus, int rows_per_block) {
+    const int R = gm.map.rows;
+    const int64_t steps_total = (batch + R - 1) / R;
+    int64_t steps;
+    if (rows_per_block > 0) {
+        steps = std::max<int64_t>(1, (rows_per_block + R - 1) / R);
+    } else {
+        const int64_t resident = int64_t(std::max(num_cus, 1)) * 2;
+        const int64_t splits = std::max<int64_t>(1, resident / std::max(gm.n_tiles, 1));
+        steps = (steps_total + splits - 1) / splits;
+    }
+    steps = std::max<int64_t>(1, std::min(steps, steps_total));
+    return steps * R;
+}
+
 template <typename TX, typename TW, int B, int C>
 ks_status_t launch_bc(const FactorCall& f, const ValuGeom& gm, const ValuArgs& args, dim3 grid) {
-    const size_t lds = size_t(2) * gm.r * gm.lds_row_bytes;
+    const size_t lds = size_t(gm.stages) * gm.insts * 1024;
     const TX* X = static_cast<const TX*>(f.X);
     const TW* K = static_cast<const TW*>(f.W);
-    if (gm.lane) {
-        hipLaunchKernelGGL((valu_kernel<TX, TW, B, C, 1, true>), grid, dim3(kThreads), lds, f.stream, X, K, f.Y, args);
+    const dim3 block(kStreamThreads);
+    if (gm.lane && gm.dv == 4) {
+        hipLaunchKernelGGL((valu_kernel<TX, TW, B, C, 4, true>), grid, block, lds, f.stream, X, K, f.Y, args);
+    } else if (gm.lane) {
+        hipLaunchKernelGGL((valu_kernel<TX, TW, B, C, 1, true>), grid, block, lds, f.stream, X, K, f.Y, args);
     } else if (f.s.d == 1) {
-        hipLaunchKernelGGL((valu_kernel<TX, TW, B, C, 1, false>), grid, dim3(kThreads), lds, f.stream, X, K, f.Y, args);
+        hipLaunchKernelGGL((valu_kernel<TX, TW, B, C, 1, false>), grid, block, lds, f.stream, X, K, f.Y, args);
     } else if (f.s.d == 2) {
-        hipLaunchKernelGGL((valu_kernel<TX, TW, B, C, 2, false>), grid, dim3(kThreads), lds, f.stream, X, K, f.Y, args);
+        hipLaunchKernelGGL((valu_kernel<TX, TW, B, C, 2, false>), grid, block, lds, f.stream, X, K, f.Y, args);
     } else {
-        hipLaunchKernelGGL((valu_kernel<TX, TW, B, C, 4, false>), grid, dim3(kThreads), lds, f.stream, X, K, f.Y, args);
+        hipLaunchKernelGGL((valu_kernel<TX, TW, B, C, 4, false>), grid, block, lds, f.stream, X, K, f.Y, args);
     }
     return hipGetLastError() == hipSuccess ? KS_OK : KS_ERR_HIP;
 }
@@ -388,27 +408,6 @@ ks_status_t launch_types(const FactorCall& f, const ValuGeom& gm, const ValuArgs
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-void split_rows(const ValuGeom& gm, int64_t batch, int num_cus, int rows_per_block,
-                int* row_splits, int* steps_per_split) {
-    const int64_t steps_total = (batch + gm.r - 1) / gm.r;
-    int64_t splits;
-    if (rows_per_block > 0) {
-        const int64_t spb = std::max<int64_t>(1, (rows_per_block + gm.r - 1) / gm.r);
-        splits = (steps_total + spb - 1) / spb;
-    } else {
-        // About eight workgroups per compute unit in total, but at least
-        // 32 row steps (128 rows) per workgroup so the weight load amortises.
-        const int64_t want = int64_t(std::max(num_cus, 1)) * 8;
-        splits = std::max<int64_t>(1, want / std::max(gm.n_tiles, 1));
-        splits = std::min(splits, std::max<int64_t>(1, steps_total / 32));
-    }
-    splits = std::max<int64_t>(1, std::min(splits, steps_total));
-    const int64_t spp = (steps_total + splits - 1) / splits;
-    splits = (steps_total + spp - 1) / spp;
-    *row_splits = static_cast<int>(splits);
-    *steps_per_split = static_cast<int>(spp);
-}
-
 }  // namespace
 
 bool valu_supports(const Shape& s, int xt, int wt) {
@@ -421,24 +420,25 @@ int valu_describe(const Shape& s, int xt, int wt, int64_t batch, int num_cus, ch
     (void)wt;
     ValuGeom gm;
     if (!geom_for(s, xt, &gm)) return std::snprintf(buf, len, "valu: unsupported");
-    int splits = 0, spp = 0;
-    split_rows(gm, batch, num_cus, 0, &splits, &spp);
+    const int64_t rps = rows_per_split(gm, batch, num_cus, 0);
     return std::snprintf(buf, len,
-                         "valu %s: nb=%d groups=%d alphas/tile=%d deltas/tile=%d tiles=%d "
-                         "row_splits=%d rows/wg=%d lds=%d",
-                         gm.lane ? "lane" : "slab", gm.nb, gm.g, gm.at, gm.dt, gm.n_tiles, splits,
-                         spp * gm.r, 2 * gm.r * gm.lds_row_bytes);
+                         "valu %s dv=%d: nb=%d groups=%d alphas/tile=%d deltas/tile=%d tiles=%d "
+                         "rows/stage=%d rows/wg=%lld wgs=%lld stages=%d x %d KB",
+                         gm.lane ? "lane" : "slab", gm.dv, gm.nb, gm.g, gm.at, gm.dt, gm.n_tiles,
+                         gm.map.rows, static_cast<long long>(rps),
+                         static_cast<long long>(gm.n_tiles * ((batch + rps - 1) / std::max<int64_t>(rps, 1))),
+                         gm.stages, gm.insts);
 }
 
 ks_status_t launch_valu(const FactorCall& f) {
     ValuGeom gm;
     if (!geom_for(f.s, f.xt, &gm)) return KS_ERR_UNSUPPORTED;
-    if (!aligned16(f.X) || !aligned16(f.W) || !aligned16(f.Y)) return KS_ERR_UNSUPPORTED;
+    if (!aligned16(f.X) || !aligned16(f.Y)) return KS_ERR_UNSUPPORTED;
     if ((f.s.n_in * elem_bytes(f.xt)) % 16 != 0 || (f.s.n_out * 4) % 16 != 0) return KS_ERR_UNSUPPORTED;
-    int splits = 0, spp = 0;
-    split_rows(gm, f.batch, f.num_cus, f.rows_per_block, &splits, &spp);
+    const int64_t rps = rows_per_split(gm, f.batch, f.num_cus, f.rows_per_block);
+    const int64_t splits = (f.batch + rps - 1) / rps;
     const int64_t blocks = int64_t(gm.n_tiles) * splits;
-    if (blocks > 0x7fffffff) return KS_ERR_UNSUPPORTED;
+    if (blocks > 0x7fffffff || rps > 0x7fffffff) return KS_ERR_UNSUPPORTED;
     ValuArgs args;
     args.a = f.s.a;
     args.d = f.s.d;
@@ -449,10 +449,12 @@ ks_status_t launch_valu(const FactorCall& f) {
     args.dt = gm.dt;
     args.tiles_delta = gm.tiles_delta;
     args.n_tiles = gm.n_tiles;
-    args.steps_per_split = spp;
-    args.lds_row_bytes = gm.lds_row_bytes;
-    args.lds_alpha_bytes = gm.lds_alpha_bytes;
+    args.rows_per_split = static_cast<int>(rps);
     args.contiguous = gm.contiguous;
+    args.insts = gm.insts;
+    args.stages = gm.stages;
+    args.xcd_remap = gm.contiguous ? 0 : 1;
+    args.map = gm.map;
     const dim3 grid(static_cast<unsigned>(blocks));
     if (f.xt == kF32 && f.wt == kF32) return launch_types<float, float>(f, gm, args, grid);
     if (f.xt == kBF16 && f.wt == kBF16) return launch_types<bf16_t, bf16_t>(f, gm, args, grid);

@@ -23,8 +23,9 @@ LIB_PATH = os.path.join(_PKG, "lib", "libks.so")
 # ks_dtype_t
 DTYPE_F32, DTYPE_BF16, DTYPE_BF16W = 0, 1, 2
 # ks_kernel_t
-KERNEL_AUTO, KERNEL_GENERIC, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2, 3
-KERNELS = {"auto": KERNEL_AUTO, "generic": KERNEL_GENERIC, "valu": KERNEL_VALU, "mfma": KERNEL_MFMA}
+KERNEL_AUTO, KERNEL_GENERIC, KERNEL_VALU, KERNEL_MFMA, KERNEL_MFMA_LDS = 0, 1, 2, 3, 4
+KERNELS = {"auto": KERNEL_AUTO, "generic": KERNEL_GENERIC, "valu": KERNEL_VALU, "mfma": KERNEL_MFMA,
+           "mfma_lds": KERNEL_MFMA_LDS}
 # chain flags
 CHAIN_AUTO, CHAIN_NO_FUSE = 0, 1
 # ks_status_t

@@ -37,7 +37,7 @@ def try_family(p, Xt, Wt, kernel):
     return Y
 
 
-ALL_FAMILIES = ["auto", "generic", "valu", "mfma"]
+ALL_FAMILIES = ["auto", "generic", "valu", "mfma", "mfma_lds"]
 
 # ---------------------------------------------------------------- small workloads
 
