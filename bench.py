@@ -65,7 +65,60 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain device copy of known size (for counter calibration)")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of a "
+                         "`--calib-copy` run into profiles/traffic_counters.json and exit")
     return ap.parse_args()
+
+
+CALIB_BYTES = 256 * 2 ** 20      # the --calib-copy device copy reads and writes this many bytes
+
+
+def ingest_counters(args) -> int:
+    """Per-launch HBM bytes of the workload's KS kernel(s) from two counter
+    runs of the same command. FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
+    are each scaled by what the same counter reads for the calibration copy
+    (CALIB_BYTES read and written), then averaged over the KS dispatches."""
+    import csv
+    from collections import defaultdict
+
+    def per_dispatch(path, counter):
+        vals = defaultdict(float)
+        names = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = r["Dispatch_Id"]
+                vals[key] += float(r["Counter_Value"])
+                names[key] = r["Kernel_Name"]
+        return vals, names
+
+    out = {}
+    scaled = {}
+    for path, counter in ((args.ingest_counters[0], "FETCH_SIZE"), (args.ingest_counters[1], "WRITE_SIZE")):
+        vals, names = per_dispatch(path, counter)
+        calib = [vals[k] for k, n in names.items() if "copyBuffer" in n or "copy_kernel" in n]
+        ks = [vals[k] for k, n in names.items() if "ks::" in n]
+        if not calib or not ks:
+            print("no calibration copy or no KS dispatch in %s" % path, file=sys.stderr)
+            return 1
+        factor = CALIB_BYTES / (max(calib) * 1024.0)
+        scaled[counter] = (sum(ks) / len(ks)) * 1024.0 * factor
+        out[counter.lower() + "_factor"] = round(factor, 4)
+        out[counter.lower() + "_kib_per_launch"] = round(sum(ks) / len(ks), 1)
+        out[counter.lower() + "_launches"] = len(ks)
+    key = args.workload + ":" + args.dtype
+    db = {}
+    if os.path.exists(TRAFFIC_FILE):
+        db = json.load(open(TRAFFIC_FILE))
+    out["bytes_per_launch"] = int(scaled["FETCH_SIZE"] + scaled["WRITE_SIZE"])
+    out["source_hash"] = kernel_source_hash()
+    db[key] = out
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(db, f, indent=1, sort_keys=True)
+    print(json.dumps({key: out}))
+    return 0
 
 
 def factor_bytes(p, x_bytes, w_bytes, batch):
@@ -75,6 +128,8 @@ def factor_bytes(p, x_bytes, w_bytes, batch):
 
 def main():
     args = parse()
+    if args.ingest_counters:
+        return ingest_counters(args)
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(rows would shard across GPUs with no exchange); run with --gpus 1.",
@@ -179,7 +234,7 @@ def main():
             traffic = None
 
     if args.calib_copy:
-        src = torch.empty(256 * 2 ** 20 // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
