@@ -188,10 +188,9 @@ ks_status_t launch_typed(const Shape& s0, const Shape& s1, const void* W0, const
     if (blocks > 0x7fffffff) return KS_ERR_UNSUPPORTED;
     const size_t lds = size_t(kStages) * (kInsts * int(sizeof(TX)) / 4) * 1024 +
                        size_t(kRows) * kBT * kZPitch * sizeof(float);
-    hipLaunchKernelGGL((fused_pair_kernel<TX, TW>), dim3(static_cast<unsigned>(blocks)), dim3(kStreamThreads),
-                       lds, stream, static_cast<const TX*>(X), static_cast<const TW*>(W0),
-                       static_cast<const TW*>(W1), Y, args);
-    return hipGetLastError() == hipSuccess ? KS_OK : KS_ERR_HIP;
+    return launch_kernel(fused_pair_kernel<TX, TW>, dim3(static_cast<unsigned>(blocks)), dim3(kStreamThreads),
+                         lds, stream, static_cast<const TX*>(X), static_cast<const TW*>(W0),
+                         static_cast<const TW*>(W1), Y, args);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -46,10 +46,9 @@ ks_status_t launch_typed(const FactorCall& f) {
     const int64_t blocks_needed = (total + 255) / 256;
     const int64_t cap = int64_t(std::max(f.num_cus, 1)) * 64;
     const unsigned blocks = static_cast<unsigned>(std::max<int64_t>(1, std::min(blocks_needed, cap)));
-    hipLaunchKernelGGL((generic_kernel<TX, TW>), dim3(blocks), dim3(256), 0, f.stream,
-                       static_cast<const TX*>(f.X), static_cast<const TW*>(f.W), f.Y,
-                       f.s.a, f.s.b, f.s.c, f.s.d, total);
-    return hipGetLastError() == hipSuccess ? KS_OK : KS_ERR_HIP;
+    return launch_kernel(generic_kernel<TX, TW>, dim3(blocks), dim3(256), 0, f.stream,
+                         static_cast<const TX*>(f.X), static_cast<const TW*>(f.W), f.Y,
+                         f.s.a, f.s.b, f.s.c, f.s.d, total);
 }
 
 }  // namespace

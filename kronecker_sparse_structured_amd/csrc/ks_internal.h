@@ -4,12 +4,35 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <tuple>
+#include <utility>
 
 #include <hip/hip_runtime.h>
 
 #include "ks.h"
 
 namespace ks {
+
+// Launches `kernel` and returns the status of this launch alone.
+// hipLaunchKernel reports it directly; hipGetLastError would also return a
+// failure left behind by an earlier, unrelated HIP call in this thread (for
+// example a stream or event query that found work still pending).
+template <typename... Params, size_t... I>
+ks_status_t launch_kernel_impl(void (*kernel)(Params...), dim3 grid, dim3 block, size_t lds,
+                               hipStream_t stream, std::index_sequence<I...>, std::tuple<Params...>& p) {
+    void* ptrs[] = {static_cast<void*>(&std::get<I>(p))..., nullptr};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, lds, stream) == hipSuccess
+               ? KS_OK
+               : KS_ERR_HIP;
+}
+
+template <typename... Params, typename... Args>
+ks_status_t launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                          Args&&... args) {
+    static_assert(sizeof...(Params) == sizeof...(Args), "argument count");
+    std::tuple<Params...> p(std::forward<Args>(args)...);
+    return launch_kernel_impl(kernel, grid, block, lds, stream, std::index_sequence_for<Params...>{}, p);
+}
 
 // Element type codes for X and W.
 enum ElemType : int { kF32 = 0, kBF16 = 1 };

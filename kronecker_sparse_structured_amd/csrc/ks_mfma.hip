@@ -341,9 +341,8 @@ int64_t rows_per_split(const MfmaGeom& g, int64_t batch, int num_cus, int rows_p
 template <typename TX, typename TW, int B, int C>
 ks_status_t launch_bc(const FactorCall& f, const MfmaGeom& g, const MfmaArgs& args, dim3 grid) {
     if constexpr (mfma_stage_insts(B, C, int(sizeof(TX))) <= 63) {
-        hipLaunchKernelGGL((mfma_kernel<TX, TW, B, C>), grid, dim3(kStreamThreads), g.lds, f.stream,
-                           static_cast<const TX*>(f.X), static_cast<const TW*>(f.W), f.Y, args);
-        return hipGetLastError() == hipSuccess ? KS_OK : KS_ERR_HIP;
+        return launch_kernel(mfma_kernel<TX, TW, B, C>, grid, dim3(kStreamThreads), g.lds, f.stream,
+                             static_cast<const TX*>(f.X), static_cast<const TW*>(f.W), f.Y, args);
     } else {
         return KS_ERR_UNSUPPORTED;
     }

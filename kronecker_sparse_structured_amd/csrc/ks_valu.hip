@@ -373,17 +373,16 @@ ks_status_t launch_bc(const FactorCall& f, const ValuGeom& gm, const ValuArgs& a
     const TW* K = static_cast<const TW*>(f.W);
     const dim3 block(kStreamThreads);
     if (gm.lane && gm.dv == 4) {
-        hipLaunchKernelGGL((valu_kernel<TX, TW, B, C, 4, true>), grid, block, lds, f.stream, X, K, f.Y, args);
+        return launch_kernel(valu_kernel<TX, TW, B, C, 4, true>, grid, block, lds, f.stream, X, K, f.Y, args);
     } else if (gm.lane) {
-        hipLaunchKernelGGL((valu_kernel<TX, TW, B, C, 1, true>), grid, block, lds, f.stream, X, K, f.Y, args);
+        return launch_kernel(valu_kernel<TX, TW, B, C, 1, true>, grid, block, lds, f.stream, X, K, f.Y, args);
     } else if (f.s.d == 1) {
-        hipLaunchKernelGGL((valu_kernel<TX, TW, B, C, 1, false>), grid, block, lds, f.stream, X, K, f.Y, args);
+        return launch_kernel(valu_kernel<TX, TW, B, C, 1, false>, grid, block, lds, f.stream, X, K, f.Y, args);
     } else if (f.s.d == 2) {
-        hipLaunchKernelGGL((valu_kernel<TX, TW, B, C, 2, false>), grid, block, lds, f.stream, X, K, f.Y, args);
+        return launch_kernel(valu_kernel<TX, TW, B, C, 2, false>, grid, block, lds, f.stream, X, K, f.Y, args);
     } else {
-        hipLaunchKernelGGL((valu_kernel<TX, TW, B, C, 4, false>), grid, block, lds, f.stream, X, K, f.Y, args);
+        return launch_kernel(valu_kernel<TX, TW, B, C, 4, false>, grid, block, lds, f.stream, X, K, f.Y, args);
     }
-    return hipGetLastError() == hipSuccess ? KS_OK : KS_ERR_HIP;
 }
 
 template <typename TX, typename TW, int B>

@@ -55,6 +55,16 @@ class ks_options_t(ctypes.Structure):
 _lib = None
 
 
+def _hip_runtimes() -> set:
+    """Paths of the HIP runtime libraries mapped into this process."""
+    try:
+        with open("/proc/self/maps") as f:
+            return {line.split()[-1] for line in f
+                    if len(line.split()) >= 6 and "libamdhip64.so" in line.split()[-1]}
+    except OSError:
+        return set()
+
+
 def load(path: str = LIB_PATH):
     """Load libks.so (raises if it has not been built)."""
     global _lib
@@ -64,7 +74,15 @@ def load(path: str = LIB_PATH):
         raise FileNotFoundError(
             "libks.so not found at %s; build it with "
             "`python -m kronecker_sparse_structured_amd.build`" % path)
+    # torch ships its own copy of the HIP runtime. Load it first so that
+    # libks binds to that copy: with two runtimes in one process, pointers
+    # and streams from torch are unknown to the one libks calls.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
+    runtimes = _hip_runtimes()
+    if len(runtimes) > 1:
+        raise RuntimeError("more than one HIP runtime is loaded in this process (%s); "
+                           "libks must share torch's" % ", ".join(sorted(runtimes)))
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.ks_status_string.argtypes = [i32]
     lib.ks_status_string.restype = ctypes.c_char_p

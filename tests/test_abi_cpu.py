@@ -156,3 +156,15 @@ def test_chain_plan():
     assert libks.ks_chain_groups(three, 10, libks.DTYPE_F32, libks.CHAIN_NO_FUSE) == [[0], [1], [2]]
     groups = libks.ks_chain_groups(three, 10, libks.DTYPE_F32, libks.CHAIN_AUTO)
     assert sum(len(g) for g in groups) == 3 and all(len(g) in (1, 2) for g in groups)
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    """Loading libks before torch must still leave a single HIP runtime in
+    the process (torch bundles its own; libks has to bind to that one)."""
+    import sys
+    code = ("from kronecker_sparse_structured_amd import libks; libks.load(); "
+            "print(len(libks._hip_runtimes()))")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip().splitlines()[-1] == "1"

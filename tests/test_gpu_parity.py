@@ -323,3 +323,41 @@ def test_butterfly_single_factor(bf16, k):
     Y = run_factor(p, to_dev(X, xb), to_dev(Ws[k], bf16))
     torch.cuda.synchronize()
     check_factor(p, X, Ws[k], Y.cpu().numpy(), bf16=xb, w_bf16=bf16)
+
+
+def _hip_runtime():
+    """The HIP runtime library mapped into this process (None if not exactly one)."""
+    import ctypes
+    paths = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            name = line.split()[-1] if len(line.split()) >= 6 else ""
+            if "libamdhip64.so" in name:
+                paths.add(name)
+    if len(paths) != 1:
+        return None
+    return ctypes.CDLL(paths.pop())
+
+
+def test_launch_status_ignores_earlier_unrelated_error():
+    """A failed HIP call made before ks_matmul (here a device attribute query
+    on a device that does not exist) must not be reported as this launch's
+    failure."""
+    import ctypes
+    wl = datagen.get("tiny")
+    X, (W,) = datagen.draw(wl)
+    p = wl.patterns[0]
+    Xt, Wt = to_dev(X), to_dev(W)
+    torch.cuda.synchronize()
+    hip = _hip_runtime()
+    if hip is None:
+        pytest.skip("could not identify the HIP runtime of this process")
+    v = ctypes.c_int(0)
+    assert hip.hipDeviceGetAttribute(ctypes.byref(v), 0, 1 << 20) != 0
+    for kernel in ALL_FAMILIES:
+        Y = try_family(p, Xt, Wt, kernel)
+        if Y is None:
+            continue
+        torch.cuda.synchronize()
+        check_factor(p, X, W, Y.cpu().numpy())
+    hip.hipGetLastError()
