@@ -87,15 +87,24 @@ typedef enum ks_kernel_t {
     KS_KERNEL_AUTO = 0,     /* the planner's choice (what ks_matmul runs)        */
     KS_KERNEL_GENERIC = 1,  /* one thread per output, any pattern                */
     KS_KERNEL_VALU = 2,     /* weights in registers, fp32 FMA (b, c <= 16)       */
-    KS_KERNEL_MFMA = 3,     /* matrix cores (b, c >= 16): the register-direct
-                               variant for small d, else LDS-staged tiles        */
-    KS_KERNEL_MFMA_LDS = 4  /* matrix cores, LDS-staged tiles only               */
+    KS_KERNEL_MFMA = 3,     /* matrix cores (b, c >= 16), LDS-staged tiles       */
+    KS_KERNEL_MFMA_LDS = 4  /* same kernels as KS_KERNEL_MFMA (kept for ABI)     */
 } ks_kernel_t;
+
+/* Who stores Y in the MFMA kernels, for ks_options_t.store_waves. */
+typedef enum ks_store_waves_t {
+    KS_STORE_AUTO = 0,      /* the planner's choice                              */
+    KS_STORE_COMPUTE = 1,   /* the compute waves, after each step's MFMAs        */
+    KS_STORE_DEDICATED = 2  /* a storer wave, overlapped with the next step's
+                               MFMAs (needs LDS for two Y tiles)                 */
+} ks_store_waves_t;
 
 typedef struct ks_options_t {
     int32_t kernel;         /* a ks_kernel_t value                               */
     int32_t rows_per_block; /* 0 = planner default; else rows per workgroup step */
-    int32_t reserved[6];    /* must be zero                                      */
+    int32_t store_waves;    /* a ks_store_waves_t value; MFMA family only;
+                               KS_ERR_UNSUPPORTED if the tile cannot use it      */
+    int32_t reserved[5];    /* must be zero                                      */
 } ks_options_t;
 
 /* Chain flags. */

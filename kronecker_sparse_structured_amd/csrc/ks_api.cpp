@@ -58,7 +58,8 @@ ks_status_t check_options(const ks_options_t* opt) {
     if (!opt) return KS_OK;
     if (opt->kernel < KS_KERNEL_AUTO || opt->kernel > KS_KERNEL_MFMA_LDS) return KS_ERR_INVALID;
     if (opt->rows_per_block < 0 || opt->rows_per_block > 4096) return KS_ERR_INVALID;
-    for (int i = 0; i < 6; ++i)
+    if (opt->store_waves < KS_STORE_AUTO || opt->store_waves > KS_STORE_DEDICATED) return KS_ERR_INVALID;
+    for (int i = 0; i < 5; ++i)
         if (opt->reserved[i] != 0) return KS_ERR_INVALID;
     return KS_OK;
 }
@@ -215,6 +216,7 @@ ks_status_t ks_matmul_ex(ks_pattern_t p, const void* W, const void* X, void* Y,
     f.s = s; f.xt = xt; f.wt = wt; f.W = W; f.X = X; f.Y = static_cast<float*>(Y);
     f.batch = batch; f.stream = stream;
     f.rows_per_block = opt ? opt->rows_per_block : 0;
+    f.store_waves = opt ? opt->store_waves : KS_STORE_AUTO;
     st = current_cus(&f.num_cus);
     if (st != KS_OK) return st;
     return run_factor(kernel, f);
@@ -293,6 +295,7 @@ ks_status_t ks_chain_matmul(const ks_pattern_t* p, int n, const void* const* W,
             ks::FactorCall f;
             f.s = plan.shapes[k]; f.xt = cur_t; f.wt = plan.wt; f.W = W[k]; f.X = cur; f.Y = out;
             f.batch = batch; f.stream = stream; f.num_cus = cus; f.rows_per_block = 0;
+            f.store_waves = KS_STORE_AUTO;
             st = run_factor(KS_KERNEL_AUTO, f);
         }
         if (st != KS_OK) return st;

@@ -57,14 +57,15 @@ struct FactorCall {
     hipStream_t stream;
     int num_cus;           // compute units of the current device
     int rows_per_block;    // 0 = default
+    int store_waves;       // ks_store_waves_t (MFMA family)
 };
 
 // Kernel launchers. Each returns KS_OK, KS_ERR_UNSUPPORTED when the family
 // cannot run this factor, or KS_ERR_HIP when the launch fails.
 ks_status_t launch_generic(const FactorCall& f);
 ks_status_t launch_valu(const FactorCall& f);
-ks_status_t launch_mfma(const FactorCall& f);       // direct variant, else LDS-staged
-ks_status_t launch_mfma_lds(const FactorCall& f);   // LDS-staged variant only
+ks_status_t launch_mfma(const FactorCall& f);
+ks_status_t launch_mfma_lds(const FactorCall& f);   // the same kernels
 
 // Whether a family can run a factor (pure host; no HIP call).
 bool valu_supports(const Shape& s, int xt, int wt);

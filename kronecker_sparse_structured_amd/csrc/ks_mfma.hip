@@ -37,9 +37,29 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kLdsPerGroup = 80 * 1024;   // two workgroups per compute unit
+constexpr int kStoreQ = 4;                // storer: row-chunk vectors per lane
 
-// Tile shape of one (b, c) instantiation.
-template <int B, int C>
+// Rows per stage: 16 per row of waves (the four waves split N first).
+__host__ __device__ constexpr int mfma_rows(int b) { return 16 * (4 / (b / 16 < 4 ? b / 16 : 4)); }
+
+// N tiles (16 outputs each) per wave.
+__host__ __device__ constexpr int mfma_ntw(int b) { return b / 16 < 4 ? 1 : b / 64; }
+
+// Pairs per tile, a power of two: the B operands take TP * NTW * c / 4
+// VGPRs, at most 64; an X stage (R rows of TP * c elements of eb bytes)
+// stays within 48 KB; and three X stages plus the fp32 Y tile (R rows of
+// TP * b) stay within 150 KB of LDS.
+__host__ __device__ constexpr int mfma_tp(int b, int c, int eb) {
+    int tp = 256 / (mfma_ntw(b) * c);
+    if (tp < 1) tp = 1;
+    while (tp > 1 && (mfma_rows(b) * tp * c * eb > 48 * 1024 ||
+                      3 * mfma_rows(b) * tp * c * eb + mfma_rows(b) * tp * b * 4 > 150 * 1024))
+        tp /= 2;
+    return tp;
+}
+
+// Tile shape of one (b, c, element size) instantiation.
+template <int B, int C, int EB>
 struct MfmaShape {
     static constexpr int NT = B / 16;                  // 16-wide N tiles
     static constexpr int WN = NT < 4 ? NT : 4;         // waves along N
@@ -47,19 +67,14 @@ struct MfmaShape {
     static constexpr int WR = 4 / WN;                  // waves along rows
     static constexpr int KS = C / 4;                   // MFMA K steps
     static constexpr int R = 16 * WR;                  // rows per stage
-    // Pairs per tile: the B operands take TP * NTW * KS VGPRs, at most 64.
-    static constexpr int TP = (256 / (NTW * C)) < 1 ? 1 : 256 / (NTW * C);
+    static constexpr int TP = mfma_tp(B, C, EB);       // pairs per tile
+    static_assert(R == mfma_rows(B) && NTW == mfma_ntw(B), "shape helpers");
 };
-
-// MfmaShape<b, c>::TP for runtime b, c.
-__host__ __device__ constexpr int mfma_tp(int b, int c) {
-    return (256 / ((b / 16 < 4 ? 1 : b / 64) * c)) < 1 ? 1 : 256 / ((b / 16 < 4 ? 1 : b / 64) * c);
-}
 
 // Loader instructions (KB) per X stage: R rows of at most TP * c elements,
 // plus one pad vector per row.
 __host__ __device__ constexpr int mfma_stage_insts(int b, int c, int eb) {
-    return ((16 * (4 / (b / 16 < 4 ? b / 16 : 4))) * (mfma_tp(b, c) * c * eb / 16 + 1) + 63) / 64;
+    return (mfma_rows(b) * (mfma_tp(b, c, eb) * c * eb / 16 + 1) + 63) / 64;
 }
 
 struct MfmaArgs {
@@ -72,18 +87,105 @@ struct MfmaArgs {
     int qy;                  // Y vectors in one row chunk of the tile
     int insts;               // loader instructions per stage (stage = insts KB of LDS)
     int stages;              // LDS ring depth
+    int ytile_bytes;         // LDS bytes of one Y tile buffer
     int xcd_remap;           // 1: renumber workgroups so neighbouring tiles share an XCD
     StageMap xmap;           // LDS layout of an X stage
     RowChunk yc;             // LDS layout of the Y tile and its global stores
 };
 
-template <typename TX, typename TW, int B, int C>
-__global__ __launch_bounds__(kStreamThreads) void mfma_kernel(const TX* __restrict__ X,
-                                                              const TW* __restrict__ K,
-                                                              float* __restrict__ Y, MfmaArgs args) {
-    using S = MfmaShape<B, C>;
-    constexpr int TP = S::TP, NTW = S::NTW, WN = S::WN, KS = S::KS, R = S::R;
+// The threads that store Y tiles (the storer waves, or the compute waves
+// when there are none) and their share of a tile. A row chunk of qy vectors
+// needs S = ceil(qy / 64) waves' worth of lanes. With W >= S waves, wave w
+// takes the 64 vectors of slot w % S in rows g, g + G, ... (g = w / S,
+// G = W / S); with fewer waves, every wave takes slots w, w + W, ... of every
+// row. Vector offsets are the same in every row and step, so they are
+// computed once.
+struct StoreTeam {
+    int g, G;                 // first row and row stride of this wave
+    int nq;                   // slots of this wave (wave-uniform, <= kStoreQ)
+    int gq[kStoreQ];          // per slot: element offset in the Y row chunk
+    int lq[kStoreQ];          // per slot: byte offset in the LDS row
+    bool ok[kStoreQ];         // per slot: this lane has a vector there
+};
+
+template <typename A>
+__device__ __forceinline__ void make_store_team(const A& args, int tid, int nthreads, int at_eff, int dt_eff,
+                                                StoreTeam* st) {
+    const int W = nthreads / 64, w = tid >> 6, lane = tid & 63;
+    const int S = (args.qy + 63) / 64;
+    int first, stride;
+    if (S <= W) {
+        st->G = W / S;
+        st->g = w / S;
+        st->nq = st->g < st->G ? 1 : 0;
+        first = 64 * (w % S) + lane;
+        stride = 0;
+    } else {
+        st->G = 1;
+        st->g = 0;
+        st->nq = min(kStoreQ, (S - w + W - 1) / W);
+        first = 64 * w + lane;
+        stride = 64 * W;
+    }
+#pragma unroll
+    for (int j = 0; j < kStoreQ; ++j) {
+        const int q = first + stride * j;
+        st->ok[j] = false;
+        st->gq[j] = st->lq[j] = 0;
+        if (j < st->nq && q < args.qy)
+            chunk_vector(args.yc, q, 4, at_eff, dt_eff, &st->gq[j], &st->lq[j], &st->ok[j]);
+    }
+}
+
+// Stores rows [0, rows) of a Y tile staged in LDS at ys (R rows) to the Y
+// rows that start at yrow0 (the tile's chunk of its first row). Per slot,
+// RB rows at a time: all their LDS reads first (no branch between
+// them), then the 16-byte nontemporal stores, so the LDS latency is paid
+// once per batch. Rows past `rows` are read (clamped into the buffer) but
+// not stored.
+template <int RB, typename A>
+__device__ __forceinline__ void store_tile_rows(const A& args, const StoreTeam& st, const unsigned char* ys,
+                                                float* yrow0, int rows, int R) {
+    // row phase, stride and slot count are the same on every lane of a wave
+    const int g = __builtin_amdgcn_readfirstlane(st.g);
+    const int G = __builtin_amdgcn_readfirstlane(st.G);
+    const int nq = __builtin_amdgcn_readfirstlane(st.nq);
+    const int64_t rstride = int64_t(G) * args.n_out;        // elements between a wave's rows
+    const int lstride = G * args.yc.lds_row;                 // LDS bytes between a wave's rows
+#pragma unroll
+    for (int j = 0; j < kStoreQ; ++j) {
+        if (j >= nq) break;
+        const unsigned char* yl = ys + st.lq[j] + g * args.yc.lds_row;
+        float* yg = yrow0 + st.gq[j] + int64_t(g) * args.n_out;
+        for (int r0 = g; r0 < rows; r0 += G * RB) {
+            u32x4 v[RB];
+#pragma unroll
+            for (int rr = 0; rr < RB; ++rr) {
+                // rows past R (possible only in the last batch) re-read row R - 1
+                const int lofs = r0 + rr * G < R ? rr * lstride : (R - 1 - r0) * args.yc.lds_row;
+                v[rr] = *reinterpret_cast<const u32x4*>(yl + lofs);
+            }
+#pragma unroll
+            for (int rr = 0; rr < RB; ++rr)
+                if (st.ok[j] && r0 + rr * G < rows)
+                    __builtin_nontemporal_store(v[rr], reinterpret_cast<u32x4*>(yg + rr * rstride));
+            yl += RB * lstride;
+            yg += RB * rstride;
+        }
+    }
+}
+
+// NS = 0: the four compute waves also store each Y tile, after an LDS
+// barrier. NS > 0: NS storer waves store tile s-1 from one of two Y buffers
+// while the compute waves run the MFMAs of step s into the other, so the
+// stores drain during the contraction instead of after it.
+template <typename TX, typename TW, int B, int C, int NS>
+__global__ __launch_bounds__(kStreamThreads + 64 * NS) void mfma_kernel(const TX* __restrict__ X,
+                                                                        const TW* __restrict__ K,
+                                                                        float* __restrict__ Y, MfmaArgs args) {
     constexpr int EB = int(sizeof(TX));
+    using S = MfmaShape<B, C, EB>;
+    constexpr int TP = S::TP, NTW = S::NTW, WN = S::WN, KS = S::KS, R = S::R;
     constexpr int VWX = 16 / EB;
     constexpr int kMaxInsts = mfma_stage_insts(B, C, EB);
     static_assert(kMaxInsts <= 63, "vmcnt is six bits");
@@ -91,7 +193,7 @@ __global__ __launch_bounds__(kStreamThreads) void mfma_kernel(const TX* __restri
     const int kStages = args.stages;
 
     extern __shared__ __align__(16) unsigned char lds[];
-    unsigned char* const ys = lds + kStages * kStageBytes;
+    unsigned char* const ys0 = lds + kStages * kStageBytes;
 
     const int t = threadIdx.x;
     const int blk = args.xcd_remap ? xcd_logical_block(blockIdx.x, gridDim.x) : int(blockIdx.x);
@@ -114,6 +216,26 @@ __global__ __launch_bounds__(kStreamThreads) void mfma_kernel(const TX* __restri
     const int nsteps = static_cast<int>((row_end - row_begin + R - 1) / R);
     const int xrow_bytes = args.xmap.row_vec * 16;
     const int xblk_bytes = args.xmap.blk_vec * 16;   // no per-block padding in X stages
+
+    if constexpr (NS > 0) {
+        if (t >= kStreamThreads) {
+            // ---------------------------------------------------- storer waves
+            StoreTeam team;
+            make_store_team(args, t - kStreamThreads, 64 * NS, at_eff, dt_eff, &team);
+            auto store_tile = [&](int s) {
+                const int64_t n0 = row_begin + int64_t(s) * R;
+                store_tile_rows<8>(args, team, ys0 + (s & 1) * args.ytile_bytes, Y + n0 * args.n_out + yg0,
+                                static_cast<int>(min(int64_t(R), row_end - n0)), R);
+            };
+            for (int s = 0; s < nsteps; ++s) {
+                lds_barrier();                               // stage s ready
+                if (s > 0) store_tile(s - 1);
+                lds_barrier();                               // Y tile s written
+            }
+            store_tile(nsteps - 1);
+            return;
+        }
+    }
 
     if (t >= kConsumerThreads) {
         // ------------------------------------------------------ loader wave
@@ -168,12 +290,15 @@ __global__ __launch_bounds__(kStreamThreads) void mfma_kernel(const TX* __restri
         }
     }
 
+    StoreTeam team;
+    if constexpr (NS == 0) make_store_team(args, t, kConsumerThreads, at_eff, dt_eff, &team);
 
     const int arow = wr * 16 + (lane & 15);       // A operand row of this lane
     const int akk = lane >> 4;                    // A operand k (gamma within a step)
     for (int s = 0; s < nsteps; ++s) {
         lds_barrier();                                                   // stage s ready
         const unsigned char* xcur = lds + (s % kStages) * kStageBytes;
+        unsigned char* const ys = NS > 0 ? ys0 + (s & 1) * args.ytile_bytes : ys0;
 #pragma unroll
         for (int p = 0; p < TP; ++p) {
             if (!pv[p]) continue;
@@ -200,18 +325,10 @@ __global__ __launch_bounds__(kStreamThreads) void mfma_kernel(const TX* __restri
             }
         }
         lds_barrier();                                                   // Y tile written
-        // store the Y tile: flat vector f of the stage is vector f % qy of row f / qy
-        const int64_t n0 = row_begin + int64_t(s) * R;
-        const int nvec = static_cast<int>(min(int64_t(R), row_end - n0)) * args.qy;
-#pragma unroll 2
-        for (int f = t; f < nvec; f += kConsumerThreads) {
-            const int r = f / args.qy;
-            int gy, ly;
-            bool ok;
-            chunk_vector(args.yc, f - r * args.qy, 4, at_eff, dt_eff, &gy, &ly, &ok);
-            if (ok)
-                __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(ys + r * args.yc.lds_row + ly),
-                                            reinterpret_cast<u32x4*>(Y + (n0 + r) * args.n_out + yg0 + gy));
+        if constexpr (NS == 0) {
+            const int64_t n0 = row_begin + int64_t(s) * R;
+            store_tile_rows<4>(args, team, ys, Y + n0 * args.n_out + yg0, static_cast<int>(min(int64_t(R), row_end - n0)),
+                            R);
         }
     }
 }
@@ -221,10 +338,20 @@ __global__ __launch_bounds__(kStreamThreads) void mfma_kernel(const TX* __restri
 
 struct MfmaGeom {
     int tp, r, at, dt, tiles_delta, n_tiles, contiguous, qy, insts, stages;
+    int ns;        // storer waves (0: the compute waves store)
+    int ytile;     // LDS bytes of one Y buffer
     StageMap xmap;
     RowChunk yc;
     size_t lds;
 };
+
+// Workgroups of this kernel that one compute unit holds: its LDS (160 KB)
+// and its wave slots (the kernel without storer waves takes 110-140 VGPRs,
+// 3-4 waves per SIMD; with a storer wave 80-90, 5 per SIMD).
+int mfma_groups_per_cu(size_t lds, int ns) {
+    const size_t waves = ns ? 20 : 12;
+    return static_cast<int>(std::min<size_t>((160 * 1024) / std::max<size_t>(lds, 1), waves / (5 + ns)));
+}
 
 bool supported_bc(int b, int c) {
     return (b == 16 || b == 32 || b == 64 || b == 128) && (c == 16 || c == 32 || c == 64 || c == 128);
@@ -239,14 +366,14 @@ int row_pad(int vec) {
     return pad;
 }
 
-bool geom_for(const Shape& s, int xt, MfmaGeom* g) {
+bool geom_for(const Shape& s, int xt, MfmaGeom* g, int store_waves = KS_STORE_AUTO) {
     if (!supported_bc(s.b, s.c)) return false;
     const int eb = elem_bytes(xt);
     const int vwx = 16 / eb;
     const int b = s.b, c = s.c, d = s.d;
     const int nt = b / 16;
     const int wn = nt < 4 ? nt : 4;
-    g->tp = mfma_tp(b, c);
+    g->tp = mfma_tp(b, c, eb);
     g->r = 16 * (4 / wn);
     const int kStageInsts = mfma_stage_insts(b, c, eb);
     if (kStageInsts > 63) return false;
@@ -259,19 +386,21 @@ bool geom_for(const Shape& s, int xt, MfmaGeom* g) {
     if (d <= g->tp) {
         if ((c * d) % vwx != 0) return false;
         // as many alphas as the pairs allow, while the X stage fits and the
-        // whole workgroup stays within about 80 KB of LDS (two per CU)
+        // whole workgroup stays within about 80 KB of LDS (two per CU), with
+        // two Y buffers (a storer wave) if possible, else with one
         const int blk = c * d / vwx;
-        g->at = 0;
-        for (int at = std::max(1, g->tp / d); at >= 1; --at) {
+        auto fits = [&](int at, int ybufs) {
             const int xv = at * blk;
             const int insts = (g->r * (xv + row_pad(xv)) + 63) / 64;
-            const size_t lds = size_t(3) * insts * 1024 + size_t(g->r) * (size_t(at) * b * d * 4 + 16);
-            if (g->r * (xv + row_pad(xv)) <= kStageInsts * 64 && (lds <= kLdsPerGroup || at == 1)) {
-                g->at = at;
-                break;
-            }
-        }
-        if (g->at == 0) return false;
+            const size_t lds = size_t(3) * insts * 1024 + size_t(ybufs) * g->r * (size_t(at) * b * d * 4 + 16);
+            return g->r * (xv + row_pad(xv)) <= kStageInsts * 64 && lds <= kLdsPerGroup;
+        };
+        const int at_max = std::max(1, g->tp / d);
+        g->at = 0;
+        for (int ybufs = 2; ybufs >= 1 && g->at == 0; --ybufs)
+            for (int at = at_max; at >= 1 && g->at == 0; --at)
+                if (fits(at, ybufs)) g->at = at;
+        if (g->at == 0) g->at = 1;
         g->dt = d;
         g->contiguous = 1;
         xm.blocks = g->at;
@@ -310,14 +439,40 @@ bool geom_for(const Shape& s, int xt, MfmaGeom* g) {
     g->n_tiles = static_cast<int>(nt_all);
     g->qy = g->contiguous ? g->at * b * d / 4 : b * g->dt / 4;
     g->insts = (xm.rows * xm.row_vec + 63) / 64;
-    // ring depth: as many stages as fit next to the Y tile in the
+    if (g->insts > 63) return false;
+    // ring depth: as many stages as fit next to the Y buffers in the
     // per-workgroup LDS budget, 3..8, with the loader's wait count
     // (stages - 2) * insts within vmcnt's range
     const int64_t ytile = int64_t(g->r) * yc.lds_row;
-    g->stages = static_cast<int>(std::max<int64_t>(3, std::min<int64_t>(8, (kLdsPerGroup - ytile) / (g->insts * 1024))));
-    while (g->stages > 3 && (g->stages - 2) * g->insts > 63) --g->stages;
+    auto ring = [&](int64_t ybytes) {
+        int st = static_cast<int>(
+            std::max<int64_t>(3, std::min<int64_t>(8, (kLdsPerGroup - ybytes) / (g->insts * 1024))));
+        while (st > 3 && (st - 2) * g->insts > 63) --st;
+        return st;
+    };
+    const int st0 = ring(ytile), st1 = ring(2 * ytile);
+    const size_t lds0 = size_t(st0) * g->insts * 1024 + size_t(ytile);
+    const size_t lds1 = size_t(st1) * g->insts * 1024 + size_t(2 * ytile);
+    // A storer wave with a second Y buffer lets the stores of one step drain
+    // during the next step's MFMAs; take it unless its LDS or its extra wave
+    // costs a workgroup per compute unit.
+    if (g->qy > 64 * 4 * kStoreQ) return false;   // the compute waves' store team covers a row chunk
+    const bool storer_fits = g->qy <= 64 * kStoreQ && lds1 <= 160 * 1024;
+    if (store_waves == KS_STORE_DEDICATED && !storer_fits) return false;
+    const bool storer = store_waves == KS_STORE_DEDICATED ||
+                        (store_waves == KS_STORE_AUTO && storer_fits &&
+                         mfma_groups_per_cu(lds1, 1) >= mfma_groups_per_cu(lds0, 0));
+    if (storer) {
+        g->ns = 1;
+        g->stages = st1;
+        g->lds = lds1;
+    } else {
+        g->ns = 0;
+        g->stages = st0;
+        g->lds = lds0;
+    }
     if ((g->stages - 2) * g->insts > 63) return false;
-    g->lds = size_t(g->stages) * g->insts * 1024 + size_t(ytile);
+    g->ytile = static_cast<int>(ytile);
     return g->lds <= 160 * 1024;
 }
 
@@ -329,7 +484,7 @@ int64_t rows_per_split(const MfmaGeom& g, int64_t batch, int num_cus, int rows_p
     if (rows_per_block > 0) {
         steps = std::max<int64_t>(1, (rows_per_block + g.r - 1) / g.r);
     } else {
-        const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(4, (160 * 1024) / int64_t(g.lds)));
+        const int64_t per_cu = std::max(1, mfma_groups_per_cu(g.lds, g.ns));
         const int64_t resident = int64_t(std::max(num_cus, 1)) * per_cu;
         const int64_t splits = std::max<int64_t>(1, resident / std::max(g.n_tiles, 1));
         steps = (steps_total + splits - 1) / splits;
@@ -341,7 +496,10 @@ int64_t rows_per_split(const MfmaGeom& g, int64_t batch, int num_cus, int rows_p
 template <typename TX, typename TW, int B, int C>
 ks_status_t launch_bc(const FactorCall& f, const MfmaGeom& g, const MfmaArgs& args, dim3 grid) {
     if constexpr (mfma_stage_insts(B, C, int(sizeof(TX))) <= 63) {
-        return launch_kernel(mfma_kernel<TX, TW, B, C>, grid, dim3(kStreamThreads), g.lds, f.stream,
+        if (g.ns == 1)
+            return launch_kernel(mfma_kernel<TX, TW, B, C, 1>, grid, dim3(kStreamThreads + 64), g.lds, f.stream,
+                                 static_cast<const TX*>(f.X), static_cast<const TW*>(f.W), f.Y, args);
+        return launch_kernel(mfma_kernel<TX, TW, B, C, 0>, grid, dim3(kStreamThreads), g.lds, f.stream,
                              static_cast<const TX*>(f.X), static_cast<const TW*>(f.W), f.Y, args);
     } else {
         return KS_ERR_UNSUPPORTED;
@@ -389,18 +547,18 @@ int mfma_describe(const Shape& s, int xt, int wt, int64_t batch, int num_cus, ch
     const int64_t rps = rows_per_split(g, batch, num_cus, 0);
     return std::snprintf(buf, len,
                          "mfma 16x16x4f32: pairs/tile=%d (alphas=%d deltas=%d %s) rows/stage=%d tiles=%d "
-                         "rows/wg=%lld wgs=%lld stages=%d x %d KB lds=%zu",
+                         "rows/wg=%lld wgs=%lld stages=%d x %d KB storers=%d lds=%zu",
                          g.tp, g.at, g.dt, g.contiguous ? "contiguous" : "segmented", g.r, g.n_tiles,
                          static_cast<long long>(rps),
                          static_cast<long long>(g.n_tiles * ((batch + rps - 1) / std::max<int64_t>(rps, 1))),
-                         g.stages, g.insts, g.lds);
+                         g.stages, g.insts, g.ns, g.lds);
 }
 
 ks_status_t launch_mfma(const FactorCall& f) { return launch_mfma_lds(f); }
 
 ks_status_t launch_mfma_lds(const FactorCall& f) {
     MfmaGeom g;
-    if (!geom_for(f.s, f.xt, &g)) return KS_ERR_UNSUPPORTED;
+    if (!geom_for(f.s, f.xt, &g, f.store_waves)) return KS_ERR_UNSUPPORTED;
     if (!aligned16(f.X) || !aligned16(f.Y)) return KS_ERR_UNSUPPORTED;
     if ((f.s.n_in * elem_bytes(f.xt)) % 16 != 0 || (f.s.n_out * 4) % 16 != 0) return KS_ERR_UNSUPPORTED;
     const int64_t rps = rows_per_split(g, f.batch, f.num_cus, f.rows_per_block);
@@ -422,6 +580,7 @@ ks_status_t launch_mfma_lds(const FactorCall& f) {
     args.qy = g.qy;
     args.insts = g.insts;
     args.stages = g.stages;
+    args.ytile_bytes = g.ytile;
     args.xcd_remap = g.contiguous ? 0 : 1;
     args.xmap = g.xmap;
     args.yc = g.yc;

@@ -26,6 +26,9 @@ DTYPE_F32, DTYPE_BF16, DTYPE_BF16W = 0, 1, 2
 KERNEL_AUTO, KERNEL_GENERIC, KERNEL_VALU, KERNEL_MFMA, KERNEL_MFMA_LDS = 0, 1, 2, 3, 4
 KERNELS = {"auto": KERNEL_AUTO, "generic": KERNEL_GENERIC, "valu": KERNEL_VALU, "mfma": KERNEL_MFMA,
            "mfma_lds": KERNEL_MFMA_LDS}
+# ks_store_waves_t
+STORE_AUTO, STORE_COMPUTE, STORE_DEDICATED = 0, 1, 2
+STORE_WAVES = {"auto": STORE_AUTO, "compute": STORE_COMPUTE, "dedicated": STORE_DEDICATED}
 # chain flags
 CHAIN_AUTO, CHAIN_NO_FUSE = 0, 1
 # ks_status_t
@@ -49,7 +52,7 @@ class ks_pattern_t(ctypes.Structure):
 
 class ks_options_t(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("rows_per_block", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 6)]
+                ("store_waves", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5)]
 
 
 _lib = None
@@ -160,10 +163,11 @@ def ks_matmul(p, W, X, Y, batch: int, dtype: int, stream=None, check: bool = Tru
 
 
 def ks_matmul_ex(p, W, X, Y, batch: int, dtype: int, stream=None, kernel: int = KERNEL_AUTO,
-                 rows_per_block: int = 0, check: bool = True, reserved=None) -> int:
+                 rows_per_block: int = 0, check: bool = True, reserved=None, store_waves=STORE_AUTO) -> int:
     opt = ks_options_t()
     opt.kernel = KERNELS.get(kernel, kernel) if isinstance(kernel, str) else int(kernel)
     opt.rows_per_block = int(rows_per_block)
+    opt.store_waves = STORE_WAVES.get(store_waves, store_waves) if isinstance(store_waves, str) else int(store_waves)
     if reserved is not None:
         for i, v in enumerate(reserved):
             opt.reserved[i] = int(v)

@@ -97,6 +97,9 @@ def test_options():
     assert st((2, 2, 2, 2), kernel=99) == libks.KS_ERR_INVALID
     assert st((2, 2, 2, 2), rows_per_block=-1) == libks.KS_ERR_INVALID
     assert st((2, 2, 2, 2), reserved=[1]) == libks.KS_ERR_INVALID
+    assert st((2, 2, 2, 2), reserved=[0, 0, 0, 0, 1]) == libks.KS_ERR_INVALID
+    assert st((2, 2, 2, 2), store_waves=3) == libks.KS_ERR_INVALID
+    assert st((2, 2, 2, 2), store_waves=-1) == libks.KS_ERR_INVALID
     # a forced family that cannot run the pattern is refused on the host
     assert st((2, 3, 5, 2), kernel="valu") == libks.KS_ERR_UNSUPPORTED
     assert st((2, 3, 5, 2), kernel="mfma") == libks.KS_ERR_UNSUPPORTED

@@ -361,3 +361,36 @@ def test_launch_status_ignores_earlier_unrelated_error():
         torch.cuda.synchronize()
         check_factor(p, X, W, Y.cpu().numpy())
     hip.hipGetLastError()
+
+
+STORE_PATTERNS = [(4, 64, 16, 6), (1, 64, 16, 64), (16, 64, 64, 4), (128, 32, 32, 1), (1, 32, 32, 128),
+                  (32, 128, 128, 1), (3, 32, 16, 5), (5, 128, 16, 2), (2, 16, 64, 2), (1, 128, 32, 4),
+                  (4, 16, 16, 16), (1, 16, 32, 256)]
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("p", STORE_PATTERNS, ids=lambda p: "%d_%d_%d_%d" % p)
+def test_mfma_store_modes(p, bf16):
+    """The MFMA kernel with Y stored by the compute waves and by a dedicated
+    storer wave (double-buffered Y tile): both match the oracle on every
+    output, and agree bit for bit (same MFMA sequence, only the store
+    schedule differs). 48 rows per workgroup give several row steps per
+    workgroup and a ragged last workgroup."""
+    batch = 131
+    X, W = datagen.random_pattern_inputs(p, batch, seed=sum(p) + 17)
+    Xt, Wt = to_dev(X, bf16), to_dev(W, bf16)
+    a, b, c, d = p
+    outs = {}
+    for mode in ("compute", "dedicated"):
+        Y = torch.full((batch, a * b * d), float("nan"), dtype=torch.float32, device=DEV)
+        st = libks.ks_matmul_ex(p, Wt, Xt, Y, batch, libks.dtype_code(Xt.dtype, Wt.dtype), kernel="mfma",
+                                rows_per_block=48, store_waves=mode, check=False)
+        if st == libks.KS_ERR_UNSUPPORTED:
+            continue
+        assert st == libks.KS_OK, libks.ks_status_string(st)
+        torch.cuda.synchronize()
+        outs[mode] = Y.cpu().numpy()
+        check_factor(p, X, W, outs[mode], bf16=bf16)
+    assert outs, "neither store mode ran"
+    if len(outs) == 2:
+        assert np.array_equal(outs["compute"], outs["dedicated"])
