@@ -7,20 +7,26 @@
 // with the b x c block K[alpha][delta]: M = rows, N = b, K = c. With b and c
 // of 16 or more that product fills v_mfma_f32_16x16x4_f32 tiles exactly, so
 // the contraction runs on the matrix cores and the vector ALUs only move
-// data. The op stays bound by HBM traffic for most such shapes (about 6 flop
-// per byte at b = 64, c = 16), so the kernel is built around moving X and Y
-// once, in whole 16-byte vectors, with no permutation pass through global
-// memory (the same page, third sentence: a fused, output-stationary kernel).
+// data. Most such shapes stay bound by HBM traffic (about 6 flop per byte at
+// b = 64, c = 16); b = c = 128 is bound by the fp32 matrix rate. The kernel
+// moves X and Y once, in whole 16-byte vectors, with no permutation pass
+// through global memory (the same page, third sentence: a fused,
+// output-stationary kernel).
 //
-// Workgroup: a tile of (alpha, delta) pairs and a range of rows; one loader
-// wave streams X into a 4-stage LDS ring (ks_stream.h), four consumer waves:
-//  * hold the B operands of their N tiles, for every pair of the tile, in
-//    VGPRs for the whole kernel (waves split the b outputs);
-//  * per stage and pair, read A operands (16 rows x 4 gammas) from LDS,
+// Workgroup: a tile of (alpha, delta) pairs and of BT of the b outputs (all
+// of them unless the block is split), over a range of rows in steps of 16.
+// One loader wave streams X into an LDS ring (ks_stream.h). Four compute
+// waves, WN along the N tiles times WP along the pairs:
+//  * hold the B operands of their N tiles and pairs in VGPRs for the whole
+//    kernel (at most VB registers);
+//  * per step and pair, read A operands (16 rows x 4 gammas) from LDS,
 //    accumulate c/4 MFMAs in fp32 and write the 16 x 16 results into a Y
-//    tile in LDS laid out like the rows of Y;
-//  * after an LDS barrier, store the Y tile with 16-byte vectors that cover
-//    whole segments of Y.
+//    tile in LDS laid out like the rows of Y.
+// The Y tile goes out in 16-byte vectors that cover whole segments of Y,
+// stored either by the compute waves after each step or by a storer wave
+// that drains step s-1 from a second Y buffer while step s computes.
+// Splitting b over several tiles (which read the same X, through the L2)
+// keeps the B operands of several pairs in registers when b and c are large.
 
 #include <algorithm>
 #include <cstdio>
@@ -39,42 +45,44 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kLdsPerGroup = 80 * 1024;   // two workgroups per compute unit
 constexpr int kStoreQ = 4;                // storer: row-chunk vectors per lane
 
-// Rows per stage: 16 per row of waves (the four waves split N first).
-__host__ __device__ constexpr int mfma_rows(int b) { return 16 * (4 / (b / 16 < 4 ? b / 16 : 4)); }
+constexpr int kRows = 16;                 // rows per step: one MFMA M tile
 
-// N tiles (16 outputs each) per wave.
-__host__ __device__ constexpr int mfma_ntw(int b) { return b / 16 < 4 ? 1 : b / 64; }
+// Waves along the N tiles and along the pairs (WN x WP = 4 compute waves),
+// and N tiles per wave, for a tile of bt outputs.
+__host__ __device__ constexpr int mfma_wn(int bt) { return bt / 16 < 4 ? bt / 16 : 4; }
+__host__ __device__ constexpr int mfma_wp(int bt) { return 4 / mfma_wn(bt); }
+__host__ __device__ constexpr int mfma_ntw(int bt) { return bt / 16 / mfma_wn(bt); }
 
-// Pairs per tile, a power of two: the B operands take TP * NTW * c / 4
-// VGPRs, at most 64; an X stage (R rows of TP * c elements of eb bytes)
-// stays within 48 KB; and three X stages plus the fp32 Y tile (R rows of
-// TP * b) stay within 150 KB of LDS.
-__host__ __device__ constexpr int mfma_tp(int b, int c, int eb) {
-    int tp = 256 / (mfma_ntw(b) * c);
-    if (tp < 1) tp = 1;
-    while (tp > 1 && (mfma_rows(b) * tp * c * eb > 48 * 1024 ||
-                      3 * mfma_rows(b) * tp * c * eb + mfma_rows(b) * tp * b * 4 > 150 * 1024))
+// Pairs per tile, WP times a power of two: a wave's B operands take
+// (TP / WP) * NTW * c / 4 VGPRs, at most vb; an X stage (16 rows of TP * c
+// elements of eb bytes) stays within 48 KB; and three X stages plus the fp32
+// Y tile (16 rows of TP * bt) stay within 150 KB of LDS.
+__host__ __device__ constexpr int mfma_tp(int bt, int c, int eb, int vb) {
+    int pw = vb / (mfma_ntw(bt) * (c / 4));
+    if (pw < 1) pw = 1;
+    int tp = pw * mfma_wp(bt);
+    while (tp > mfma_wp(bt) && (kRows * tp * c * eb > 48 * 1024 ||
+                                3 * kRows * tp * c * eb + kRows * tp * bt * 4 > 150 * 1024))
         tp /= 2;
     return tp;
 }
 
-// Tile shape of one (b, c, element size) instantiation.
-template <int B, int C, int EB>
+// Tile shape of one (bt, c, element size, B-operand budget) instantiation.
+template <int BT, int C, int EB, int VB>
 struct MfmaShape {
-    static constexpr int NT = B / 16;                  // 16-wide N tiles
-    static constexpr int WN = NT < 4 ? NT : 4;         // waves along N
-    static constexpr int NTW = NT / WN;                // N tiles per wave
-    static constexpr int WR = 4 / WN;                  // waves along rows
+    static constexpr int WN = mfma_wn(BT);             // waves along N
+    static constexpr int WP = mfma_wp(BT);             // waves along pairs
+    static constexpr int NTW = mfma_ntw(BT);           // N tiles per wave
     static constexpr int KS = C / 4;                   // MFMA K steps
-    static constexpr int R = 16 * WR;                  // rows per stage
-    static constexpr int TP = mfma_tp(B, C, EB);       // pairs per tile
-    static_assert(R == mfma_rows(B) && NTW == mfma_ntw(B), "shape helpers");
+    static constexpr int TP = mfma_tp(BT, C, EB, VB);  // pairs per tile
+    static constexpr int PW = TP / WP;                 // pairs per wave
+    static_assert(PW * WP == TP && PW * NTW * KS <= (VB > NTW * KS ? VB : NTW * KS), "B operand budget");
 };
 
-// Loader instructions (KB) per X stage: R rows of at most TP * c elements,
+// Loader instructions (KB) per X stage: 16 rows of at most TP * c elements,
 // plus one pad vector per row.
-__host__ __device__ constexpr int mfma_stage_insts(int b, int c, int eb) {
-    return (mfma_rows(b) * (mfma_tp(b, c, eb) * c * eb / 16 + 1) + 63) / 64;
+__host__ __device__ constexpr int mfma_stage_insts(int bt, int c, int eb, int vb) {
+    return (kRows * (mfma_tp(bt, c, eb, vb) * c * eb / 16 + 1) + 63) / 64;
 }
 
 struct MfmaArgs {
@@ -89,6 +97,8 @@ struct MfmaArgs {
     int stages;              // LDS ring depth
     int ytile_bytes;         // LDS bytes of one Y tile buffer
     int xcd_remap;           // 1: renumber workgroups so neighbouring tiles share an XCD
+    int bsplit;              // tiles per (alpha, delta) block: b = bsplit * BT
+    int b;                   // outputs per block (the K block stride is b * c)
     StageMap xmap;           // LDS layout of an X stage
     RowChunk yc;             // LDS layout of the Y tile and its global stores
 };
@@ -179,15 +189,15 @@ __device__ __forceinline__ void store_tile_rows(const A& args, const StoreTeam& 
 // barrier. NS > 0: NS storer waves store tile s-1 from one of two Y buffers
 // while the compute waves run the MFMAs of step s into the other, so the
 // stores drain during the contraction instead of after it.
-template <typename TX, typename TW, int B, int C, int NS>
+template <typename TX, typename TW, int BT, int C, int NS, int VB>
 __global__ __launch_bounds__(kStreamThreads + 64 * NS) void mfma_kernel(const TX* __restrict__ X,
                                                                         const TW* __restrict__ K,
                                                                         float* __restrict__ Y, MfmaArgs args) {
     constexpr int EB = int(sizeof(TX));
-    using S = MfmaShape<B, C, EB>;
-    constexpr int TP = S::TP, NTW = S::NTW, WN = S::WN, KS = S::KS, R = S::R;
+    using S = MfmaShape<BT, C, EB, VB>;
+    constexpr int NTW = S::NTW, WN = S::WN, WP = S::WP, PW = S::PW, KS = S::KS, R = kRows;
     constexpr int VWX = 16 / EB;
-    constexpr int kMaxInsts = mfma_stage_insts(B, C, EB);
+    constexpr int kMaxInsts = mfma_stage_insts(BT, C, EB, VB);
     static_assert(kMaxInsts <= 63, "vmcnt is six bits");
     const int kStageBytes = args.insts * 1024;
     const int kStages = args.stages;
@@ -199,8 +209,11 @@ __global__ __launch_bounds__(kStreamThreads + 64 * NS) void mfma_kernel(const TX
     const int blk = args.xcd_remap ? xcd_logical_block(blockIdx.x, gridDim.x) : int(blockIdx.x);
     const int tile = blk % args.n_tiles;
     const int split = blk / args.n_tiles;
-    const int ta = tile / args.tiles_delta;
-    const int td = tile - ta * args.tiles_delta;
+    // tiles that read the same X (the b splits of one block) are neighbours
+    const int tad = tile / args.bsplit;
+    const int beta0 = (tile - tad * args.bsplit) * BT;
+    const int ta = tad / args.tiles_delta;
+    const int td = tad - ta * args.tiles_delta;
     const int alpha0 = ta * args.at;
     const int delta0 = td * args.dt;
     const int d = args.d;
@@ -208,7 +221,7 @@ __global__ __launch_bounds__(kStreamThreads + 64 * NS) void mfma_kernel(const TX
     const int dt_eff = min(args.dt, d - delta0);
     const bool contig = args.contiguous != 0;
     const int64_t xg0 = int64_t(alpha0) * C * d + (contig ? 0 : delta0);
-    const int64_t yg0 = int64_t(alpha0) * B * d + (contig ? 0 : delta0);
+    const int64_t yg0 = (int64_t(alpha0) * args.b + beta0) * d + (contig ? 0 : delta0);
 
     const int64_t row_begin = int64_t(split) * args.rows_per_split;
     if (row_begin >= args.batch) return;
@@ -263,29 +276,30 @@ __global__ __launch_bounds__(kStreamThreads + 64 * NS) void mfma_kernel(const TX
     // ---------------------------------------------------------- consumers
     const int wave = t >> 6;
     const int lane = t & 63;
-    const int wn = wave % WN;
-    const int wr = wave / WN;
+    const int wn = wave % WN;                     // N tiles wn * NTW ..
+    const int wp = wave / WN;                     // pairs wp, wp + WP, ..
 
     const int gsx = contig ? d * EB : xblk_bytes;          // X: gamma stride in LDS
     const int bsy = contig ? d * 4 : args.yc.seg_lds;      // Y: beta stride in LDS
-    int xoff[TP], yoff[TP];
-    bool pv[TP];
-    float breg[TP][NTW][KS];
+    int xoff[PW], yoff[PW];
+    bool pv[PW];
+    float breg[PW][NTW][KS];
 #pragma unroll
-    for (int p = 0; p < TP; ++p) {
+    for (int i = 0; i < PW; ++i) {
+        const int p = wp + WP * i;
         const int al = p / args.dt;
         const int de = p - al * args.dt;
-        pv[p] = p < args.at * args.dt && al < at_eff && de < dt_eff;
-        xoff[p] = contig ? al * xblk_bytes + de * EB : de * EB;
-        yoff[p] = contig ? al * args.yc.lds_slab + de * 4 : de * 4;
-        const TW* kp = K + ((int64_t(alpha0 + al) * d + delta0 + de) * B) * C;
+        pv[i] = p < args.at * args.dt && al < at_eff && de < dt_eff;
+        xoff[i] = contig ? al * xblk_bytes + de * EB : de * EB;
+        yoff[i] = contig ? al * args.yc.lds_slab + de * 4 : de * 4;
+        const TW* kp = K + ((int64_t(alpha0 + al) * d + delta0 + de) * args.b + beta0) * C;
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
             const int beta = (wn * NTW + nt) * 16 + (lane & 15);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int gamma = ks * 4 + (lane >> 4);
-                breg[p][nt][ks] = pv[p] ? to_f32(kp[beta * C + gamma]) : 0.0f;
+                breg[i][nt][ks] = pv[i] ? to_f32(kp[beta * C + gamma]) : 0.0f;
             }
         }
     }
@@ -293,33 +307,33 @@ __global__ __launch_bounds__(kStreamThreads + 64 * NS) void mfma_kernel(const TX
     StoreTeam team;
     if constexpr (NS == 0) make_store_team(args, t, kConsumerThreads, at_eff, dt_eff, &team);
 
-    const int arow = wr * 16 + (lane & 15);       // A operand row of this lane
+    const int arow = lane & 15;                   // A operand row of this lane
     const int akk = lane >> 4;                    // A operand k (gamma within a step)
     for (int s = 0; s < nsteps; ++s) {
         lds_barrier();                                                   // stage s ready
         const unsigned char* xcur = lds + (s % kStages) * kStageBytes;
         unsigned char* const ys = NS > 0 ? ys0 + (s & 1) * args.ytile_bytes : ys0;
 #pragma unroll
-        for (int p = 0; p < TP; ++p) {
-            if (!pv[p]) continue;
+        for (int i = 0; i < PW; ++i) {
+            if (!pv[i]) continue;
             floatx4 acc[NTW];
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) acc[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-            const unsigned char* xa = xcur + arow * xrow_bytes + xoff[p] + akk * gsx;
+            const unsigned char* xa = xcur + arow * xrow_bytes + xoff[i] + akk * gsx;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const float av = to_f32(*reinterpret_cast<const TX*>(xa + ks * 4 * gsx));
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt)
-                    acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, breg[p][nt][ks], acc[nt], 0, 0, 0);
+                    acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, breg[i][nt][ks], acc[nt], 0, 0, 0);
             }
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) {
                 const int beta = (wn * NTW + nt) * 16 + (lane & 15);
-                unsigned char* yb = ys + yoff[p] + beta * bsy;
+                unsigned char* yb = ys + yoff[i] + beta * bsy;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const int row = wr * 16 + 4 * (lane >> 4) + v;
+                    const int row = 4 * (lane >> 4) + v;
                     *reinterpret_cast<float*>(yb + row * args.yc.lds_row) = acc[nt][v];
                 }
             }
@@ -340,22 +354,27 @@ struct MfmaGeom {
     int tp, r, at, dt, tiles_delta, n_tiles, contiguous, qy, insts, stages;
     int ns;        // storer waves (0: the compute waves store)
     int ytile;     // LDS bytes of one Y buffer
+    int vb;        // B-operand VGPR budget of the instantiation (64 or 128)
+    int bsplit;    // tiles per (alpha, delta) block along b
+    int bt;        // outputs per tile (b / bsplit)
     StageMap xmap;
     RowChunk yc;
     size_t lds;
 };
 
 // Workgroups of this kernel that one compute unit holds: its LDS (160 KB)
-// and its wave slots (the kernel without storer waves takes 110-140 VGPRs,
-// 3-4 waves per SIMD; with a storer wave 80-90, 5 per SIMD).
-int mfma_groups_per_cu(size_t lds, int ns) {
-    const size_t waves = ns ? 20 : 12;
+// and its wave slots (with the 64-register B budget the kernel takes
+// 110-140 VGPRs, 3-4 waves per SIMD, or 80-90 with a storer wave, 5 per
+// SIMD; with the 128-register budget 150-190 VGPRs, 2-3 per SIMD).
+int mfma_groups_per_cu(size_t lds, int ns, int vb) {
+    const size_t waves = vb > 64 ? (ns ? 12 : 8) : (ns ? 20 : 12);
     return static_cast<int>(std::min<size_t>((160 * 1024) / std::max<size_t>(lds, 1), waves / (5 + ns)));
 }
 
-bool supported_bc(int b, int c) {
-    return (b == 16 || b == 32 || b == 64 || b == 128) && (c == 16 || c == 32 || c == 64 || c == 128);
-}
+bool pow2_block(int v) { return v == 16 || v == 32 || v == 64 || v == 128; }
+
+// The 128-register B budget is built for tiles whose c is 64 or 128.
+bool vb_built(int bt, int c, int vb) { return vb == 64 || (vb == 128 && bt >= 32 && c >= 64); }
 
 // Smallest pad (in 16-byte vectors) making a row pitch of `vec` vectors an
 // odd multiple of 16 bytes modulo 256, so 16 consecutive rows start in
@@ -366,16 +385,20 @@ int row_pad(int vec) {
     return pad;
 }
 
-bool geom_for(const Shape& s, int xt, MfmaGeom* g, int store_waves = KS_STORE_AUTO) {
-    if (!supported_bc(s.b, s.c)) return false;
+// Geometry of one candidate (B budget vb, b split into bsplit tiles).
+bool geom_for(const Shape& s, int xt, int vb, int bsplit, int store_waves, MfmaGeom* g) {
+    const int b = s.b, c = s.c, d = s.d;
+    if (b % bsplit != 0) return false;
+    const int bt = b / bsplit;
+    if (!pow2_block(bt) || !pow2_block(c) || !vb_built(bt, c, vb)) return false;
     const int eb = elem_bytes(xt);
     const int vwx = 16 / eb;
-    const int b = s.b, c = s.c, d = s.d;
-    const int nt = b / 16;
-    const int wn = nt < 4 ? nt : 4;
-    g->tp = mfma_tp(b, c, eb);
-    g->r = 16 * (4 / wn);
-    const int kStageInsts = mfma_stage_insts(b, c, eb);
+    g->vb = vb;
+    g->bsplit = bsplit;
+    g->bt = bt;
+    g->tp = mfma_tp(bt, c, eb, vb);
+    g->r = kRows;
+    const int kStageInsts = mfma_stage_insts(bt, c, eb, vb);
     if (kStageInsts > 63) return false;
     // the loader addresses a stage with 32-bit byte offsets
     if (int64_t(g->r) * s.n_in * eb >= (int64_t(1) << 31)) return false;
@@ -392,7 +415,7 @@ bool geom_for(const Shape& s, int xt, MfmaGeom* g, int store_waves = KS_STORE_AU
         auto fits = [&](int at, int ybufs) {
             const int xv = at * blk;
             const int insts = (g->r * (xv + row_pad(xv)) + 63) / 64;
-            const size_t lds = size_t(3) * insts * 1024 + size_t(ybufs) * g->r * (size_t(at) * b * d * 4 + 16);
+            const size_t lds = size_t(3) * insts * 1024 + size_t(ybufs) * g->r * (size_t(at) * bt * d * 4 + 16);
             return g->r * (xv + row_pad(xv)) <= kStageInsts * 64 && lds <= kLdsPerGroup;
         };
         const int at_max = std::max(1, g->tp / d);
@@ -408,8 +431,9 @@ bool geom_for(const Shape& s, int xt, MfmaGeom* g, int store_waves = KS_STORE_AU
         xm.gstride = c * d;
         xm.row_vec = g->at * xm.blk_vec;
         yc.contiguous = 1;
-        yc.slab = b * d;
-        yc.lds_slab = b * d * 4;
+        yc.slab = bt * d;
+        yc.slab_global = b * d;
+        yc.lds_slab = bt * d * 4;
         yc.lds_row = g->at * yc.lds_slab + 16;
         yc.nseg = yc.seg_global = yc.seg_lds = yc.seg_cap = 0;
     } else {
@@ -423,21 +447,21 @@ bool geom_for(const Shape& s, int xt, MfmaGeom* g, int store_waves = KS_STORE_AU
         xm.gstride = d;
         xm.row_vec = c * xm.blk_vec;
         yc.contiguous = 0;
-        yc.slab = yc.lds_slab = 0;
-        yc.nseg = b;
+        yc.slab = yc.slab_global = yc.lds_slab = 0;
+        yc.nseg = bt;
         yc.seg_global = d;
         yc.seg_cap = g->tp;
         yc.seg_lds = g->tp * 4;
-        yc.lds_row = b * g->tp * 4 + 16;
+        yc.lds_row = bt * g->tp * 4 + 16;
     }
     xm.row_vec += row_pad(xm.row_vec);
     if (xm.rows * xm.row_vec > kStageInsts * 64) return false;
     const int64_t tiles_alpha = (s.a + g->at - 1) / g->at;
     g->tiles_delta = g->contiguous ? 1 : (d + g->dt - 1) / g->dt;
-    const int64_t nt_all = tiles_alpha * g->tiles_delta;
+    const int64_t nt_all = tiles_alpha * g->tiles_delta * bsplit;
     if (nt_all > (int64_t(1) << 30)) return false;
     g->n_tiles = static_cast<int>(nt_all);
-    g->qy = g->contiguous ? g->at * b * d / 4 : b * g->dt / 4;
+    g->qy = g->contiguous ? g->at * bt * d / 4 : bt * g->dt / 4;
     g->insts = (xm.rows * xm.row_vec + 63) / 64;
     if (g->insts > 63) return false;
     // ring depth: as many stages as fit next to the Y buffers in the
@@ -461,7 +485,7 @@ bool geom_for(const Shape& s, int xt, MfmaGeom* g, int store_waves = KS_STORE_AU
     if (store_waves == KS_STORE_DEDICATED && !storer_fits) return false;
     const bool storer = store_waves == KS_STORE_DEDICATED ||
                         (store_waves == KS_STORE_AUTO && storer_fits &&
-                         mfma_groups_per_cu(lds1, 1) >= mfma_groups_per_cu(lds0, 0));
+                         mfma_groups_per_cu(lds1, 1, vb) >= mfma_groups_per_cu(lds0, 0, vb));
     if (storer) {
         g->ns = 1;
         g->stages = st1;
@@ -476,6 +500,29 @@ bool geom_for(const Shape& s, int xt, MfmaGeom* g, int store_waves = KS_STORE_AU
     return g->lds <= 160 * 1024;
 }
 
+// The planner's tile: the first candidate whose X runs (the contiguous
+// part of a row that one tile reads) are at least 32 bytes, else the first
+// that runs at all. Candidates go from the cheapest (64 B registers per
+// wave, whole blocks) to wider register budgets and split blocks.
+bool choose_geom(const Shape& s, int xt, int store_waves, MfmaGeom* g) {
+    static const int kCand[][2] = {{64, 1}, {128, 1}, {128, 2}, {64, 2}, {128, 4}, {64, 4}};
+    const int eb = elem_bytes(xt);
+    bool found = false;
+    for (const auto& cand : kCand) {
+        MfmaGeom t;
+        if (!geom_for(s, xt, cand[0], cand[1], store_waves, &t)) continue;
+        if (t.contiguous || t.dt * eb >= 32) {
+            *g = t;
+            return true;
+        }
+        if (!found) {
+            *g = t;
+            found = true;
+        }
+    }
+    return found;
+}
+
 // Rows per workgroup: a multiple of the stage rows, so that the grid is about
 // one resident wave of workgroups with equal shares.
 int64_t rows_per_split(const MfmaGeom& g, int64_t batch, int num_cus, int rows_per_block) {
@@ -484,7 +531,7 @@ int64_t rows_per_split(const MfmaGeom& g, int64_t batch, int num_cus, int rows_p
     if (rows_per_block > 0) {
         steps = std::max<int64_t>(1, (rows_per_block + g.r - 1) / g.r);
     } else {
-        const int64_t per_cu = std::max(1, mfma_groups_per_cu(g.lds, g.ns));
+        const int64_t per_cu = std::max(1, mfma_groups_per_cu(g.lds, g.ns, g.vb));
         const int64_t resident = int64_t(std::max(num_cus, 1)) * per_cu;
         const int64_t splits = std::max<int64_t>(1, resident / std::max(g.n_tiles, 1));
         steps = (steps_total + splits - 1) / splits;
@@ -493,33 +540,42 @@ int64_t rows_per_split(const MfmaGeom& g, int64_t batch, int num_cus, int rows_p
     return steps * g.r;
 }
 
-template <typename TX, typename TW, int B, int C>
-ks_status_t launch_bc(const FactorCall& f, const MfmaGeom& g, const MfmaArgs& args, dim3 grid) {
-    if constexpr (mfma_stage_insts(B, C, int(sizeof(TX))) <= 63) {
+template <typename TX, typename TW, int BT, int C, int VB>
+ks_status_t launch_vb(const FactorCall& f, const MfmaGeom& g, const MfmaArgs& args, dim3 grid) {
+    if constexpr (mfma_stage_insts(BT, C, int(sizeof(TX)), VB) <= 63) {
         if (g.ns == 1)
-            return launch_kernel(mfma_kernel<TX, TW, B, C, 1>, grid, dim3(kStreamThreads + 64), g.lds, f.stream,
-                                 static_cast<const TX*>(f.X), static_cast<const TW*>(f.W), f.Y, args);
-        return launch_kernel(mfma_kernel<TX, TW, B, C, 0>, grid, dim3(kStreamThreads), g.lds, f.stream,
+            return launch_kernel(mfma_kernel<TX, TW, BT, C, 1, VB>, grid, dim3(kStreamThreads + 64), g.lds,
+                                 f.stream, static_cast<const TX*>(f.X), static_cast<const TW*>(f.W), f.Y, args);
+        return launch_kernel(mfma_kernel<TX, TW, BT, C, 0, VB>, grid, dim3(kStreamThreads), g.lds, f.stream,
                              static_cast<const TX*>(f.X), static_cast<const TW*>(f.W), f.Y, args);
     } else {
         return KS_ERR_UNSUPPORTED;
     }
 }
 
-template <typename TX, typename TW, int B>
+template <typename TX, typename TW, int BT, int C>
+ks_status_t launch_bc(const FactorCall& f, const MfmaGeom& g, const MfmaArgs& args, dim3 grid) {
+    if (g.vb == 64) return launch_vb<TX, TW, BT, C, 64>(f, g, args, grid);
+    if constexpr (BT >= 32 && C >= 64) {
+        if (g.vb == 128) return launch_vb<TX, TW, BT, C, 128>(f, g, args, grid);
+    }
+    return KS_ERR_UNSUPPORTED;
+}
+
+template <typename TX, typename TW, int BT>
 ks_status_t launch_b(const FactorCall& f, const MfmaGeom& g, const MfmaArgs& args, dim3 grid) {
     switch (f.s.c) {
-        case 16: return launch_bc<TX, TW, B, 16>(f, g, args, grid);
-        case 32: return launch_bc<TX, TW, B, 32>(f, g, args, grid);
-        case 64: return launch_bc<TX, TW, B, 64>(f, g, args, grid);
-        case 128: return launch_bc<TX, TW, B, 128>(f, g, args, grid);
+        case 16: return launch_bc<TX, TW, BT, 16>(f, g, args, grid);
+        case 32: return launch_bc<TX, TW, BT, 32>(f, g, args, grid);
+        case 64: return launch_bc<TX, TW, BT, 64>(f, g, args, grid);
+        case 128: return launch_bc<TX, TW, BT, 128>(f, g, args, grid);
     }
     return KS_ERR_UNSUPPORTED;
 }
 
 template <typename TX, typename TW>
 ks_status_t launch_types(const FactorCall& f, const MfmaGeom& g, const MfmaArgs& args, dim3 grid) {
-    switch (f.s.b) {
+    switch (g.bt) {
         case 16: return launch_b<TX, TW, 16>(f, g, args, grid);
         case 32: return launch_b<TX, TW, 32>(f, g, args, grid);
         case 64: return launch_b<TX, TW, 64>(f, g, args, grid);
@@ -535,7 +591,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool mfma_supports(const Shape& s, int xt, int wt) {
     (void)wt;
     MfmaGeom g;
-    return geom_for(s, xt, &g);
+    return choose_geom(s, xt, KS_STORE_AUTO, &g);
 }
 
 bool mfma_lds_supports(const Shape& s, int xt, int wt) { return mfma_supports(s, xt, wt); }
@@ -543,12 +599,12 @@ bool mfma_lds_supports(const Shape& s, int xt, int wt) { return mfma_supports(s,
 int mfma_describe(const Shape& s, int xt, int wt, int64_t batch, int num_cus, char* buf, size_t len) {
     (void)wt;
     MfmaGeom g;
-    if (!geom_for(s, xt, &g)) return std::snprintf(buf, len, "mfma: unsupported");
+    if (!choose_geom(s, xt, KS_STORE_AUTO, &g)) return std::snprintf(buf, len, "mfma: unsupported");
     const int64_t rps = rows_per_split(g, batch, num_cus, 0);
     return std::snprintf(buf, len,
-                         "mfma 16x16x4f32: pairs/tile=%d (alphas=%d deltas=%d %s) rows/stage=%d tiles=%d "
-                         "rows/wg=%lld wgs=%lld stages=%d x %d KB storers=%d lds=%zu",
-                         g.tp, g.at, g.dt, g.contiguous ? "contiguous" : "segmented", g.r, g.n_tiles,
+                         "mfma 16x16x4f32: pairs/tile=%d (alphas=%d deltas=%d %s) outputs/tile=%d of %d "
+                         "B regs=%d rows/wg=%lld wgs=%lld stages=%d x %d KB storers=%d lds=%zu",
+                         g.tp, g.at, g.dt, g.contiguous ? "contiguous" : "segmented", g.bt, s.b, g.vb,
                          static_cast<long long>(rps),
                          static_cast<long long>(g.n_tiles * ((batch + rps - 1) / std::max<int64_t>(rps, 1))),
                          g.stages, g.insts, g.ns, g.lds);
@@ -558,7 +614,7 @@ ks_status_t launch_mfma(const FactorCall& f) { return launch_mfma_lds(f); }
 
 ks_status_t launch_mfma_lds(const FactorCall& f) {
     MfmaGeom g;
-    if (!geom_for(f.s, f.xt, &g, f.store_waves)) return KS_ERR_UNSUPPORTED;
+    if (!choose_geom(f.s, f.xt, f.store_waves, &g)) return KS_ERR_UNSUPPORTED;
     if (!aligned16(f.X) || !aligned16(f.Y)) return KS_ERR_UNSUPPORTED;
     if ((f.s.n_in * elem_bytes(f.xt)) % 16 != 0 || (f.s.n_out * 4) % 16 != 0) return KS_ERR_UNSUPPORTED;
     const int64_t rps = rows_per_split(g, f.batch, f.num_cus, f.rows_per_block);
@@ -581,7 +637,10 @@ ks_status_t launch_mfma_lds(const FactorCall& f) {
     args.insts = g.insts;
     args.stages = g.stages;
     args.ytile_bytes = g.ytile;
-    args.xcd_remap = g.contiguous ? 0 : 1;
+    // neighbouring tiles share X lines (segmented) or all of X (split b)
+    args.xcd_remap = (g.contiguous && g.bsplit == 1) ? 0 : 1;
+    args.bsplit = g.bsplit;
+    args.b = f.s.b;
     args.xmap = g.xmap;
     args.yc = g.yc;
     const dim3 grid(static_cast<unsigned>(blocks));

@@ -5,7 +5,8 @@
 // [delta0, delta0 + dt) of a KS factor. In a row of X (layout
 // [alpha][gamma][delta]) or Y (layout [alpha][beta][delta]) that part is
 //  * contiguous, when the tile spans every delta (dt == d): at slabs of
-//    w*d elements each (w = c for X, b for Y), one after the other; or
+//    w*d elements each (w = c for X, b or the tile's share of b for Y),
+//    slab_global elements apart; or
 //  * segmented, when at == 1 and dt < d: w segments of dt elements, d apart.
 // In LDS a row is stored slab after slab (contiguous) or segment after
 // segment (segmented), each slab or segment padded as the kernel chooses.
@@ -19,7 +20,8 @@ namespace ks {
 
 struct RowChunk {
     int contiguous;     // 1: slabs of `slab` elements; 0: `nseg` segments
-    int slab;           // contiguous: elements per alpha slab (w*d)
+    int slab;           // contiguous: elements per alpha slab in the tile
+    int slab_global;    // contiguous: global elements between alpha slabs
     int lds_slab;       // contiguous: LDS bytes per slab (16-byte multiple)
     int nseg;           // segmented: segments per row (w)
     int seg_global;     // segmented: global elements between segments (d)
@@ -37,7 +39,7 @@ __device__ __forceinline__ void chunk_vector(const RowChunk& m, int q, int vw, i
         const int per = m.slab / vw;
         const int s = q / per;
         const int e = q - s * per;
-        *gofs = q * vw;
+        *gofs = s * m.slab_global + e * vw;
         *lofs = s * m.lds_slab + e * 16;
         *ok = s < at_eff;
     } else {
