@@ -148,8 +148,11 @@ def test_chain_workspace_sizes():
 
 
 def test_plan_describe():
-    assert libks.ks_plan_describe((1, 16, 16, 4096), 4096, libks.DTYPE_F32).startswith("valu lane")
-    assert libks.ks_plan_describe((4096, 16, 16, 1), 4096, libks.DTYPE_F32).startswith("valu slab")
+    assert libks.ks_plan_describe((1, 16, 16, 4096), 4096, libks.DTYPE_F32).startswith("mfma")
+    assert "segmented" in libks.ks_plan_describe((1, 16, 16, 4096), 4096, libks.DTYPE_F32)
+    assert libks.ks_plan_describe((1, 8, 8, 4096), 4096, libks.DTYPE_F32).startswith("valu lane")
+    assert libks.ks_plan_describe((4096, 8, 8, 1), 4096, libks.DTYPE_F32).startswith("valu slab")
+    assert "outputs/tile=64 of 128" in libks.ks_plan_describe((1, 128, 128, 32), 4096, libks.DTYPE_F32)
     assert libks.ks_plan_describe((2, 3, 5, 7), 10, libks.DTYPE_F32).startswith("generic")
 
 
