@@ -53,6 +53,17 @@ __host__ __device__ constexpr int nb_rule(int b, int c, int dv) {
     return nb;
 }
 
+// Betas per thread for a mapping. In slab mode with d = 4, one thread per
+// alpha (all b betas) stores b strided 16-byte vectors; one beta per thread
+// instead makes consecutive lanes store consecutive vectors (the lanes of
+// one alpha share its X slab, an LDS broadcast). Measured on (256, 4, 4, 4):
+// 3.9 against 2.5 TB/s; for other slab shapes the register rule is as fast
+// or faster.
+__host__ __device__ constexpr int nb_pick(int b, int c, int dv, bool lane) {
+    const int nb = nb_rule(b, c, dv);
+    return (!lane && dv == 4 && nb == b) ? 1 : nb;
+}
+
 struct ValuArgs {
     int a, d;
     int64_t n_in, n_out;
@@ -69,14 +80,14 @@ struct ValuArgs {
     StageMap map;        // LDS layout of one stage
 };
 
-template <typename TX, typename TW, int B, int C, int DV, bool LANE>
+template <typename TX, typename TW, int B, int C, int DV, bool LANE, bool ILV>
 __global__ __launch_bounds__(kStreamThreads) void valu_kernel(const TX* __restrict__ X,
                                                               const TW* __restrict__ K,
                                                               float* __restrict__ Y,
                                                               ValuArgs args) {
     constexpr int EB = int(sizeof(TX));
     constexpr int VW = 16 / EB;                 // elements per 16-byte vector
-    constexpr int NB = nb_rule(B, C, DV);
+    constexpr int NB = ILV ? 1 : nb_pick(B, C, DV, LANE);
     constexpr int G = B / NB;                   // beta groups
     constexpr int P = kConsumerThreads / G;     // delta runs (lane) or alphas (slab) per group
     static_assert(B % NB == 0, "beta groups must divide b");
@@ -130,7 +141,15 @@ __global__ __launch_bounds__(kStreamThreads) void valu_kernel(const TX* __restri
 
     // ---------------------------------------------------------- consumers
     int g, al_l, de_l;   // beta group, alpha within the tile, first delta within the tile
-    if (LANE) {
+    if (LANE && ILV) {
+        // lanes ordered (alpha, beta, delta run): for each beta the lanes of
+        // one alpha store its d outputs next to those of the next beta
+        const int runs = args.dt / DV;              // delta runs per alpha
+        const int run = t % runs;
+        g = (t / runs) % G;
+        al_l = t / (runs * G);
+        de_l = run * DV;
+    } else if (LANE) {
         g = t / P;
         const int p = t - g * P;
         const int runs = args.dt / DV;              // delta runs per alpha
@@ -254,6 +273,7 @@ __global__ __launch_bounds__(kStreamThreads) void valu_kernel(const TX* __restri
 
 struct ValuGeom {
     bool lane;
+    bool ilv;   // lane mode with lanes ordered (alpha, beta, delta run), one beta each
     int dv, nb, g, p, at, dt, tiles_delta, n_tiles, contiguous, vw, insts, stages;
     StageMap map;
 };
@@ -277,7 +297,13 @@ bool geom_for(const Shape& s, int xt, ValuGeom* gm) {
         if (d % vw != 0) return false;
         gm->lane = true;
         gm->dv = (d % 4 == 0) ? 4 : 1;
-        gm->nb = nb_rule(b, c, gm->dv);
+        // d = 8: an alpha's outputs for one beta are only two 16-byte runs,
+        // so with beta-major lanes each store would touch a quarter or less
+        // of its cache lines; one beta per thread with lanes ordered
+        // (alpha, beta, run) stores whole lines (measured 2.8 -> 4.4 TB/s on
+        // (128, 4, 4, 8) and 3.1 -> 3.9 on (64, 8, 8, 8); slower from d = 16)
+        gm->ilv = gm->dv == 4 && d / gm->dv <= 2;
+        gm->nb = gm->ilv ? 1 : nb_rule(b, c, gm->dv);
         gm->g = b / gm->nb;
         gm->p = kConsumerThreads / gm->g;
         const int span = gm->p * gm->dv;            // deltas one group covers
@@ -312,8 +338,9 @@ bool geom_for(const Shape& s, int xt, ValuGeom* gm) {
         if (d != 1 && d != 2 && d != 4) return false;
         if ((c * d) % vw != 0) return false;
         gm->lane = false;
+        gm->ilv = false;
         gm->dv = d;
-        gm->nb = nb_rule(b, c, d);
+        gm->nb = nb_pick(b, c, d, false);
         gm->g = b / gm->nb;
         gm->p = kConsumerThreads / gm->g;
         gm->dt = d;
@@ -376,15 +403,18 @@ ks_status_t launch_bc(const FactorCall& f, const ValuGeom& gm, const ValuArgs& a
     const TW* K = static_cast<const TW*>(f.W);
     const dim3 block(kStreamThreads);
     if (gm.lane && gm.dv == 4) {
-        return launch_kernel(valu_kernel<TX, TW, B, C, 4, true>, grid, block, lds, f.stream, X, K, f.Y, args);
+        if (gm.ilv)
+            return launch_kernel(valu_kernel<TX, TW, B, C, 4, true, true>, grid, block, lds, f.stream, X, K, f.Y,
+                                 args);
+        return launch_kernel(valu_kernel<TX, TW, B, C, 4, true, false>, grid, block, lds, f.stream, X, K, f.Y, args);
     } else if (gm.lane) {
-        return launch_kernel(valu_kernel<TX, TW, B, C, 1, true>, grid, block, lds, f.stream, X, K, f.Y, args);
+        return launch_kernel(valu_kernel<TX, TW, B, C, 1, true, false>, grid, block, lds, f.stream, X, K, f.Y, args);
     } else if (f.s.d == 1) {
-        return launch_kernel(valu_kernel<TX, TW, B, C, 1, false>, grid, block, lds, f.stream, X, K, f.Y, args);
+        return launch_kernel(valu_kernel<TX, TW, B, C, 1, false, false>, grid, block, lds, f.stream, X, K, f.Y, args);
     } else if (f.s.d == 2) {
-        return launch_kernel(valu_kernel<TX, TW, B, C, 2, false>, grid, block, lds, f.stream, X, K, f.Y, args);
+        return launch_kernel(valu_kernel<TX, TW, B, C, 2, false, false>, grid, block, lds, f.stream, X, K, f.Y, args);
     } else {
-        return launch_kernel(valu_kernel<TX, TW, B, C, 4, false>, grid, block, lds, f.stream, X, K, f.Y, args);
+        return launch_kernel(valu_kernel<TX, TW, B, C, 4, false, false>, grid, block, lds, f.stream, X, K, f.Y, args);
     }
 }
 
@@ -426,7 +456,8 @@ int valu_describe(const Shape& s, int xt, int wt, int64_t batch, int num_cus, ch
     return std::snprintf(buf, len,
                          "valu %s dv=%d: nb=%d groups=%d alphas/tile=%d deltas/tile=%d tiles=%d "
                          "rows/stage=%d rows/wg=%lld wgs=%lld stages=%d x %d KB",
-                         gm.lane ? "lane" : "slab", gm.dv, gm.nb, gm.g, gm.at, gm.dt, gm.n_tiles,
+                         gm.lane ? (gm.ilv ? "lane-interleaved" : "lane") : "slab", gm.dv, gm.nb, gm.g, gm.at,
+                         gm.dt, gm.n_tiles,
                          gm.map.rows, static_cast<long long>(rps),
                          static_cast<long long>(gm.n_tiles * ((batch + rps - 1) / std::max<int64_t>(rps, 1))),
                          gm.stages, gm.insts);
