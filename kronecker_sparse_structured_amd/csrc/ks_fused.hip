@@ -18,9 +18,9 @@
 // waves
 //  (A) compute Z[r][beta0][delta0] for their 2 beta0 x 1 delta0 each
 //      (c0 FMAs per value, weights in registers) into LDS,
-//  (B) after an LDS barrier, compute Y[r][alpha1][beta1][delta1] for 2
-//      outputs each (c1 FMAs per value, weights in registers) and store them;
-//      lanes cover consecutive (beta1, delta1), so stores are coalesced.
+//  (B) after an LDS barrier, compute Y[r][alpha1][beta1][delta1] for runs
+//      of 4 delta1 (c1 FMAs per value, weights in registers) and store each
+//      run as one 16-byte vector; a wave's stores cover 1 KB of a row.
 // Z never leaves the chip: the pair moves |X| + |Y| + weights through HBM
 // instead of |X| + 2|Z| + |Y|.
 
@@ -34,6 +34,8 @@
 namespace ks {
 namespace {
 
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
 // Shape family handled: F0 = (1, b0, 16, 64), F1 = (b0, 8, 8, 8), b0 % 8 == 0.
 constexpr int kC0 = 16, kD0 = 64;          // first factor: gamma0, delta0 extents
 constexpr int kB1 = 8, kC1 = 8, kD1 = 8;   // second factor: beta1, gamma1, delta1 extents
@@ -42,6 +44,7 @@ constexpr int kRows = 4;                   // rows per stage
 constexpr int kStages = 4;                 // LDS ring depth
 constexpr int kInsts = kRows * kC0 * kD0 * 4 / 1024;   // loader instructions per fp32 stage
 constexpr int kZPitch = kD0 + 8;           // Z row pitch per beta0 (floats), spreads LDS banks
+static_assert(kRows % 2 == 0 && (kZPitch * 4) % 16 == 0, "phase B takes rows in pairs, Z in 16-byte runs");
 
 struct FusedArgs {
     int b0;                 // beta0 extent (= alpha1 extent)
@@ -111,18 +114,22 @@ __global__ __launch_bounds__(kStreamThreads) void fused_pair_kernel(const TX* __
 #pragma unroll
         for (int g = 0; g < kC0; ++g) k0r[j][g] = to_f32(kp[g]);
     }
-    // (B) thread -> (alpha1, beta1, delta1) and (alpha1, beta1 + 4, delta1)
-    const int e1 = t & (kD1 - 1);
-    const int b1 = (t >> 3) & 3;
-    const int a1 = t >> 5;                                 // 0..7 within the tile
-    float k1r[2][kC1];
+    // (B) thread -> one of two rows, (alpha1, beta1) and a run of 4 delta1:
+    // lanes in (alpha1, beta1, run) order store 16-byte vectors that tile
+    // the row's slab of Y contiguously
+    const int rsub = t >> 7;                               // row within a pair of rows
+    const int run = t & 1;
+    const int b1 = (t >> 1) & (kB1 - 1);
+    const int a1 = (t >> 4) & (kBT - 1);                   // 0..7 within the tile
+    const int e10 = run * 4;                               // first delta1 of the run
+    float k1r[4][kC1];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const TW* kp = K1 + ((int64_t(beta0 + a1) * kD1 + e1) * kB1 + b1 + 4 * j) * kC1;   // K1[a][e][b][:]
+    for (int k = 0; k < 4; ++k) {
+        const TW* kp = K1 + ((int64_t(beta0 + a1) * kD1 + e10 + k) * kB1 + b1) * kC1;   // K1[a][e][b][:]
 #pragma unroll
-        for (int g = 0; g < kC1; ++g) k1r[j][g] = to_f32(kp[g]);
+        for (int g = 0; g < kC1; ++g) k1r[k][g] = to_f32(kp[g]);
     }
-    const int64_t yoff = int64_t(beta0 + a1) * (kB1 * kD1) + b1 * kD1 + e1;
+    const int64_t yoff = int64_t(beta0 + a1) * (kB1 * kD1) + b1 * kD1 + e10;
 
     for (int s = 0; s < nsteps; ++s) {
         lds_barrier();                                                   // stage s ready
@@ -146,19 +153,19 @@ __global__ __launch_bounds__(kStreamThreads) void fused_pair_kernel(const TX* __
         }
         lds_barrier();                                                   // Z written
         // (B) Y[r][a1][b1][e1] = sum_g K1[a1][e1][b1][g] * Z[r][a1][g * 8 + e1]
-#pragma unroll 1
-        for (int r = 0; r < rows; ++r) {
-            const float* zr = zs + (r * kBT + a1) * kZPitch + e1;
-            float y0 = 0.0f, y1 = 0.0f;
+#pragma unroll
+        for (int r0 = 0; r0 < kRows; r0 += 2) {
+            const int r = r0 + rsub;
+            const float* zr = zs + (r * kBT + a1) * kZPitch + e10;
+            floatx4 y = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int g = 0; g < kC1; ++g) {
-                const float z = zr[g * kD1];
-                y0 = fmaf(k1r[0][g], z, y0);
-                y1 = fmaf(k1r[1][g], z, y1);
+                const floatx4 z = *reinterpret_cast<const floatx4*>(zr + g * kD1);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) y[k] = fmaf(k1r[k][g], z[k], y[k]);
             }
-            float* yr = Y + (n0 + r) * args.n_out + yoff;
-            __builtin_nontemporal_store(y0, yr);
-            __builtin_nontemporal_store(y1, yr + 4 * kD1);
+            if (r < rows)
+                __builtin_nontemporal_store(y, reinterpret_cast<floatx4*>(Y + (n0 + r) * args.n_out + yoff));
         }
     }
 }
