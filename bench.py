@@ -75,12 +75,23 @@ CALIB_BYTES = 256 * 2 ** 20      # the --calib-copy device copy reads and writes
 
 
 def ingest_counters(args) -> int:
-    """Per-launch HBM bytes of the workload's KS kernel(s) from two counter
+    """HBM bytes per step of the workload's KS kernel(s) from two counter
     runs of the same command. FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
     are each scaled by what the same counter reads for the calibration copy
-    (CALIB_BYTES read and written), then averaged over the KS dispatches."""
+    (CALIB_BYTES read and written) and summed over the KS dispatches, then
+    divided by the number of steps (one dispatch per step for a single
+    factor, one per launch group for a chain)."""
     import csv
     from collections import defaultdict
+    from kronecker_sparse_structured_amd import datagen, libks
+
+    wl = datagen.get(args.workload)
+    if len(wl.patterns) > 1:
+        dt = libks.DTYPE_BF16 if args.dtype == "bf16" else libks.DTYPE_F32
+        flags = libks.CHAIN_NO_FUSE if args.no_fuse else libks.CHAIN_AUTO
+        per_step = len(libks.ks_chain_groups(wl.patterns, wl.batch, dt, flags))
+    else:
+        per_step = 1
 
     def per_dispatch(path, counter):
         vals = defaultdict(float)
@@ -98,21 +109,32 @@ def ingest_counters(args) -> int:
     scaled = {}
     for path, counter in ((args.ingest_counters[0], "FETCH_SIZE"), (args.ingest_counters[1], "WRITE_SIZE")):
         vals, names = per_dispatch(path, counter)
-        calib = [vals[k] for k, n in names.items() if "copyBuffer" in n or "copy_kernel" in n]
-        ks = [vals[k] for k, n in names.items() if "ks::" in n]
+        ks_ids = [k for k, n in names.items() if "ks::" in n]
+        last_ks = max((int(k) for k in ks_ids), default=-1)
+        # the calibration copies run after the timed KS launches (earlier
+        # copies are the bench's input replication, of other sizes)
+        calib = [vals[k] for k, n in names.items()
+                 if ("copyBuffer" in n or "copy_kernel" in n) and int(k) > last_ks]
+        ks = [vals[k] for k in ks_ids]
         if not calib or not ks:
             print("no calibration copy or no KS dispatch in %s" % path, file=sys.stderr)
             return 1
+        if len(ks) % per_step != 0:
+            print("%d KS dispatches is not a whole number of %d-launch steps" % (len(ks), per_step),
+                  file=sys.stderr)
+            return 1
+        steps = len(ks) // per_step
         factor = CALIB_BYTES / (max(calib) * 1024.0)
-        scaled[counter] = (sum(ks) / len(ks)) * 1024.0 * factor
+        scaled[counter] = (sum(ks) / steps) * 1024.0 * factor
         out[counter.lower() + "_factor"] = round(factor, 4)
-        out[counter.lower() + "_kib_per_launch"] = round(sum(ks) / len(ks), 1)
+        out[counter.lower() + "_kib_per_step"] = round(sum(ks) / steps, 1)
         out[counter.lower() + "_launches"] = len(ks)
-    key = args.workload + ":" + args.dtype
+    key = args.workload + ":" + args.dtype + (":nofuse" if args.no_fuse else "")
     db = {}
     if os.path.exists(TRAFFIC_FILE):
         db = json.load(open(TRAFFIC_FILE))
-    out["bytes_per_launch"] = int(scaled["FETCH_SIZE"] + scaled["WRITE_SIZE"])
+    out["bytes_per_step"] = int(scaled["FETCH_SIZE"] + scaled["WRITE_SIZE"])
+    out["launches_per_step"] = per_step
     out["source_hash"] = kernel_source_hash()
     db[key] = out
     with open(TRAFFIC_FILE, "w") as f:
@@ -249,9 +271,10 @@ def main():
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         try:
-            rec = json.load(open(TRAFFIC_FILE)).get(args.workload + ":" + args.dtype)
+            rec = json.load(open(TRAFFIC_FILE)).get(args.workload + ":" + args.dtype +
+                                                     (":nofuse" if args.no_fuse else ""))
             if rec and rec.get("source_hash") == kernel_source_hash():
-                traffic = rec.get("bytes_per_launch")
+                traffic = rec.get("bytes_per_step")
         except (ValueError, OSError):
             traffic = None
 
