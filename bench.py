@@ -23,6 +23,7 @@ this host's cores on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -219,7 +220,6 @@ def main():
     # The timed loop calls the C entry points with arguments marshalled
     # beforehand, so that the host enqueues launches faster than the GPU
     # runs them and the stream never idles between steps.
-    import ctypes
     lib = libks.load()
     sp = ctypes.c_void_p(int(stream.cuda_stream))
     if chain:
@@ -295,6 +295,45 @@ def main():
         "roofline_time_frac": round(t_roof / (mean_ms * 1e-3), 4),
     }
 
+    # chains: each factor timed on its own (back-to-back launches of its
+    # kernel on inputs of its shape), and the chain's fraction also against
+    # the fully fused minimum |X| + |Y| + weights
+    per_factor = None
+    if chain:
+        per_factor = []
+        for k, p in enumerate(wl.patterns):
+            dtk = dt if k == 0 else (libks.DTYPE_BF16W if bf16 else libks.DTYPE_F32)
+            xbk = xb if k == 0 else 4
+            fbytes = factor_bytes(p, xbk, wbytes, batch)
+            ksets = max(1, int(np.ceil(CACHE_BYTES / fbytes)) + 1)
+            xs = [Xt[0] if k == 0 else torch.randn((batch, datagen.n_in(p)), device=dev)]
+            for _ in range(ksets - 1):
+                xs.append(xs[0].clone())
+            ys = [torch.empty((batch, datagen.n_out(p)), dtype=torch.float32, device=dev) for _ in range(ksets)]
+            opt = libks.ks_options_t()
+            pat = libks.ks_pattern_t(*p)
+            fcalls = [(pat, ctypes.c_void_p(Wt[k].data_ptr()), ctypes.c_void_p(xs[j].data_ptr()),
+                       ctypes.c_void_p(ys[j].data_ptr()), batch, dtk, sp, ctypes.byref(opt)) for j in range(ksets)]
+            reps = 20
+            for j in range(3):
+                lib.ks_matmul_ex(*fcalls[j % ksets])
+            f0 = torch.cuda.Event(enable_timing=True)
+            f1 = torch.cuda.Event(enable_timing=True)
+            f0.record(stream)
+            for j in range(reps):
+                st = lib.ks_matmul_ex(*fcalls[j % ksets])
+                if st != 0:
+                    raise libks.KSError(st, "bench factor")
+            f1.record(stream)
+            torch.cuda.synchronize()
+            fms = f0.elapsed_time(f1) / reps
+            per_factor.append({"pattern": list(p), "ms": round(fms, 5),
+                               "GB/s": round(fbytes / (fms * 1e-3) / 1e9, 1),
+                               "frac": round(fbytes / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                               "plan": libks.ks_plan_describe(p, batch, dtk)})
+            del xs, ys
+        roofline["frac_vs_fused_minimum"] = round(bytes_min / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(wl, bf16, args.cpu_seconds)
@@ -334,6 +373,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if per_factor is not None:
+        out["per_factor"] = per_factor
     print(json.dumps(out), flush=True)
     return 0
 
@@ -377,13 +418,37 @@ def cpu_baseline(wl, bf16, target_s):
     xb = 2 if bf16 else 4
     row_bytes = xb * wl.n_in + 4 * wl.n_out
     gbs = row_bytes * rows_done / total_t / 1e9
+    cores = oracle.num_threads(lib)
+
+    # the same oracle on one thread (OpenMP's runtime setter), fewer rows
+    one = None
+    try:
+        import ctypes
+        gomp = ctypes.CDLL("libgomp.so.1")
+        gomp.omp_set_num_threads(1)
+        rows1 = max(1, min(small.batch, int(target_s / 8 / (per_row * cores))))
+        t1 = run(rows1)
+        gomp.omp_set_num_threads(cores)
+        one = round(row_bytes * rows1 / t1 / 1e9, 4)
+    except OSError:
+        rows1 = 0
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": round(gbs, 4),
         "unit": "GB/s",
-        "cores": oracle.num_threads(lib),
+        "cores": cores,
         "kind": "oracle",
-        "sample": "%d rows of %s (%d of %d rows, %d repeat(s)), %.1f s" % (
-            rows_done, wl.name, want, wl.batch, reps, total_t),
+        "sample": "%d rows of %s (%d of %d rows, %d repeat(s)), %.1f s on %d threads; %s" % (
+            rows_done, wl.name, want, wl.batch, reps, total_t, cores, model or "cpu model unknown"),
+        "value_one_thread": one,
     }
 
 
