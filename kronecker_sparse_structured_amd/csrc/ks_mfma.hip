@@ -42,7 +42,7 @@ namespace {
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kLdsPerGroup = 80 * 1024;   // two workgroups per compute unit
+constexpr int kLdsPerGroupDefault = 80 * 1024;   // two workgroups per compute unit
 constexpr int kStoreQ = 4;                // storer: row-chunk vectors per lane
 
 constexpr int kRows = 16;                 // rows per step: one MFMA M tile
@@ -397,6 +397,12 @@ bool geom_for(const Shape& s, int xt, int vb, int bsplit, int store_waves, MfmaG
     if (!pow2_block(bt) || !pow2_block(c) || !vb_built(bt, c, vb)) return false;
     const int eb = elem_bytes(xt);
     const int vwx = 16 / eb;
+    // LDS budget per workgroup. 80 KB keeps two workgroups on a compute
+    // unit. Tiles of 16 or 32 outputs with d < 16 ran faster as one
+    // workgroup per unit with 86 KB (two X alpha slabs per stage and a
+    // storer wave: 5.3-5.9 against 4.3-5.4 TB/s on the b = c = 16, 32 square
+    // patterns and the last butterfly factor); with d >= 16 they did not.
+    const int kLdsPerGroup = (bt <= 32 && d < 16) ? 86 * 1024 : kLdsPerGroupDefault;
     g->vb = vb;
     g->bsplit = bsplit;
     g->bt = bt;
