@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain device copy of known size (for counter calibration)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every pattern of the square sweep (n = 4096, 16,384 rows) and print "
+                         "one line per pattern plus a JSON summary; not the single-line contract run")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of a "
                          "`--calib-copy` run into profiles/traffic_counters.json and exit")
@@ -144,6 +147,23 @@ def ingest_counters(args) -> int:
     return 0
 
 
+WARM_SECONDS = 0.2
+
+
+def warm_up(step, min_steps, torch) -> int:
+    """Run step(i) at least min_steps times and until about WARM_SECONDS of
+    GPU work have passed; returns the number of steps run."""
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(max(min_steps, 1)):
+            step(n)
+            n += 1
+        torch.cuda.synchronize()
+        if n >= min_steps and time.perf_counter() - t0 >= WARM_SECONDS:
+            return n
+
+
 def factor_bytes(p, x_bytes, w_bytes, batch):
     a, b, c, d = p
     return x_bytes * batch * a * c * d + 4 * batch * a * b * d + w_bytes * a * b * c * d
@@ -158,6 +178,8 @@ def main():
               "(rows would shard across GPUs with no exchange); run with --gpus 1.",
               file=sys.stderr)
         return 2
+    if args.sweep:
+        return sweep(args)
 
     import numpy as np
     import torch
@@ -245,9 +267,9 @@ def main():
         if st != 0:
             raise libks.KSError(st, "bench step")
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    # W warm-up steps, and more until the GPU has been busy for about
+    # WARM_SECONDS: clocks ramp up over milliseconds after an idle spell
+    warm_steps = warm_up(step, args.warmup, torch)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -315,8 +337,7 @@ def main():
             fcalls = [(pat, ctypes.c_void_p(Wt[k].data_ptr()), ctypes.c_void_p(xs[j].data_ptr()),
                        ctypes.c_void_p(ys[j].data_ptr()), batch, dtk, sp, ctypes.byref(opt)) for j in range(ksets)]
             reps = 20
-            for j in range(3):
-                lib.ks_matmul_ex(*fcalls[j % ksets])
+            warm_up(lambda j: lib.ks_matmul_ex(*fcalls[j % ksets]), 3, torch)
             f0 = torch.cuda.Event(enable_timing=True)
             f1 = torch.cuda.Event(enable_timing=True)
             f0.record(stream)
@@ -344,7 +365,7 @@ def main():
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warm_steps,
         "ms_per_step": round(wall * 1e3 / args.steps, 5),
         "kernel_ms_mean": round(mean_ms, 5),
         "tflops": round(tflops, 3),
@@ -376,6 +397,78 @@ def main():
     if per_factor is not None:
         out["per_factor"] = per_factor
     print(json.dumps(out), flush=True)
+    return 0
+
+
+def sweep(args) -> int:
+    """The square sweep: every (a, b, b, d) with b in {4 .. 128} and
+    a * b * d = 4096 on 16,384 rows, fp32 (or bf16), each on its own seeded
+    inputs, timed like the contract run (rotated input sets, back-to-back
+    launches, HIP events around the timed launches on the launch stream)."""
+    import numpy as np
+    import torch
+    from kronecker_sparse_structured_amd import datagen, libks
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bf16 = args.dtype == "bf16"
+    dt = libks.DTYPE_BF16 if bf16 else libks.DTYPE_F32
+    xb = 2 if bf16 else 4
+    lib = libks.load()
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(int(stream.cuda_stream))
+    peak_flops = BF16_PEAK_TFLOPS if bf16 else FP32_PEAK_TFLOPS
+    rows = []
+    for p in datagen.square_sweep_patterns():
+        wl = datagen.get("square_%d_%d_%d_%d" % p)
+        X, Ws = datagen.draw(wl)
+        put = ((lambda a: torch.from_numpy(datagen.bf16_bits(a).view(np.int16)).to(dev).view(torch.bfloat16))
+               if bf16 else (lambda a: torch.from_numpy(a).to(dev)))
+        batch = wl.batch
+        nbytes = factor_bytes(p, xb, xb, batch)
+        flops = 2 * batch * datagen.nnz(p)
+        nset = max(2, int(np.ceil(CACHE_BYTES / nbytes)) + 1)
+        Xt = [put(X)]
+        for _ in range(nset - 1):
+            Xt.append(Xt[0].clone())
+        Wt = put(Ws[0])
+        Yt = [torch.empty((batch, datagen.n_out(p)), dtype=torch.float32, device=dev) for _ in range(nset)]
+        opt = libks.ks_options_t()
+        pat = libks.ks_pattern_t(*p)
+        calls = [(pat, ctypes.c_void_p(Wt.data_ptr()), ctypes.c_void_p(Xt[k].data_ptr()),
+                  ctypes.c_void_p(Yt[k].data_ptr()), batch, dt, sp, ctypes.byref(opt)) for k in range(nset)]
+        warm_up(lambda i: lib.ks_matmul_ex(*calls[i % nset]), 5, torch)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        steps = 30
+        e0.record(stream)
+        for i in range(steps):
+            st = lib.ks_matmul_ex(*calls[i % nset])
+            if st != 0:
+                raise libks.KSError(st, "sweep %s" % (p,))
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        t_roof = max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (peak_flops * 1e12))
+        bound = "hbm" if nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (peak_flops * 1e12) else "mfma"
+        row = {"pattern": list(p), "ms": round(ms, 5),
+               "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+               "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
+               "bound": bound,
+               "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+               "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / peak_flops, 4),
+               "roofline_frac": round(t_roof / (ms * 1e-3), 4),
+               "plan": libks.ks_plan_describe(p, batch, dt)}
+        rows.append(row)
+        print("%-18s %9.1f us %8.1f GB/s %7.2f TFLOP/s  %s  roofline %.3f   %s" % (
+            str(tuple(p)), ms * 1e3, row["GB/s"], row["TFLOP/s"], bound, row["roofline_frac"], row["plan"][:60]),
+            flush=True)
+        del Xt, Yt, Wt, X, Ws
+    fr = [r["roofline_frac"] for r in rows]
+    print(json.dumps({"sweep": "square n=4096, 16384 rows", "dtype": args.dtype, "patterns": len(rows),
+                      "roofline_frac_median": round(float(np.median(fr)), 4),
+                      "roofline_frac_min": round(float(np.min(fr)), 4),
+                      "roofline_frac_max": round(float(np.max(fr)), 4), "rows": rows}), flush=True)
     return 0
 
 
