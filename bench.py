@@ -64,6 +64,8 @@ def parse():
     ap.add_argument("--no-rotate", action="store_true", help="reuse one input/output set (warm caches)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle leg")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg")
+    ap.add_argument("--no-factors", action="store_true",
+                    help="chains: skip timing each factor on its own (profiler runs)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain device copy of known size (for counter calibration)")
     ap.add_argument("--sweep", action="store_true",
@@ -321,7 +323,7 @@ def main():
     # kernel on inputs of its shape), and the chain's fraction also against
     # the fully fused minimum |X| + |Y| + weights
     per_factor = None
-    if chain:
+    if chain and not args.no_factors and not args.calib_copy:
         per_factor = []
         for k, p in enumerate(wl.patterns):
             dtk = dt if k == 0 else (libks.DTYPE_BF16W if bf16 else libks.DTYPE_F32)
