@@ -377,8 +377,11 @@ int mfma_groups_per_cu(size_t lds, int ns, int vb) {
 
 bool pow2_block(int v) { return v == 16 || v == 32 || v == 64 || v == 128; }
 
-// The 128-register B budget is built for tiles whose c is 64 or 128.
-bool vb_built(int bt, int c, int vb) { return vb == 64 || (vb == 128 && bt >= 32 && c >= 64); }
+// The 128-register B budget is built for tiles whose c is 64 or 128, the
+// 32-register one for tiles of 16 or 32 outputs.
+bool vb_built(int bt, int c, int vb) {
+    return vb == 64 || (vb == 128 && bt >= 32 && c >= 64) || (vb == 32 && bt <= 32);
+}
 
 // Smallest pad (in 16-byte vectors) making a row pitch of `vec` vectors an
 // odd multiple of 16 bytes modulo 256, so 16 consecutive rows start in
@@ -516,15 +519,20 @@ bool geom_for(const Shape& s, int xt, int vb, int bsplit, int store_waves, MfmaG
 
 // The planner's tile: the first candidate whose X runs (the contiguous
 // part of a row that one tile reads) are at least 32 bytes, else the first
-// that runs at all. Candidates go from the cheapest (64 B registers per
-// wave, whole blocks) to wider register budgets and split blocks.
+// that runs at all. Candidates go from the cheapest (32 or 64 B registers
+// per wave, whole blocks) to wider register budgets and split blocks.
 bool choose_geom(const Shape& s, int xt, int store_waves, MfmaGeom* g) {
-    static const int kCand[][2] = {{64, 1}, {128, 1}, {128, 2}, {64, 2}, {128, 4}, {64, 4}};
+    static const int kCand[][2] = {{32, 1}, {64, 1}, {128, 1}, {128, 2}, {64, 2}, {128, 4}, {64, 4}};
     const int eb = elem_bytes(xt);
     bool found = false;
     for (const auto& cand : kCand) {
         MfmaGeom t;
         if (!geom_for(s, xt, cand[0], cand[1], store_waves, &t)) continue;
+        // The 32-register budget halves the pairs per tile: only for
+        // contiguous tiles (segmented ones would read half-length runs).
+        // There it measured 5.6-5.9 against 5.1-5.4 TB/s on the b = c = 32
+        // square patterns with d <= 8.
+        if (cand[0] == 32 && !t.contiguous) continue;
         if (t.contiguous || t.dt * eb >= 32) {
             *g = t;
             return true;
@@ -570,6 +578,9 @@ ks_status_t launch_vb(const FactorCall& f, const MfmaGeom& g, const MfmaArgs& ar
 template <typename TX, typename TW, int BT, int C>
 ks_status_t launch_bc(const FactorCall& f, const MfmaGeom& g, const MfmaArgs& args, dim3 grid) {
     if (g.vb == 64) return launch_vb<TX, TW, BT, C, 64>(f, g, args, grid);
+    if constexpr (BT <= 32) {
+        if (g.vb == 32) return launch_vb<TX, TW, BT, C, 32>(f, g, args, grid);
+    }
     if constexpr (BT >= 32 && C >= 64) {
         if (g.vb == 128) return launch_vb<TX, TW, BT, C, 128>(f, g, args, grid);
     }
