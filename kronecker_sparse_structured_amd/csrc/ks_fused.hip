@@ -12,15 +12,20 @@
 // this kind.
 //
 // Workgroup: 8 consecutive beta0 (= alpha1) values and a range of rows; one
-// loader wave streams whole rows of X into an LDS ring (ks_stream.h); the 8
-// workgroups that share rows run on the same XCD, so X is fetched from HBM
-// once and served to the others from L2. Per stage of R rows, four consumer
-// waves
-//  (A) compute Z[r][beta0][delta0] for their 2 beta0 x 1 delta0 each
-//      (c0 FMAs per value, weights in registers) into LDS,
-//  (B) after an LDS barrier, compute Y[r][alpha1][beta1][delta1] for runs
-//      of 4 delta1 (c1 FMAs per value, weights in registers) and store each
-//      run as one 16-byte vector; a wave's stores cover 1 KB of a row.
+// loader wave streams whole rows of X into an LDS ring (ks_stream.h), each
+// row followed by 32 bytes of padding so that the four rows a matrix-core
+// instruction reads start in different banks; the 8 workgroups that share
+// rows run on the same XCD, so X is fetched from HBM once and served to the
+// others from L2. Per stage of 4 rows, four consumer waves
+//  (A) compute Z[r][beta0][delta0] into LDS on the matrix cores: for a fixed
+//      delta0 it is a (rows x c0) by (c0 x beta0) product, and the 16-block
+//      4x4x1 fp32 MFMA does 16 such delta0 at once (weights in registers),
+//  (B) compute Y[r][alpha1][beta1][delta1] of the previous stage from the
+//      other Z buffer: for fp32 rows on the VALU, runs of 4 delta1 per
+//      thread (c1 FMAs per value, weights in registers) stored as 16-byte
+//      vectors; for bf16 rows on the matrix cores again, block = (alpha1,
+//      delta1), a (rows x c1) by (c1 x beta1) product per block.
+// One LDS barrier per stage separates the two.
 // Z never leaves the chip: the pair moves |X| + |Y| + weights through HBM
 // instead of |X| + 2|Z| + |Y|.
 
@@ -41,10 +46,36 @@ constexpr int kC0 = 16, kD0 = 64;          // first factor: gamma0, delta0 exten
 constexpr int kB1 = 8, kC1 = 8, kD1 = 8;   // second factor: beta1, gamma1, delta1 extents
 constexpr int kBT = 8;                     // beta0 (= alpha1) values per workgroup
 constexpr int kRows = 4;                   // rows per stage
-constexpr int kStages = 4;                 // LDS ring depth
-constexpr int kInsts = kRows * kC0 * kD0 * 4 / 1024;   // loader instructions per fp32 stage
-constexpr int kZPitch = kD0 + 8;           // Z row pitch per beta0 (floats), spreads LDS banks
-static_assert(kRows % 2 == 0 && (kZPitch * 4) % 16 == 0, "phase B takes rows in pairs, Z in 16-byte runs");
+constexpr int kXPadBytes = 32;             // LDS pad after each row of X: rows start 8 banks apart
+constexpr int kZPitch = kD0 + 8;           // Z pitch per beta0 (floats): beta0 neighbours 8 banks apart
+constexpr int kZRow = kBT * kZPitch + 8;   // Z pitch per row (floats): rows 8 banks apart
+constexpr int kZFloats = kRows * kZRow;    // one Z buffer
+constexpr int kZBufs = 2;                  // Z double buffer: phase B of stage s - 1 runs beside phase A of stage s
+constexpr int kFusedConsumers = 4;         // consumer waves per workgroup
+constexpr int kFusedThreads = kFusedConsumers * 64 + 64;   // + one loader wave
+constexpr int kSetsPerWave = kBT / kFusedConsumers;        // phase A: groups of 4 beta0 per wave
+// Phase B runs on the VALU (16-byte stores) for fp32 rows and on the matrix
+// cores (4-byte stores) for bf16 rows: the faster of the two for each, by
+// measurement on the GPT-2-medium shape.
+constexpr bool phase_b_mfma(int eb) { return eb == 2; }
+constexpr int kRowsPerPass = kFusedConsumers * 64 / (kBT * kB1 * 2);   // VALU phase B: rows per pass
+static_assert(kRowsPerPass >= 1 && kRows % kRowsPerPass == 0 && (kZPitch * 4) % 16 == 0 && (kZRow * 4) % 16 == 0,
+              "phase B covers whole rows per pass, Z in 16-byte runs");
+static_assert(kRows % 4 == 0 && kBT % kFusedConsumers == 0 && kFusedConsumers % 4 == 0 && kD0 == 64,
+              "phase A: 4x4 MFMA blocks of rows x beta0, 16 delta0 per block group");
+static_assert(kRows == 4 && kBT * kD1 == 16 * kFusedConsumers && kB1 == 8,
+              "MFMA phase B: 4x4 blocks of rows x beta1, 16 (alpha1, delta1) blocks per wave");
+
+// Loader instructions (1 KB each) for one stage of rows of elem_bytes-wide
+// elements with kXPadBytes after each row.
+constexpr int stage_insts(int eb) { return (kRows * (kC0 * kD0 * eb + kXPadBytes) + 1023) / 1024; }
+constexpr int stage_bytes(int eb) { return stage_insts(eb) * 1024; }
+constexpr int kStagesF32 = 3;              // LDS ring depth for fp32 rows
+constexpr int kStagesBF16 = 4;             // ... and for bf16 rows (half the bytes)
+constexpr int stages_for(int eb) { return eb == 4 ? kStagesF32 : kStagesBF16; }
+constexpr size_t fused_lds_bytes(int eb) {
+    return size_t(stages_for(eb)) * stage_bytes(eb) + size_t(kZBufs) * kZFloats * sizeof(float);
+}
 
 struct FusedArgs {
     int b0;                 // beta0 extent (= alpha1 extent)
@@ -55,16 +86,18 @@ struct FusedArgs {
 };
 
 template <typename TX, typename TW>
-__global__ __launch_bounds__(kStreamThreads) void fused_pair_kernel(const TX* __restrict__ X,
-                                                                    const TW* __restrict__ K0,
-                                                                    const TW* __restrict__ K1,
-                                                                    float* __restrict__ Y, FusedArgs args) {
+__global__ __launch_bounds__(kFusedThreads) void fused_pair_kernel(const TX* __restrict__ X,
+                                                                   const TW* __restrict__ K0,
+                                                                   const TW* __restrict__ K1,
+                                                                   float* __restrict__ Y, FusedArgs args) {
     constexpr int EB = int(sizeof(TX));
     constexpr int VW = 16 / EB;
-    constexpr int INSTS = kInsts * EB / 4;                 // a stage holds kRows whole rows of X
-    constexpr int kStageBytes = INSTS * 1024;
+    constexpr int INSTS = stage_insts(EB);
+    constexpr int kStageBytes = stage_bytes(EB);
+    constexpr int kStages = stages_for(EB);
+    constexpr int kRowBytes = kC0 * kD0 * EB + kXPadBytes;   // LDS pitch of a row of X
     extern __shared__ __align__(16) unsigned char lds[];
-    float* const zs = reinterpret_cast<float*>(lds + kStages * kStageBytes);   // [kRows][kBT][kZPitch]
+    float* const zs = reinterpret_cast<float*>(lds + kStages * kStageBytes);   // kZBufs x [kRows][kBT][kZPitch]
 
     const int t = threadIdx.x;
     const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
@@ -77,96 +110,160 @@ __global__ __launch_bounds__(kStreamThreads) void fused_pair_kernel(const TX* __
     const int64_t row_end = min(args.batch, row_begin + int64_t(args.rows_per_split));
     const int nsteps = static_cast<int>((row_end - row_begin + kRows - 1) / kRows);
 
-    if (t >= kConsumerThreads) {
+    if (t >= kFusedConsumers * 64) {
         // ------------------------------------------------------ loader wave
         StageMap m;
         m.rows = kRows;
         m.blocks = 1;
         m.blk_vec = kC0 * kD0 / VW;                        // one whole row of X
-        m.pad_vec = 0;
-        m.row_vec = m.blk_vec;
+        m.pad_vec = kXPadBytes / 16;
+        m.row_vec = m.blk_vec + m.pad_vec;
         m.gstride = 0;
         LoaderPlan<INSTS> lp;
-        make_loader_plan<INSTS>(m, INSTS, VW, EB, args.n_in, 1, m.blk_vec, t - kConsumerThreads, &lp);
+        make_loader_plan<INSTS>(m, INSTS, VW, EB, args.n_in, 1, m.blk_vec, t - kFusedConsumers * 64, &lp);
         auto issue = [&](int s) {
             const int64_t n0 = row_begin + int64_t(s) * kRows;
             issue_stage<INSTS>(lp, INSTS, X + n0 * args.n_in, stage_limit(n0, row_end, args.n_in, EB),
                                lds + (s % kStages) * kStageBytes);
         };
         for (int s = 0; s < kStages - 1 && s < nsteps; ++s) issue(s);
-        for (int s = 0; s < nsteps; ++s) {
-            wait_vmcnt_upto(min(kStages - 2, nsteps - 1 - s) * INSTS);
-            lds_barrier();                                   // stage s ready
+        for (int s = 0; s <= nsteps; ++s) {
+            if (s < nsteps) wait_vmcnt_upto(min(kStages - 2, nsteps - 1 - s) * INSTS);
+            lds_barrier();                                   // stage s ready, Z of stage s - 1 written
             if (s + kStages - 1 < nsteps) issue(s + kStages - 1);
-            lds_barrier();                                   // Z written
         }
         return;
     }
 
     // ---------------------------------------------------------- consumers
-    // (A) thread -> delta0 and two beta0 values of the tile
-    const int d0 = t & (kD0 - 1);
-    const int bpair = t >> 6;                              // 0..3
-    float k0r[2][kC0];
+    // Both phases are batched 4x4 outer products on the matrix cores: in
+    // v_mfma_f32_4x4x1f32 lane l belongs to block l / 4, supplies row l % 4
+    // of that block's A column and column l % 4 of its B row, and receives
+    // D[i][l % 4] of its block in accumulator register i. One instruction
+    // per gamma and group of 4 output columns.
+    const int lane = t & 63;
+    const int wave = t >> 6;
+    const int q = lane & 3;                                // A: row; B and D: column within a group of 4
+    // (A) block = delta0, A = X[row][gamma0][delta0], B = K0[0][delta0][beta0][gamma0];
+    // wave w -> delta0 in [16 (w % 4), 16 (w % 4) + 16) and kSetsPerWave
+    // groups of 4 beta0, all kRows rows
+    const int a_d0 = 16 * (wave & 3) + (lane >> 2);        // delta0 of this lane's block
+    const int a_b0 = (wave >> 2) * kSetsPerWave * 4;       // first beta0 (within the tile) of the wave
+    float k0r[kSetsPerWave][kC0];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const TW* kp = K0 + (int64_t(d0) * args.b0 + beta0 + 2 * bpair + j) * kC0;   // K0[0][d0][beta][:]
+    for (int j = 0; j < kSetsPerWave; ++j) {
+        const TW* kp = K0 + (int64_t(a_d0) * args.b0 + beta0 + a_b0 + 4 * j + q) * kC0;   // K0[0][d0][beta][:]
 #pragma unroll
         for (int g = 0; g < kC0; ++g) k0r[j][g] = to_f32(kp[g]);
     }
-    // (B) thread -> one of two rows, (alpha1, beta1) and a run of 4 delta1:
-    // lanes in (alpha1, beta1, run) order store 16-byte vectors that tile
-    // the row's slab of Y contiguously
-    const int rsub = t >> 7;                               // row within a pair of rows
-    const int run = t & 1;
-    const int b1 = (t >> 1) & (kB1 - 1);
-    const int a1 = (t >> 4) & (kBT - 1);                   // 0..7 within the tile
-    const int e10 = run * 4;                               // first delta1 of the run
-    float k1r[4][kC1];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const TW* kp = K1 + ((int64_t(beta0 + a1) * kD1 + e10 + k) * kB1 + b1) * kC1;   // K1[a][e][b][:]
-#pragma unroll
-        for (int g = 0; g < kC1; ++g) k1r[k][g] = to_f32(kp[g]);
-    }
-    const int64_t yoff = int64_t(beta0 + a1) * (kB1 * kD1) + b1 * kD1 + e10;
 
-    for (int s = 0; s < nsteps; ++s) {
-        lds_barrier();                                                   // stage s ready
+    // (A) Z[r][beta0][d0] = sum_g K0[0][d0][beta0][g] * X[r][g][d0] for stage s
+    auto phase_a = [&](int s, float* zb) {
         const unsigned char* xs = lds + (s % kStages) * kStageBytes;
-        const int64_t n0 = row_begin + int64_t(s) * kRows;
-        const int rows = static_cast<int>(min(int64_t(kRows), row_end - n0));
-        // (A) Z[r][beta0][d0] = sum_g K0[0][d0][beta0][g] * X[r][g][d0]
 #pragma unroll
-        for (int r = 0; r < kRows; ++r) {
-            const TX* xr = reinterpret_cast<const TX*>(xs + r * kC0 * kD0 * EB) + d0;
-            float z0 = 0.0f, z1 = 0.0f;
+        for (int rg = 0; rg < kRows; rg += 4) {
+            const TX* xa = reinterpret_cast<const TX*>(xs + (rg + q) * kRowBytes) + a_d0;
+            floatx4 z[kSetsPerWave];
+#pragma unroll
+            for (int j = 0; j < kSetsPerWave; ++j) z[j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int g = 0; g < kC0; ++g) {
-                const float x = to_f32(xr[g * kD0]);
-                z0 = fmaf(k0r[0][g], x, z0);
-                z1 = fmaf(k0r[1][g], x, z1);
-            }
-            float* zr = zs + (r * kBT + 2 * bpair) * kZPitch + d0;
-            zr[0] = z0;
-            zr[kZPitch] = z1;
-        }
-        lds_barrier();                                                   // Z written
-        // (B) Y[r][a1][b1][e1] = sum_g K1[a1][e1][b1][g] * Z[r][a1][g * 8 + e1]
+                const float x = to_f32(xa[g * kD0]);
 #pragma unroll
-        for (int r0 = 0; r0 < kRows; r0 += 2) {
-            const int r = r0 + rsub;
-            const float* zr = zs + (r * kBT + a1) * kZPitch + e10;
-            floatx4 y = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+                for (int j = 0; j < kSetsPerWave; ++j) z[j] = __builtin_amdgcn_mfma_f32_4x4x1f32(x, k0r[j][g], z[j], 0, 0, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < kSetsPerWave; ++j) {
+                float* zw = zb + rg * kZRow + (a_b0 + 4 * j + q) * kZPitch + a_d0;   // lane's beta0 and delta0
+#pragma unroll
+                for (int i = 0; i < 4; ++i) zw[i * kZRow] = z[j][i];
+            }
+        }
+    };
+
+    // one barrier per stage: phase A of stage s and phase B of stage s - 1
+    // share an iteration, on alternate Z buffers
+    auto pipeline = [&](auto&& phase_b) {
+        for (int s = 0; s <= nsteps; ++s) {
+            lds_barrier();                                   // stage s ready, Z of stage s - 1 written
+            if (s < nsteps) phase_a(s, zs + (s & 1) * kZFloats);
+            if (s > 0) phase_b(s - 1, zs + ((s - 1) & 1) * kZFloats);
+        }
+    };
+
+    if constexpr (phase_b_mfma(EB)) {
+        // (B) block = (alpha1, delta1), A = Z[row][alpha1][gamma1 * 8 + delta1],
+        // B = K1[alpha1][delta1][beta1][gamma1]; wave w -> alpha1 in
+        // {2w, 2w + 1} (within the tile), all 8 delta1 and both groups of 4
+        // beta1. A wave's store of one accumulator register covers, for one
+        // row, Y[alpha1][beta1 of the group][all delta1]: two runs of 128 bytes.
+        const int b_e1 = (lane >> 2) & (kD1 - 1);
+        const int b_a1 = 2 * wave + (lane >> 5);
+        float k1m[2][kC1];
+#pragma unroll
+        for (int grp = 0; grp < 2; ++grp) {
+            const TW* kp = K1 + ((int64_t(beta0 + b_a1) * kD1 + b_e1) * kB1 + 4 * grp + q) * kC1;   // K1[a][e][b][:]
+#pragma unroll
+            for (int g = 0; g < kC1; ++g) k1m[grp][g] = to_f32(kp[g]);
+        }
+        const int64_t yoff = int64_t(beta0 + b_a1) * (kB1 * kD1) + q * kD1 + b_e1;
+        auto phase_b = [&](int s, const float* zb) {
+            const int64_t n0 = row_begin + int64_t(s) * kRows;
+            const int rows = static_cast<int>(min(int64_t(kRows), row_end - n0));
+            const float* za = zb + q * kZRow + b_a1 * kZPitch + b_e1;
+            floatx4 y[2] = {floatx4{0.0f, 0.0f, 0.0f, 0.0f}, floatx4{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
             for (int g = 0; g < kC1; ++g) {
-                const floatx4 z = *reinterpret_cast<const floatx4*>(zr + g * kD1);
-#pragma unroll
-                for (int k = 0; k < 4; ++k) y[k] = fmaf(k1r[k][g], z[k], y[k]);
+                const float z = za[g * kD1];
+                y[0] = __builtin_amdgcn_mfma_f32_4x4x1f32(z, k1m[0][g], y[0], 0, 0, 0);
+                y[1] = __builtin_amdgcn_mfma_f32_4x4x1f32(z, k1m[1][g], y[1], 0, 0, 0);
             }
-            if (r < rows)
-                __builtin_nontemporal_store(y, reinterpret_cast<floatx4*>(Y + (n0 + r) * args.n_out + yoff));
+            float* yr = Y + n0 * args.n_out + yoff;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (i < rows) {
+                    __builtin_nontemporal_store(y[0][i], yr + i * args.n_out);
+                    __builtin_nontemporal_store(y[1][i], yr + i * args.n_out + 4 * kD1);
+                }
+            }
+        };
+        pipeline(phase_b);
+    } else {
+        // (B) thread -> one row of a pass, (alpha1, beta1) and a run of 4 delta1:
+        // lanes in (alpha1, beta1, run) order store 16-byte vectors that tile
+        // the row's slab of Y contiguously
+        const int rsub = t / (kBT * kB1 * 2);              // row within a pass
+        const int run = t & 1;
+        const int b1 = (t >> 1) & (kB1 - 1);
+        const int a1 = (t >> 4) & (kBT - 1);               // alpha1 within the tile
+        const int e10 = run * 4;                           // first delta1 of the run
+        float k1r[4][kC1];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const TW* kp = K1 + ((int64_t(beta0 + a1) * kD1 + e10 + k) * kB1 + b1) * kC1;   // K1[a][e][b][:]
+#pragma unroll
+            for (int g = 0; g < kC1; ++g) k1r[k][g] = to_f32(kp[g]);
         }
+        const int64_t yoff = int64_t(beta0 + a1) * (kB1 * kD1) + b1 * kD1 + e10;
+        auto phase_b = [&](int s, const float* zb) {
+            const int64_t n0 = row_begin + int64_t(s) * kRows;
+            const int rows = static_cast<int>(min(int64_t(kRows), row_end - n0));
+#pragma unroll
+            for (int r0 = 0; r0 < kRows; r0 += kRowsPerPass) {
+                const int r = r0 + rsub;
+                const float* zr = zb + r * kZRow + a1 * kZPitch + e10;
+                floatx4 y = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int g = 0; g < kC1; ++g) {
+                    const floatx4 z = *reinterpret_cast<const floatx4*>(zr + g * kD1);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) y[k] = fmaf(k1r[k][g], z[k], y[k]);
+                }
+                if (r < rows)
+                    __builtin_nontemporal_store(y, reinterpret_cast<floatx4*>(Y + (n0 + r) * args.n_out + yoff));
+            }
+        };
+        pipeline(phase_b);
     }
 }
 
@@ -185,17 +282,17 @@ ks_status_t launch_typed(const Shape& s0, const Shape& s1, const void* W0, const
     args.n_out = s1.n_out;
     args.batch = batch;
     args.n_tiles = s0.b / kBT;
-    // about one resident wave of workgroups (two per compute unit)
+    // about one resident wave of workgroups (as many per compute unit as fit its 160 KB of LDS)
+    const size_t lds = fused_lds_bytes(int(sizeof(TX)));
+    const int per_cu = std::max(1, std::min(4, int((160 * 1024) / lds)));
     const int64_t steps_total = (batch + kRows - 1) / kRows;
-    const int64_t splits = std::max<int64_t>(1, int64_t(std::max(num_cus, 1)) * 2 / args.n_tiles);
+    const int64_t splits = std::max<int64_t>(1, int64_t(std::max(num_cus, 1)) * per_cu / args.n_tiles);
     const int64_t steps = std::max<int64_t>(1, (steps_total + splits - 1) / splits);
     args.rows_per_split = static_cast<int>(steps * kRows);
     const int64_t nsplit = (batch + args.rows_per_split - 1) / args.rows_per_split;
     const int64_t blocks = nsplit * args.n_tiles;
     if (blocks > 0x7fffffff) return KS_ERR_UNSUPPORTED;
-    const size_t lds = size_t(kStages) * (kInsts * int(sizeof(TX)) / 4) * 1024 +
-                       size_t(kRows) * kBT * kZPitch * sizeof(float);
-    return launch_kernel(fused_pair_kernel<TX, TW>, dim3(static_cast<unsigned>(blocks)), dim3(kStreamThreads),
+    return launch_kernel(fused_pair_kernel<TX, TW>, dim3(static_cast<unsigned>(blocks)), dim3(kFusedThreads),
                          lds, stream, static_cast<const TX*>(X), static_cast<const TW*>(W0),
                          static_cast<const TW*>(W1), Y, args);
 }

@@ -289,6 +289,27 @@ def test_gpt2_chain_full_size_sampled(fuse):
     _chain_workload("gpt2_mlp", False, fuse, rows=sample_rows(16384))
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("lead", [False, True])
+@pytest.mark.parametrize("b0", [8, 64, 128])
+def test_fused_pair_shapes(b0, lead, bf16):
+    """The one-launch pair (1, b0, 16, 64) -> (b0, 8, 8, 8) for several b0,
+    with a ragged row count; behind a leading factor in a bf16 chain the
+    pair reads fp32 rows with bf16 weights."""
+    pats = [(1, b0, 16, 64), (b0, 8, 8, 8)]
+    sig = [0.25, 1.0 / np.sqrt(8.0)]
+    if lead:
+        pats = [(4, 16, 16, 16)] + pats
+        sig = [0.25] + sig
+    wl = datagen.Workload("pair", pats, 203, sig, 40 + b0)
+    groups = libks.ks_chain_groups(wl.patterns, wl.batch, libks.DTYPE_BF16 if bf16 else libks.DTYPE_F32)
+    assert [len(g) for g in groups] == ([1, 2] if lead else [2])
+    X, Ws = datagen.draw(wl)
+    Y = libks.chain_matmul(to_dev(X, bf16), [to_dev(W, bf16) for W in Ws], wl.patterns)
+    torch.cuda.synchronize()
+    chain_check(wl.patterns, X, Ws, Y.cpu().numpy(), bf16)
+
+
 def test_gpt2_factors_single():
     wl = datagen.get("gpt2_mlp")
     wl = datagen.scaled(wl, 257)
