@@ -97,6 +97,7 @@ struct MfmaArgs {
     int stages;              // LDS ring depth
     int ytile_bytes;         // LDS bytes of one Y tile buffer
     int xcd_remap;           // 1: renumber workgroups so neighbouring tiles share an XCD
+    int vec_a;               // 1: the tile's deltas per gamma come in runs of 4 (dt % 4 == 0)
     int bsplit;              // tiles per (alpha, delta) block: b = bsplit * BT
     int b;                   // outputs per block (the K block stride is b * c)
     StageMap xmap;           // LDS layout of an X stage
@@ -284,13 +285,22 @@ __global__ __launch_bounds__(kStreamThreads + 64 * NS) void mfma_kernel(const TX
     const int wp = wave / WN;                     // pairs wp, wp + WP, ..
 
     const int gsx = contig ? d * EB : xblk_bytes;          // X: gamma stride in LDS
+    // A operands of 4 pairs with consecutive deltas (same alpha) lie side by
+    // side in the X stage, so one 4-element LDS read feeds all four. Single
+    // reads of one pair's operands (16 rows x 4 gammas) fall on a quarter of
+    // the banks when the gamma stride is a multiple of 16 bytes: 8-way
+    // conflicts, which the vector reads avoid and with a quarter of the LDS
+    // instructions. Used for the large contractions, where a wave holds 4
+    // pairs or more.
+    constexpr int VDX = (C >= 64 && PW % 4 == 0) ? 4 : 1;
+    const bool vec = VDX > 1 && args.vec_a != 0;
     const int bsy = contig ? d * 4 : args.yc.seg_lds;      // Y: beta stride in LDS
     int xoff[PW], yoff[PW];
     bool pv[PW];
     float breg[PW][NTW][KS];
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
-        const int p = wp + WP * i;
+        const int p = vec ? 4 * (wp + WP * (i / 4)) + (i % 4) : wp + WP * i;   // runs of 4 deltas
         const int al = p / args.dt;
         const int de = p - al * args.dt;
         pv[i] = p < args.at * args.dt && al < at_eff && de < dt_eff;
@@ -317,28 +327,66 @@ __global__ __launch_bounds__(kStreamThreads + 64 * NS) void mfma_kernel(const TX
         lds_barrier();                                                   // stage s ready
         const unsigned char* xcur = lds + (s % kStages) * kStageBytes;
         unsigned char* const ys = NS > 0 ? ys0 + (s & 1) * args.ytile_bytes : ys0;
+        if (VDX > 1 && vec) {
 #pragma unroll
-        for (int i = 0; i < PW; ++i) {
-            if (!pv[i]) continue;
-            floatx4 acc[NTW];
+            for (int j = 0; j < PW / VDX; ++j) {
+                if (!pv[VDX * j]) continue;
+                floatx4 acc[VDX][NTW];
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) acc[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-            const unsigned char* xa = xcur + arow * xrow_bytes + xoff[i] + akk * gsx;
+                for (int u = 0; u < VDX; ++u)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const float av = to_f32(*reinterpret_cast<const TX*>(xa + ks * 4 * gsx));
+                    for (int nt = 0; nt < NTW; ++nt) acc[u][nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+                const unsigned char* xa = xcur + arow * xrow_bytes + xoff[VDX * j] + akk * gsx;
 #pragma unroll
-                for (int nt = 0; nt < NTW; ++nt)
-                    acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, breg[i][nt][ks], acc[nt], 0, 0, 0);
+                for (int ks = 0; ks < KS; ++ks) {
+                    float av[4];
+                    load4_f32(reinterpret_cast<const TX*>(xa + ks * 4 * gsx), av);
+#pragma unroll
+                    for (int u = 0; u < VDX; ++u)
+#pragma unroll
+                        for (int nt = 0; nt < NTW; ++nt)
+                            acc[u][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], breg[VDX * j + u][nt][ks],
+                                                                              acc[u][nt], 0, 0, 0);
+                }
+#pragma unroll
+                for (int u = 0; u < VDX; ++u) {
+                    if (!pv[VDX * j + u]) continue;
+#pragma unroll
+                    for (int nt = 0; nt < NTW; ++nt) {
+                        const int beta = (wn * NTW + nt) * 16 + (lane & 15);
+                        unsigned char* yb = ys + yoff[VDX * j + u] + beta * bsy;
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const int row = 4 * (lane >> 4) + v;
+                            *reinterpret_cast<float*>(yb + row * args.yc.lds_row) = acc[u][nt][v];
+                        }
+                    }
+                }
             }
+        } else {
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) {
-                const int beta = (wn * NTW + nt) * 16 + (lane & 15);
-                unsigned char* yb = ys + yoff[i] + beta * bsy;
+            for (int i = 0; i < PW; ++i) {
+                if (!pv[i]) continue;
+                floatx4 acc[NTW];
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int row = 4 * (lane >> 4) + v;
-                    *reinterpret_cast<float*>(yb + row * args.yc.lds_row) = acc[nt][v];
+                for (int nt = 0; nt < NTW; ++nt) acc[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+                const unsigned char* xa = xcur + arow * xrow_bytes + xoff[i] + akk * gsx;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const float av = to_f32(*reinterpret_cast<const TX*>(xa + ks * 4 * gsx));
+#pragma unroll
+                    for (int nt = 0; nt < NTW; ++nt)
+                        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, breg[i][nt][ks], acc[nt], 0, 0, 0);
+                }
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) {
+                    const int beta = (wn * NTW + nt) * 16 + (lane & 15);
+                    unsigned char* yb = ys + yoff[i] + beta * bsy;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int row = 4 * (lane >> 4) + v;
+                        *reinterpret_cast<float*>(yb + row * args.yc.lds_row) = acc[nt][v];
+                    }
                 }
             }
         }
@@ -664,6 +712,7 @@ ks_status_t launch_mfma_lds(const FactorCall& f) {
     args.ytile_bytes = g.ytile;
     // neighbouring tiles share X lines (segmented) or all of X (split b)
     args.xcd_remap = (g.contiguous && g.bsplit == 1) ? 0 : 1;
+    args.vec_a = g.dt % 4 == 0 ? 1 : 0;
     args.bsplit = g.bsplit;
     args.b = f.s.b;
     args.xmap = g.xmap;
