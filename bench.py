@@ -387,9 +387,8 @@ def main():
             "flops_per_step": flops,
             "chain_fused": bool(chain and not args.no_fuse),
             "kernel": args.kernel if not chain else "chain",
-            "plan": "; ".join(libks.ks_plan_describe(p, batch, libks.DTYPE_F32 if not bf16 else
-                                                     (libks.DTYPE_BF16 if i == 0 else libks.DTYPE_BF16W))
-                              for i, p in enumerate(wl.patterns)),
+            "plan": chain_plan_text(wl.patterns, batch, dt, flags, bf16) if chain else
+                    libks.ks_plan_describe(wl.patterns[0], batch, dt),
             "rotating_sets": nset,
             "parallelism": "single GPU",
         },
@@ -400,6 +399,22 @@ def main():
         out["per_factor"] = per_factor
     print(json.dumps(out), flush=True)
     return 0
+
+
+def chain_plan_text(patterns, batch, dt, flags, bf16) -> str:
+    """One entry per launch of the chain: the kernel plan of a single factor,
+    or the pair that runs as one launch."""
+    from kronecker_sparse_structured_amd import libks
+    parts = []
+    for grp in libks.ks_chain_groups(patterns, batch, dt, flags):
+        if len(grp) == 2:
+            parts.append("fused pair %s -> %s (one launch, intermediate in LDS)"
+                         % (tuple(patterns[grp[0]]), tuple(patterns[grp[1]])))
+        else:
+            k = grp[0]
+            fdt = libks.DTYPE_F32 if not bf16 else (libks.DTYPE_BF16 if k == 0 else libks.DTYPE_BF16W)
+            parts.append(libks.ks_plan_describe(patterns[k], batch, fdt))
+    return "; ".join(parts)
 
 
 def sweep(args) -> int:

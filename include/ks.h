@@ -169,8 +169,14 @@ ks_status_t ks_chain_workspace_size(const ks_pattern_t* p, int n, int64_t batch,
  *          may be NULL when that size is 0. 16-byte aligned. Must not
  *          overlap X, Y or any W.
  *   flags  KS_CHAIN_AUTO: consecutive factors whose joint tile fits on chip
- *          run as one fused launch with the intermediate kept in LDS.
- *          KS_CHAIN_NO_FUSE: one launch per factor.
+ *          run as one fused launch with the intermediate kept in LDS. Two
+ *          pair families are fused, scanning the chain from factor 0:
+ *          (1, b0, 16, 64) -> (b0, 8, 8, 8) with b0 % 8 == 0 (a group of
+ *          beta0 needs whole rows of X and yields a slab of Y's row), and
+ *          (a, 16, 16, 16) -> (16a, 16, 16, 1) (the second factor works
+ *          inside the first one's per-alpha output slabs; the last two
+ *          factors of the 16-ary butterfly). KS_CHAIN_NO_FUSE: one launch
+ *          per factor. Results of the two modes agree to rounding.
  * All launches go to `stream` in order; there is no host synchronisation.
  */
 ks_status_t ks_chain_matmul(const ks_pattern_t* p, int n, const void* const* W,

@@ -119,6 +119,7 @@ struct ChainPlan {
     std::vector<Shape> shapes;
     std::vector<int> group_start;  // first factor of each launch group
     std::vector<int> group_len;    // 1 (single factor) or 2 (fused pair)
+    std::vector<int> group_kind;   // 0 single factor, 1 row-fused pair, 2 slab-fused pair
     int xt0 = ks::kF32, wt = ks::kF32;
     int64_t max_mid = 0;           // widest intermediate between groups
     int nbuf = 0;                  // workspace buffers (0, 1 or 2)
@@ -143,12 +144,19 @@ ks_status_t plan_chain(const ks_pattern_t* p, int n, int64_t batch, ks_dtype_t d
     }
     for (int k = 0; k < n;) {
         const int xt = (k == 0) ? plan->xt0 : ks::kF32;
-        int len = 1;
-        if (flags == KS_CHAIN_AUTO && k + 1 < n &&
-            ks::fused_pair_supports(plan->shapes[k], plan->shapes[k + 1], xt, plan->wt, plan->wt))
-            len = 2;
+        int len = 1, kind = 0;
+        if (flags == KS_CHAIN_AUTO && k + 1 < n) {
+            if (ks::fused_pair_supports(plan->shapes[k], plan->shapes[k + 1], xt, plan->wt, plan->wt)) {
+                len = 2;
+                kind = 1;
+            } else if (ks::slab_pair_supports(plan->shapes[k], plan->shapes[k + 1], xt, plan->wt, plan->wt)) {
+                len = 2;
+                kind = 2;
+            }
+        }
         plan->group_start.push_back(k);
         plan->group_len.push_back(len);
+        plan->group_kind.push_back(kind);
         k += len;
     }
     const int groups = static_cast<int>(plan->group_start.size());
@@ -289,9 +297,12 @@ ks_status_t ks_chain_matmul(const ks_pattern_t* p, int n, const void* const* W,
         const int k = plan.group_start[g];
         float* out = (g == groups - 1) ? static_cast<float*>(Y)
                                        : reinterpret_cast<float*>(bufs[g % 2]);
-        if (plan.group_len[g] == 2) {
+        if (plan.group_kind[g] == 1) {
             st = ks::launch_fused_pair(plan.shapes[k], plan.shapes[k + 1], cur_t, plan.wt, plan.wt,
                                        W[k], W[k + 1], cur, out, batch, stream, cus);
+        } else if (plan.group_kind[g] == 2) {
+            st = ks::launch_slab_pair(plan.shapes[k], plan.shapes[k + 1], cur_t, plan.wt, plan.wt,
+                                      W[k], W[k + 1], cur, out, batch, stream, cus);
         } else {
             ks::FactorCall f;
             f.s = plan.shapes[k]; f.xt = cur_t; f.wt = plan.wt; f.W = W[k]; f.X = cur; f.Y = out;

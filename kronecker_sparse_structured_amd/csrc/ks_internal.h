@@ -83,4 +83,12 @@ ks_status_t launch_fused_pair(const Shape& s0, const Shape& s1, int xt, int wt0,
                               const void* W0, const void* W1, const void* X, float* Y,
                               int64_t batch, hipStream_t stream, int num_cus);
 
+// Fused pair whose second factor works inside the first one's output slabs:
+// F = (a, 16, 16, 16) then G = (16 a, 16, 16, 1). KS_ERR_UNSUPPORTED when the
+// pair is not of that family.
+bool slab_pair_supports(const Shape& s0, const Shape& s1, int xt, int wt0, int wt1);
+ks_status_t launch_slab_pair(const Shape& s0, const Shape& s1, int xt, int wt0, int wt1,
+                             const void* W0, const void* W1, const void* X, float* Y,
+                             int64_t batch, hipStream_t stream, int num_cus);
+
 }  // namespace ks

@@ -164,6 +164,22 @@ def test_chain_plan():
     assert sum(len(g) for g in groups) == 3 and all(len(g) in (1, 2) for g in groups)
 
 
+def test_chain_plan_fuses_known_pairs():
+    """The planner fuses the GPT-2 pair (rows shared by groups of beta0) and
+    the butterfly's last two factors (the second works inside the first's
+    output slabs); nothing else in those chains, and nothing with NO_FUSE."""
+    gpt2 = [(1, 64, 16, 64), (64, 8, 8, 8)]
+    bfly = [(16 ** k, 16, 16, 16 ** (3 - k)) for k in range(4)]
+    for dt in (libks.DTYPE_F32, libks.DTYPE_BF16):
+        assert libks.ks_chain_groups(gpt2, 1000, dt) == [[0, 1]]
+        assert libks.ks_chain_groups(bfly, 1000, dt) == [[0], [1], [2, 3]]
+        assert libks.ks_chain_groups(bfly, 1000, dt, libks.CHAIN_NO_FUSE) == [[0], [1], [2], [3]]
+    # slab family: (a, 16, 16, 16) -> (16 a, 16, 16, 1) for any a; other shapes stay apart
+    assert libks.ks_chain_groups([(3, 16, 16, 16), (48, 16, 16, 1)], 7, libks.DTYPE_F32) == [[0, 1]]
+    assert libks.ks_chain_groups([(4, 16, 16, 16), (64, 16, 8, 2)], 7, libks.DTYPE_F32) == [[0], [1]]
+    assert libks.ks_chain_groups([(4, 8, 16, 16), (32, 16, 16, 1)], 7, libks.DTYPE_F32) == [[0], [1]]
+
+
 def test_one_hip_runtime_whatever_the_import_order():
     """Loading libks before torch must still leave a single HIP runtime in
     the process (torch bundles its own; libks has to bind to that one)."""

@@ -310,6 +310,28 @@ def test_fused_pair_shapes(b0, lead, bf16):
     chain_check(wl.patterns, X, Ws, Y.cpu().numpy(), bf16)
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("lead", [False, True])
+@pytest.mark.parametrize("a", [1, 3, 16])
+def test_slab_pair_shapes(a, lead, bf16):
+    """The one-launch pair (a, 16, 16, 16) -> (16 a, 16, 16, 1) (the second
+    factor works inside the first one's output slabs) for several a, with a
+    ragged row count; behind a leading factor in a bf16 chain the pair reads
+    fp32 rows with bf16 weights."""
+    pats = [(a, 16, 16, 16), (16 * a, 16, 16, 1)]
+    sig = [0.25, 0.25]
+    if lead:
+        pats = [(a * 16, 4, 4, 4)] + pats
+        sig = [0.5] + sig
+    wl = datagen.Workload("slab", pats, 203, sig, 70 + a)
+    groups = libks.ks_chain_groups(wl.patterns, wl.batch, libks.DTYPE_BF16 if bf16 else libks.DTYPE_F32)
+    assert [len(g) for g in groups] == ([1, 2] if lead else [2])
+    X, Ws = datagen.draw(wl)
+    Y = libks.chain_matmul(to_dev(X, bf16), [to_dev(W, bf16) for W in Ws], wl.patterns)
+    torch.cuda.synchronize()
+    chain_check(wl.patterns, X, Ws, Y.cpu().numpy(), bf16)
+
+
 def test_gpt2_factors_single():
     wl = datagen.get("gpt2_mlp")
     wl = datagen.scaled(wl, 257)
