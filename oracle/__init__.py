@@ -52,6 +52,10 @@ def _bind(lib):
                                         ctypes.POINTER(ctypes.c_float), ctypes.c_longlong,
                                         dp, dp, dp]
     lib.ks_oracle_chain_err.restype = ctypes.c_int
+    lib.ks_oracle_matmul_dx.argtypes = [ctypes.c_int] * 4 + [dp, dp, dp, ctypes.c_longlong]
+    lib.ks_oracle_matmul_dx.restype = ctypes.c_int
+    lib.ks_oracle_matmul_dw.argtypes = [ctypes.c_int] * 4 + [dp, dp, dp, ctypes.c_longlong]
+    lib.ks_oracle_matmul_dw.restype = ctypes.c_int
     lib.ks_oracle_num_threads.argtypes = []
     lib.ks_oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -101,6 +105,36 @@ def ks_matmul(pattern: Sequence[int], K: np.ndarray, X: np.ndarray, lib=None) ->
     Y = np.empty((batch, a * b * d), dtype=np.float64)
     _check(lib.ks_oracle_matmul(a, b, c, d, _dptr(K), _dptr(X), _dptr(Y), batch), "ks_matmul")
     return Y
+
+
+def ks_matmul_dx(pattern: Sequence[int], K: np.ndarray, dY: np.ndarray, lib=None) -> np.ndarray:
+    """dL/dX = dY W for one factor (see ks_oracle.c); dY is batch x a*b*d, fp64."""
+    lib = lib or load()
+    a, b, c, d = (int(v) for v in pattern)
+    K = np.ascontiguousarray(K, dtype=np.float64).reshape(-1)
+    dY = np.ascontiguousarray(dY, dtype=np.float64)
+    if K.size != a * b * c * d:
+        raise ValueError("K has %d values, pattern needs %d" % (K.size, a * b * c * d))
+    batch = dY.shape[0]
+    if dY.size != batch * a * b * d:
+        raise ValueError("dY width does not match a*b*d")
+    dX = np.empty((batch, a * c * d), dtype=np.float64)
+    _check(lib.ks_oracle_matmul_dx(a, b, c, d, _dptr(K), _dptr(dY), _dptr(dX), batch), "ks_matmul_dx")
+    return dX
+
+
+def ks_matmul_dw(pattern: Sequence[int], dY: np.ndarray, X: np.ndarray, lib=None) -> np.ndarray:
+    """dL/dK for one factor, shape (a, d, b, c) (see ks_oracle.c); fp64 inputs."""
+    lib = lib or load()
+    a, b, c, d = (int(v) for v in pattern)
+    dY = np.ascontiguousarray(dY, dtype=np.float64)
+    X = np.ascontiguousarray(X, dtype=np.float64)
+    batch = dY.shape[0]
+    if dY.size != batch * a * b * d or X.size != batch * a * c * d:
+        raise ValueError("dY / X widths do not match the pattern")
+    dK = np.empty((a, d, b, c), dtype=np.float64)
+    _check(lib.ks_oracle_matmul_dw(a, b, c, d, _dptr(dY), _dptr(X), _dptr(dK), batch), "ks_matmul_dw")
+    return dK
 
 
 def _chain_args(patterns, Ks):

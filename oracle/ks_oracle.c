@@ -92,6 +92,79 @@ int ks_oracle_matmul(int a, int b, int c, int d, const double* K,
     return KS_ORACLE_OK;
 }
 
+/*
+ * Gradients of one factor, for the layer's backward pass. The pages give the
+ * layer (a KS linear layer usable from PyTorch) but not its derivatives;
+ * these are the plain chain rule on Y = X * W^T with the support above.
+ * Given dY = dL/dY (batch x a*b*d):
+ *   dL/dX = dY * W, i.e. for every row n
+ *       dX[n][alpha][gamma][delta] = sum_beta K[alpha][delta][beta][gamma]
+ *                                            * dY[n][alpha][beta][delta];
+ *   dL/dK: each K[alpha][delta][beta][gamma] sits in W exactly once, at row
+ *   alpha*b*d + beta*d + delta and column alpha*c*d + gamma*d + delta, so it
+ *   collects that entry of dY^T * X:
+ *       dK[alpha][delta][beta][gamma] = sum_n dY[n][alpha][beta][delta]
+ *                                             * X[n][alpha][gamma][delta].
+ * Both are evaluated exactly as written, in fp64: beta ascending for dX,
+ * n ascending for dK.
+ */
+
+/* dX of one row (a*c*d) from dy (a*b*d). */
+static void ks_dx_row(int a, int b, int c, int d, const double* K,
+                      const double* dy, double* dx) {
+    for (int alpha = 0; alpha < a; ++alpha) {
+        for (int gamma = 0; gamma < c; ++gamma) {
+            for (int delta = 0; delta < d; ++delta) {
+                double acc = 0.0;
+                for (int beta = 0; beta < b; ++beta) {
+                    double k = K[(((long long)alpha * d + delta) * b + beta) * c + gamma];
+                    double g = dy[((long long)alpha * b + beta) * d + delta];
+                    acc += k * g;
+                }
+                dx[((long long)alpha * c + gamma) * d + delta] = acc;
+            }
+        }
+    }
+}
+
+int ks_oracle_matmul_dx(int a, int b, int c, int d, const double* K,
+                        const double* dY, double* dX, long long batch) {
+    if (!pattern_ok(a, b, c, d) || batch < 0) return KS_ORACLE_BAD_ARG;
+    if (batch == 0) return KS_ORACLE_OK;
+    if (!K || !dY || !dX) return KS_ORACLE_BAD_ARG;
+    long long n_in = (long long)a * c * d;
+    long long n_out = (long long)a * b * d;
+#pragma omp parallel for schedule(static)
+    for (long long n = 0; n < batch; ++n)
+        ks_dx_row(a, b, c, d, K, dY + n * n_out, dX + n * n_in);
+    return KS_ORACLE_OK;
+}
+
+int ks_oracle_matmul_dw(int a, int b, int c, int d, const double* dY,
+                        const double* X, double* dK, long long batch) {
+    if (!pattern_ok(a, b, c, d) || batch < 0 || !dK) return KS_ORACLE_BAD_ARG;
+    if (batch > 0 && (!dY || !X)) return KS_ORACLE_BAD_ARG;
+    long long n_in = (long long)a * c * d;
+    long long n_out = (long long)a * b * d;
+    long long blocks = (long long)a * d;
+#pragma omp parallel for schedule(static)
+    for (long long blk = 0; blk < blocks; ++blk) {
+        int alpha = (int)(blk / d), delta = (int)(blk % d);
+        for (int beta = 0; beta < b; ++beta) {
+            for (int gamma = 0; gamma < c; ++gamma) {
+                double acc = 0.0;
+                for (long long n = 0; n < batch; ++n) {
+                    double g = dY[n * n_out + ((long long)alpha * b + beta) * d + delta];
+                    double v = X[n * n_in + ((long long)alpha * c + gamma) * d + delta];
+                    acc += g * v;
+                }
+                dK[(((long long)alpha * d + delta) * b + beta) * c + gamma] = acc;
+            }
+        }
+    }
+    return KS_ORACLE_OK;
+}
+
 /* Widths of a chain: width[0] = n_in of factor 0, width[k+1] = n_out of
  * factor k. Returns 0 when consecutive factors do not fit together. */
 static int chain_widths(int nf, const int* pat, long long* width) {

@@ -260,6 +260,53 @@ def pin_chain_err_streaming(lib):
     np.testing.assert_allclose(ma, np.max(np.abs(diff)), rtol=1e-12)
 
 
+def pin_backward_dense(lib):
+    """Gradients of Y = X W^T against the dense W from numpy.kron: dX equals
+    dY @ W, and dK equals dY^T @ X read at each K entry's position in W
+    (row alpha*b*d + beta*d + delta, column alpha*c*d + gamma*d + delta), on
+    integer data, exactly. Also a = d = 1 (dense GEMM gradients) and batch 0
+    (dK = 0)."""
+    rng = np.random.default_rng(111)
+    pats = [(2, 3, 4, 5), (3, 5, 2, 2), (1, 4, 6, 3), (4, 2, 2, 1), (1, 7, 5, 1), (2, 1, 3, 4), (3, 2, 1, 2)]
+    for p in pats:
+        a, b, c, d = p
+        K = int_data(rng, (a, d, b, c))
+        X = int_data(rng, (6, a * c * d))
+        dY = int_data(rng, (6, a * b * d))
+        W = dense_from_kron(p, K)
+        assert np.array_equal(oracle.ks_matmul_dx(p, K, dY, lib=lib), dY @ W), p
+        G = dY.T @ X
+        ref = np.empty((a, d, b, c))
+        for al, de, be, ga in itertools.product(range(a), range(d), range(b), range(c)):
+            ref[al, de, be, ga] = G[al * b * d + be * d + de, al * c * d + ga * d + de]
+        assert np.array_equal(oracle.ks_matmul_dw(p, dY, X, lib=lib), ref), p
+    A, B = int_data(rng, (5, 4)), int_data(rng, (5, 3))     # a = d = 1: Y = X K^T with K (3 x 4)
+    K = int_data(rng, (1, 1, 3, 4))
+    assert np.array_equal(oracle.ks_matmul_dx((1, 3, 4, 1), K, B, lib=lib), B @ K[0, 0])
+    assert np.array_equal(oracle.ks_matmul_dw((1, 3, 4, 1), B, A, lib=lib)[0, 0], B.T @ A)
+    z = oracle.ks_matmul_dw((2, 3, 4, 5), np.zeros((0, 30)), np.zeros((0, 40)), lib=lib)
+    assert z.shape == (2, 5, 3, 4) and not z.any()
+
+
+def pin_backward_adjoint(lib):
+    """<dY, f(X)> = <dL/dX, X> = <dL/dK, K> for L = <dY, f(X)> with f linear
+    in both X and K; and the gradient in X is the forward map of the
+    transposed pattern (a, c, b, d) with transposed blocks."""
+    rng = np.random.default_rng(112)
+    for p in [(2, 3, 4, 5), (1, 6, 2, 3), (5, 2, 3, 1), (3, 4, 4, 2)]:
+        a, b, c, d = p
+        K = int_data(rng, (a, d, b, c))
+        X = int_data(rng, (4, a * c * d))
+        dY = int_data(rng, (4, a * b * d))
+        L = np.sum(dY * oracle.ks_matmul(p, K, X, lib=lib))
+        dX = oracle.ks_matmul_dx(p, K, dY, lib=lib)
+        dK = oracle.ks_matmul_dw(p, dY, X, lib=lib)
+        assert np.sum(dX * X) == L, p
+        assert np.sum(dK * K) == L, p
+        Kt = np.ascontiguousarray(K.transpose(0, 1, 3, 2))
+        assert np.array_equal(dX, oracle.ks_matmul((a, c, b, d), Kt, dY, lib=lib)), p
+
+
 ALL_PINS = [
     pin_dense_kron_brute_force,
     pin_support_is_kronecker_mask,
@@ -273,4 +320,6 @@ ALL_PINS = [
     pin_linearity_and_adjoint,
     pin_chain_dense_product,
     pin_chain_err_streaming,
+    pin_backward_dense,
+    pin_backward_adjoint,
 ]

@@ -18,19 +18,37 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "ks_oracle.c")
 # (name, exact text in ks_oracle.c, replacement)
 MUTANTS = [
     ("swap_beta_gamma_in_K",
-     "* b + beta) * c + gamma]", "* c + gamma) * b + beta]"),
+     "* b + beta) * c + gamma];\n                    double v = x[", "* c + gamma) * b + beta];\n                    double v = x["),
     ("swap_alpha_delta_in_K",
-     "K[(((long long)alpha * d + delta) * b", "K[(((long long)delta * a + alpha) * b"),
+     "double k = K[(((long long)alpha * d + delta) * b + beta) * c + gamma];\n                    double v = x[",
+     "double k = K[(((long long)delta * a + alpha) * b + beta) * c + gamma];\n                    double v = x["),
     ("transpose_x_block",
-     "x[((long long)alpha * c + gamma) * d + delta]", "x[((long long)alpha * d + delta) * c + gamma]"),
+     "double v = x[((long long)alpha * c + gamma) * d + delta];", "double v = x[((long long)alpha * d + delta) * c + gamma];"),
     ("transpose_y_block",
-     "y[((long long)alpha * b + beta) * d + delta]", "y[((long long)alpha * d + delta) * b + beta]"),
+     " y[((long long)alpha * b + beta) * d + delta] = acc;", " y[((long long)alpha * d + delta) * b + beta] = acc;"),
     ("drop_last_gamma",
-     "gamma < c; ++gamma", "gamma < c - 1; ++gamma"),
+     "for (int gamma = 0; gamma < c; ++gamma) {\n                    double k",
+     "for (int gamma = 0; gamma < c - 1; ++gamma) {\n                    double k"),
     ("skip_first_gamma",
-     "int gamma = 0;", "int gamma = 1;"),
+     "for (int gamma = 0; gamma < c; ++gamma) {\n                    double k",
+     "for (int gamma = 1; gamma < c; ++gamma) {\n                    double k"),
     ("wrong_sign",
      "acc += k * v;", "acc += (gamma == 1 ? -k : k) * v;"),
+    ("dx_swap_beta_gamma_in_K",
+     "double k = K[(((long long)alpha * d + delta) * b + beta) * c + gamma];\n                    double g = dy",
+     "double k = K[(((long long)alpha * d + delta) * c + gamma) * b + beta];\n                    double g = dy"),
+    ("dx_drop_last_beta",
+     "for (int beta = 0; beta < b; ++beta) {\n                    double k", "for (int beta = 0; beta < b - 1; ++beta) {\n                    double k"),
+    ("dx_transpose_dy_block",
+     "double g = dy[((long long)alpha * b + beta) * d + delta];", "double g = dy[((long long)alpha * d + delta) * b + beta];"),
+    ("dw_drop_first_row",
+     "for (long long n = 0; n < batch; ++n) {\n                    double g = dY", "for (long long n = 1; n < batch; ++n) {\n                    double g = dY"),
+    ("dw_swap_alpha_delta_in_dK",
+     "dK[(((long long)alpha * d + delta) * b + beta) * c + gamma] = acc;", "dK[(((long long)delta * a + alpha) * b + beta) * c + gamma] = acc;"),
+    ("dw_transpose_output_block",
+     "dK[(((long long)alpha * d + delta) * b + beta) * c + gamma] = acc;", "dK[(((long long)alpha * d + delta) * c + gamma) * b + beta] = acc;"),
+    ("dw_x_at_wrong_delta",
+     "double v = X[n * n_in + ((long long)alpha * c + gamma) * d + delta];", "double v = X[n * n_in + ((long long)alpha * c + gamma) * d + (d - 1 - delta)];"),
     ("reverse_chain",
      "ks_factor_row(pat[4 * k], pat[4 * k + 1], pat[4 * k + 2], pat[4 * k + 3],\n                      Ks[k], cur, out);",
      "ks_factor_row(pat[4 * (nf - 1 - k)], pat[4 * (nf - 1 - k) + 1], pat[4 * (nf - 1 - k) + 2], pat[4 * (nf - 1 - k) + 3],\n                      Ks[nf - 1 - k], cur, out);"),
