@@ -144,6 +144,55 @@ ks_status_t ks_matmul_ex(ks_pattern_t p, const void* W, const void* X, void* Y,
                          const ks_options_t* opt);
 
 /*
+ * Gradients of ks_matmul, for a layer's backward pass. The pages give the
+ * layer (a KS linear layer usable from PyTorch: KS abstract page,
+ * taxoreview.com "dblp:303/4794", first paragraph, last sentence); its
+ * derivatives are the chain rule on Y = X * W^T. With dY = dL/dY
+ * (batch x a*b*d):
+ *   dX = dY * W     dX[n][alpha][gamma][delta]
+ *                     = sum_beta K[alpha][delta][beta][gamma] dY[n][alpha][beta][delta]
+ *   dK              dK[alpha][delta][beta][gamma]
+ *                     = sum_n dY[n][alpha][beta][delta] X[n][alpha][gamma][delta]
+ *
+ * ks_matmul_dx_workspace_size: bytes of workspace ks_matmul_dx needs (W's
+ *   blocks transposed: nnz elements of W's type, rounded up to 256), to
+ *   *bytes. KS_ERR_NULL if bytes is NULL; pattern and dtype statuses as for
+ *   ks_matmul.
+ * ks_matmul_dx: dX = dY * W.
+ *   W      device K tensor (a, d, b, c) as in ks_matmul.
+ *   dY     device, batch x (a*b*d): fp32 for KS_DTYPE_F32 and KS_DTYPE_BF16W,
+ *          bf16 for KS_DTYPE_BF16; W is bf16 for KS_DTYPE_BF16 and BF16W.
+ *   dX     device fp32, batch x (a*c*d); fully overwritten.
+ *   ws     device workspace, >= ks_matmul_dx_workspace_size bytes, 16-byte
+ *          aligned (KS_ERR_WORKSPACE if NULL or smaller, KS_ERR_ALIGN).
+ *   Runs as the forward product of pattern (a, c, b, d) with every block of
+ *   W transposed (two launches on `stream`). dX must not overlap dY, W or
+ *   ws, nor ws dY or W (KS_ERR_OVERLAP). batch = 0: nothing is launched.
+ */
+ks_status_t ks_matmul_dx_workspace_size(ks_pattern_t p, ks_dtype_t dt, size_t* bytes);
+ks_status_t ks_matmul_dx(ks_pattern_t p, const void* W, const void* dY, void* dX, int64_t batch,
+                         ks_dtype_t dt, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * ks_matmul_dw_workspace_size: bytes of workspace ks_matmul_dw needs for
+ *   this batch (0 if none; partial sums over ranges of rows), to *bytes.
+ * ks_matmul_dw: dK (the gradient with respect to the K tensor).
+ *   dY     device fp32, batch x (a*b*d).
+ *   X      device, batch x (a*c*d): fp32 for KS_DTYPE_F32 and KS_DTYPE_BF16W,
+ *          bf16 for KS_DTYPE_BF16 (the forward input).
+ *   dW     device fp32, shape (a, d, b, c); fully overwritten (zeros when
+ *          batch = 0).
+ *   ws     device workspace of the queried size (may be NULL when 0),
+ *          16-byte aligned.
+ *   Partial sums over row ranges are added in a fixed order, so repeated
+ *   calls give identical bits. dW must not overlap dY, X or ws, nor ws dY
+ *   or X (KS_ERR_OVERLAP).
+ */
+ks_status_t ks_matmul_dw_workspace_size(ks_pattern_t p, int64_t batch, ks_dtype_t dt, size_t* bytes);
+ks_status_t ks_matmul_dw(ks_pattern_t p, const void* dY, const void* X, void* dW, int64_t batch,
+                         ks_dtype_t dt, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * ks_chain_workspace_size: bytes of device workspace ks_chain_matmul needs
  * for these arguments (0 if none), written to *bytes.
  *   p, n   the factors in application order (p[0] is applied to X first).

@@ -236,6 +236,97 @@ ks_status_t ks_matmul(ks_pattern_t p, const void* W, const void* X, void* Y,
     return ks_matmul_ex(p, W, X, Y, batch, dt, stream, nullptr);
 }
 
+ks_status_t ks_matmul_dx_workspace_size(ks_pattern_t p, ks_dtype_t dt, size_t* bytes) {
+    if (!bytes) return KS_ERR_NULL;
+    Shape s;
+    ks_status_t st = shape_of(p, &s);
+    if (st != KS_OK) return st;
+    int xt = 0, wt = 0;
+    st = factor_types(dt, &xt, &wt);
+    if (st != KS_OK) return st;
+    *bytes = (static_cast<size_t>(s.nnz) * ks::elem_bytes(wt) + 255) / 256 * 256;
+    return KS_OK;
+}
+
+ks_status_t ks_matmul_dx(ks_pattern_t p, const void* W, const void* dY, void* dX, int64_t batch,
+                         ks_dtype_t dt, void* ws, size_t ws_bytes, hipStream_t stream) {
+    Shape s;
+    ks_status_t st = shape_of(p, &s);
+    if (st != KS_OK) return st;
+    st = check_batch(batch);
+    if (st != KS_OK) return st;
+    int xt = 0, wt = 0;
+    st = factor_types(dt, &xt, &wt);
+    if (st != KS_OK) return st;
+    if (batch == 0) return KS_OK;
+    if (!W || !dY || !dX) return KS_ERR_NULL;
+    size_t need = 0;
+    ks_matmul_dx_workspace_size(p, dt, &need);
+    if (!ws || ws_bytes < need) return KS_ERR_WORKSPACE;
+    if (!aligned(dY, ks::elem_bytes(xt)) || !aligned(W, ks::elem_bytes(wt)) || !aligned(dX, 4) || !aligned(ws, 16))
+        return KS_ERR_ALIGN;
+    const uint64_t gb = static_cast<uint64_t>(batch) * s.n_out * ks::elem_bytes(xt);
+    const uint64_t xb = static_cast<uint64_t>(batch) * s.n_in * 4u;
+    const uint64_t wb = static_cast<uint64_t>(s.nnz) * ks::elem_bytes(wt);
+    if (overlap(dX, xb, dY, gb) || overlap(dX, xb, W, wb) || overlap(dX, xb, ws, need) ||
+        overlap(ws, need, dY, gb) || overlap(ws, need, W, wb))
+        return KS_ERR_OVERLAP;
+    // dX = dY W: the forward product of pattern (a, c, b, d) whose blocks are
+    // W's blocks transposed
+    st = ks::launch_transpose_blocks(s, wt, W, ws, stream);
+    if (st != KS_OK) return st;
+    Shape st_s;
+    ks_pattern_t pt = {p.a, p.c, p.b, p.d};
+    st = shape_of(pt, &st_s);
+    if (st != KS_OK) return st;
+    ks::FactorCall f;
+    f.s = st_s; f.xt = xt; f.wt = wt; f.W = ws; f.X = dY; f.Y = static_cast<float*>(dX);
+    f.batch = batch; f.stream = stream; f.rows_per_block = 0; f.store_waves = KS_STORE_AUTO;
+    st = current_cus(&f.num_cus);
+    if (st != KS_OK) return st;
+    return run_factor(KS_KERNEL_AUTO, f);
+}
+
+ks_status_t ks_matmul_dw_workspace_size(ks_pattern_t p, int64_t batch, ks_dtype_t dt, size_t* bytes) {
+    if (!bytes) return KS_ERR_NULL;
+    Shape s;
+    ks_status_t st = shape_of(p, &s);
+    if (st != KS_OK) return st;
+    st = check_batch(batch);
+    if (st != KS_OK) return st;
+    int xt = 0, wt = 0;
+    st = factor_types(dt, &xt, &wt);
+    if (st != KS_OK) return st;
+    *bytes = ks::dw_workspace_bytes(s, batch);
+    return KS_OK;
+}
+
+ks_status_t ks_matmul_dw(ks_pattern_t p, const void* dY, const void* X, void* dW, int64_t batch,
+                         ks_dtype_t dt, void* ws, size_t ws_bytes, hipStream_t stream) {
+    Shape s;
+    ks_status_t st = shape_of(p, &s);
+    if (st != KS_OK) return st;
+    st = check_batch(batch);
+    if (st != KS_OK) return st;
+    int xt = 0, wt = 0;
+    st = factor_types(dt, &xt, &wt);
+    if (st != KS_OK) return st;
+    if (!dW) return KS_ERR_NULL;
+    if (batch > 0 && (!dY || !X)) return KS_ERR_NULL;
+    const size_t need = ks::dw_workspace_bytes(s, batch);
+    if (need > 0 && (!ws || ws_bytes < need)) return KS_ERR_WORKSPACE;
+    if (!aligned(dW, 4) || (batch > 0 && (!aligned(dY, 4) || !aligned(X, ks::elem_bytes(xt)))) ||
+        (need > 0 && !aligned(ws, 16)))
+        return KS_ERR_ALIGN;
+    const uint64_t gb = static_cast<uint64_t>(batch) * s.n_out * 4u;
+    const uint64_t xb = static_cast<uint64_t>(batch) * s.n_in * ks::elem_bytes(xt);
+    const uint64_t wb = static_cast<uint64_t>(s.nnz) * 4u;
+    if (overlap(dW, wb, dY, gb) || overlap(dW, wb, X, xb) || overlap(dW, wb, ws, need) ||
+        overlap(ws, need, dY, gb) || overlap(ws, need, X, xb))
+        return KS_ERR_OVERLAP;
+    return ks::launch_dw(s, xt, static_cast<const float*>(dY), X, static_cast<float*>(dW), batch, ws, stream);
+}
+
 ks_status_t ks_chain_workspace_size(const ks_pattern_t* p, int n, int64_t batch,
                                     ks_dtype_t dt, unsigned flags, size_t* bytes) {
     if (!bytes) return KS_ERR_NULL;

@@ -106,6 +106,14 @@ def load(path: str = LIB_PATH):
     lib.ks_chain_plan.restype = i32
     lib.ks_plan_describe.argtypes = [ks_pattern_t, i64, i32, ctypes.c_char_p, ctypes.c_size_t]
     lib.ks_plan_describe.restype = i32
+    lib.ks_matmul_dx_workspace_size.argtypes = [ks_pattern_t, i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.ks_matmul_dx_workspace_size.restype = i32
+    lib.ks_matmul_dx.argtypes = [ks_pattern_t, vp, vp, vp, i64, i32, vp, ctypes.c_size_t, vp]
+    lib.ks_matmul_dx.restype = i32
+    lib.ks_matmul_dw_workspace_size.argtypes = [ks_pattern_t, i64, i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.ks_matmul_dw_workspace_size.restype = i32
+    lib.ks_matmul_dw.argtypes = [ks_pattern_t, vp, vp, vp, i64, i32, vp, ctypes.c_size_t, vp]
+    lib.ks_matmul_dw.restype = i32
     _lib = lib
     return lib
 
@@ -174,6 +182,32 @@ def ks_matmul_ex(p, W, X, Y, batch: int, dtype: int, stream=None, kernel: int = 
     st = load().ks_matmul_ex(_pattern(p), _ptr(W), _ptr(X), _ptr(Y), int(batch), int(dtype),
                              _stream(stream, Y, X, W), ctypes.byref(opt))
     return _raise(st, "ks_matmul_ex", check)
+
+
+def ks_matmul_dx_workspace_size(p, dtype: int, check: bool = True):
+    out = ctypes.c_size_t(0)
+    st = load().ks_matmul_dx_workspace_size(_pattern(p), int(dtype), ctypes.byref(out))
+    _raise(st, "ks_matmul_dx_workspace_size", check)
+    return out.value if check else (st, out.value)
+
+
+def ks_matmul_dx(p, W, dY, dX, batch: int, dtype: int, ws, ws_bytes: int, stream=None, check: bool = True) -> int:
+    st = load().ks_matmul_dx(_pattern(p), _ptr(W), _ptr(dY), _ptr(dX), int(batch), int(dtype), _ptr(ws),
+                             int(ws_bytes), _stream(stream, dX, dY, W))
+    return _raise(st, "ks_matmul_dx", check)
+
+
+def ks_matmul_dw_workspace_size(p, batch: int, dtype: int, check: bool = True):
+    out = ctypes.c_size_t(0)
+    st = load().ks_matmul_dw_workspace_size(_pattern(p), int(batch), int(dtype), ctypes.byref(out))
+    _raise(st, "ks_matmul_dw_workspace_size", check)
+    return out.value if check else (st, out.value)
+
+
+def ks_matmul_dw(p, dY, X, dW, batch: int, dtype: int, ws, ws_bytes: int, stream=None, check: bool = True) -> int:
+    st = load().ks_matmul_dw(_pattern(p), _ptr(dY), _ptr(X), _ptr(dW), int(batch), int(dtype), _ptr(ws),
+                             int(ws_bytes), _stream(stream, dW, dY, X))
+    return _raise(st, "ks_matmul_dw", check)
 
 
 def _patterns(ps: Sequence):
@@ -286,3 +320,42 @@ def chain_matmul(X, Ws, patterns, out=None, fuse=True, stream=None):
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=X.device) if nbytes else None
     ks_chain_matmul(patterns, Ws, X, out, batch, dt, ws, nbytes, flags, stream)
     return out
+
+
+def matmul_dx(dY, W, pattern, out=None, stream=None):
+    """dX = dY W for one KS factor (the gradient of matmul with respect to X)."""
+    import torch
+    a, b, c, d = (int(v) for v in pattern)
+    _check_tensor(dY, "dY")
+    _check_tensor(W, "W")
+    if dY.dim() != 2 or dY.shape[1] != a * b * d:
+        raise ValueError("dY must be (batch, a*b*d) = (*, %d)" % (a * b * d))
+    batch = dY.shape[0]
+    dt = dtype_code(dY.dtype, W.dtype)
+    if out is None:
+        out = torch.empty((batch, a * c * d), dtype=torch.float32, device=dY.device)
+    nbytes = ks_matmul_dx_workspace_size((a, b, c, d), dt)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dY.device)
+    ks_matmul_dx((a, b, c, d), W, dY, out, batch, dt, ws, nbytes, stream)
+    return out
+
+
+def matmul_dw(dY, X, pattern, out=None, stream=None):
+    """dK (shape (a, d, b, c), fp32): the gradient of matmul with respect to W."""
+    import torch
+    a, b, c, d = (int(v) for v in pattern)
+    _check_tensor(dY, "dY")
+    _check_tensor(X, "X")
+    if dY.dtype != torch.float32:
+        raise TypeError("dY must be fp32")
+    if X.dim() != 2 or X.shape[1] != a * c * d or dY.shape != (X.shape[0], a * b * d):
+        raise ValueError("X must be (batch, a*c*d) and dY (batch, a*b*d)")
+    batch = X.shape[0]
+    dt = DTYPE_BF16 if X.dtype == torch.bfloat16 else DTYPE_F32
+    if out is None:
+        out = torch.empty((a, d, b, c), dtype=torch.float32, device=X.device)
+    nbytes = ks_matmul_dw_workspace_size((a, b, c, d), batch, dt)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=X.device) if nbytes else None
+    ks_matmul_dw((a, b, c, d), dY, X, out, batch, dt, ws, nbytes, stream)
+    return out
+

@@ -190,3 +190,51 @@ def test_one_hip_runtime_whatever_the_import_order():
     out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip().splitlines()[-1] == "1"
+
+
+def test_backward_workspace_sizes():
+    p = (4, 64, 16, 6)
+    nnz = 4 * 64 * 16 * 6
+    assert libks.ks_matmul_dx_workspace_size(p, libks.DTYPE_F32) == (nnz * 4 + 255) // 256 * 256
+    assert libks.ks_matmul_dx_workspace_size(p, libks.DTYPE_BF16) == (nnz * 2 + 255) // 256 * 256
+    assert libks.ks_matmul_dw_workspace_size(p, 1, libks.DTYPE_F32) == 0
+    big = libks.ks_matmul_dw_workspace_size(p, 25216, libks.DTYPE_F32)
+    assert big % 256 == 0 and big >= 2 * nnz * 4 and big <= 64 << 20
+    assert libks.ks_matmul_dx_workspace_size((0, 1, 1, 1), 0, check=False)[0] == libks.KS_ERR_PATTERN
+    assert libks.ks_matmul_dw_workspace_size(p, -1, 0, check=False)[0] == libks.KS_ERR_BATCH
+    assert libks.ks_matmul_dw_workspace_size(p, 5, 7, check=False)[0] == libks.KS_ERR_DTYPE
+
+
+def test_backward_argument_errors():
+    p = (2, 4, 8, 2)
+    need = libks.ks_matmul_dx_workspace_size(p, libks.DTYPE_F32)
+    dx = lambda **kw: libks.ks_matmul_dx(kw.get("p", p), kw.get("W", WP), kw.get("dY", XP), kw.get("dX", YP),
+                                         kw.get("batch", 4), kw.get("dt", libks.DTYPE_F32), kw.get("ws", WSP),
+                                         kw.get("wsb", need), stream=0, check=False)
+    assert dx(p=(1, 0, 1, 1)) == libks.KS_ERR_PATTERN
+    assert dx(batch=-2) == libks.KS_ERR_BATCH
+    assert dx(dt=9) == libks.KS_ERR_DTYPE
+    assert dx(batch=0, W=None, dY=None, dX=None, ws=None) == libks.KS_OK
+    assert dx(W=None) == libks.KS_ERR_NULL
+    assert dx(ws=None) == libks.KS_ERR_WORKSPACE
+    assert dx(wsb=need - 1) == libks.KS_ERR_WORKSPACE
+    assert dx(dX=YP + 2) == libks.KS_ERR_ALIGN
+    assert dx(ws=WSP + 4) == libks.KS_ERR_ALIGN
+    assert dx(dX=XP) == libks.KS_ERR_OVERLAP          # dX over dY
+    assert dx(ws=WP) == libks.KS_ERR_OVERLAP          # workspace over W
+    dw = lambda **kw: libks.ks_matmul_dw(kw.get("p", p), kw.get("dY", YP), kw.get("X", XP), kw.get("dW", WP),
+                                         kw.get("batch", 1), kw.get("dt", libks.DTYPE_F32), kw.get("ws", None),
+                                         kw.get("wsb", 0), stream=0, check=False)
+    assert libks.ks_matmul_dw_workspace_size(p, 1, libks.DTYPE_F32) == 0    # one row range: no partial sums
+    assert dw(p=(1, 1, 1, 0)) == libks.KS_ERR_PATTERN
+    assert dw(batch=-1) == libks.KS_ERR_BATCH
+    assert dw(dt=5) == libks.KS_ERR_DTYPE
+    assert dw(dW=None) == libks.KS_ERR_NULL
+    assert dw(X=None) == libks.KS_ERR_NULL
+    assert dw(dW=WP + 1) == libks.KS_ERR_ALIGN
+    assert dw(dW=XP) == libks.KS_ERR_OVERLAP
+    big = (64, 8, 8, 8)
+    need_w = libks.ks_matmul_dw_workspace_size(big, 4096, libks.DTYPE_F32)
+    assert need_w > 0
+    assert dw(p=big, batch=4096, ws=None, wsb=0) == libks.KS_ERR_WORKSPACE
+    assert dw(p=big, batch=4096, ws=WSP, wsb=need_w - 1) == libks.KS_ERR_WORKSPACE

@@ -437,3 +437,110 @@ def test_mfma_store_modes(p, bf16):
     assert outs, "neither store mode ran"
     if len(outs) == 2:
         assert np.array_equal(outs["compute"], outs["dedicated"])
+
+
+# ---------------------------------------------------------------- gradients
+
+BACKWARD_PATTERNS = [(2, 16, 16, 8), (4, 64, 16, 6), (64, 8, 8, 8), (3, 5, 7, 2), (2, 128, 128, 4),
+                     (1, 4, 4, 64), (5, 1, 3, 2)]
+
+
+def _rel(a, b):
+    return float(np.linalg.norm(np.asarray(a, dtype=np.float64) - b) / max(np.linalg.norm(b), 1e-300))
+
+
+@pytest.mark.parametrize("p", BACKWARD_PATTERNS, ids=lambda p: "%d_%d_%d_%d" % p)
+@pytest.mark.parametrize("dt", ["f32", "bf16", "bf16w"])
+def test_backward_dx_dw(p, dt):
+    """dX = dY W and dK against the fp64 oracle on a ragged batch: fp32
+    everything; bf16 X and W (dY bf16 for dX); fp32 inputs with bf16 W."""
+    a, b, c, d = p
+    batch = 333
+    rng = np.random.default_rng(500 + a * 7 + b)
+    X = rng.standard_normal((batch, a * c * d), dtype=np.float32)
+    W = rng.standard_normal((a, d, b, c), dtype=np.float32) / np.float32(np.sqrt(c))
+    dY = rng.standard_normal((batch, a * b * d), dtype=np.float32)
+    xb = dt == "bf16"
+    wb = dt in ("bf16", "bf16w")
+    dXg = libks.matmul_dx(to_dev(dY, xb), to_dev(W, wb), p)
+    dWg = libks.matmul_dw(to_dev(dY, False), to_dev(X, xb), p)
+    torch.cuda.synchronize()
+    ref_dx = oracle.ks_matmul_dx(p, host_values(W, wb), host_values(dY, xb))
+    ref_dw = oracle.ks_matmul_dw(p, host_values(dY, False), host_values(X, xb))
+    assert _rel(dXg.cpu().numpy(), ref_dx) <= FP32_REL_TOL, "dX"
+    assert _rel(dWg.cpu().numpy(), ref_dw) <= FP32_REL_TOL, "dW"
+
+
+def test_backward_edges():
+    """batch 0 gives dK = 0; batch 1 (no partial sums); repeated calls give
+    identical bits (partial sums added in a fixed order)."""
+    p = (4, 64, 16, 6)
+    a, b, c, d = p
+    W = torch.randn((a, d, b, c), device=DEV)
+    dW = libks.matmul_dw(torch.empty((0, a * b * d), device=DEV), torch.empty((0, a * c * d), device=DEV), p)
+    torch.cuda.synchronize()
+    assert not dW.any()
+    rng = np.random.default_rng(7)
+    X = rng.standard_normal((1, a * c * d), dtype=np.float32)
+    dY = rng.standard_normal((1, a * b * d), dtype=np.float32)
+    dW1 = libks.matmul_dw(to_dev(dY), to_dev(X), p).cpu().numpy()
+    assert _rel(dW1, oracle.ks_matmul_dw(p, host_values(dY, False), host_values(X, False))) <= FP32_REL_TOL
+    X = to_dev(rng.standard_normal((3001, a * c * d), dtype=np.float32))
+    dY = to_dev(rng.standard_normal((3001, a * b * d), dtype=np.float32))
+    r1 = libks.matmul_dw(dY, X, p).cpu()
+    r2 = libks.matmul_dw(dY, X, p).cpu()
+    assert torch.equal(r1, r2)
+    dx0 = libks.matmul_dx(torch.empty((0, a * b * d), device=DEV), W, p)
+    assert dx0.shape == (0, a * c * d)
+
+
+def test_backward_vit_full_size():
+    """The ViT factor's gradients at 25,216 rows: dX on sampled rows, dK in
+    full (the oracle sums all rows)."""
+    wl = datagen.get("vit_mlp")
+    p = wl.patterns[0]
+    X, Ws = datagen.draw(wl)
+    rng = np.random.default_rng(8)
+    dY = rng.standard_normal((wl.batch, wl.n_out), dtype=np.float32)
+    dXg = libks.matmul_dx(to_dev(dY), to_dev(Ws[0]), p)
+    dWg = libks.matmul_dw(to_dev(dY), to_dev(X), p)
+    torch.cuda.synchronize()
+    rows = sample_rows(wl.batch)
+    ref_dx = oracle.ks_matmul_dx(p, host_values(Ws[0], False), host_values(dY[rows], False))
+    assert _rel(dXg.index_select(0, torch.from_numpy(rows).to(DEV)).cpu().numpy(), ref_dx) <= FP32_REL_TOL
+    ref_dw = oracle.ks_matmul_dw(p, host_values(dY, False), host_values(X, False))
+    assert _rel(dWg.cpu().numpy(), ref_dw) <= FP32_REL_TOL
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_kslinear_layer_gradients(bf16):
+    """The autograd layer over a 2-factor chain: output and the gradients of
+    L = <G, y> with respect to x and both weights, against the fp64 chain
+    rule built from the oracle's single-factor functions."""
+    from kronecker_sparse_structured_amd import layer
+    pats = [(4, 16, 16, 8), (64, 8, 8, 1)]
+    dtype = torch.bfloat16 if bf16 else torch.float32
+    L = layer.KSLinear(pats, dtype=dtype, device=DEV, seed=3)
+    rng = np.random.default_rng(9)
+    x_np = rng.standard_normal((5, 37, L.n_in), dtype=np.float32)
+    G_np = rng.standard_normal((5, 37, L.n_out), dtype=np.float32)
+    x = to_dev(x_np.reshape(-1, L.n_in), bf16).reshape(5, 37, L.n_in).requires_grad_(True)
+    y = L(x)
+    (y * torch.from_numpy(G_np).to(DEV)).sum().backward()
+    torch.cuda.synchronize()
+    xs = host_values(x_np.reshape(-1, L.n_in), bf16)
+    Ks = [oracle.widen(w.detach().view(torch.int16).cpu().numpy().view(np.uint16), "bf16") if bf16 else
+          oracle.widen(w.detach().cpu().numpy(), "f32") for w in L.weights]
+    z = oracle.ks_matmul(pats[0], Ks[0], xs)
+    y_ref = oracle.ks_matmul(pats[1], Ks[1], z)
+    assert _rel(y.detach().reshape(-1, L.n_out).cpu().numpy(), y_ref) <= FP32_REL_TOL
+    g = G_np.reshape(-1, L.n_out).astype(np.float64)
+    dK1 = oracle.ks_matmul_dw(pats[1], g, z)
+    dz = oracle.ks_matmul_dx(pats[1], Ks[1], g)
+    dK0 = oracle.ks_matmul_dw(pats[0], dz, xs)
+    dx = oracle.ks_matmul_dx(pats[0], Ks[0], dz)
+    tol = 1e-2 if bf16 else FP32_REL_TOL     # bf16 layer: gradients are rounded to bf16 on return
+    assert _rel(L.weights[1].grad.float().cpu().numpy(), dK1) <= tol
+    assert _rel(L.weights[0].grad.float().cpu().numpy(), dK0) <= tol
+    assert _rel(x.grad.float().reshape(-1, L.n_in).cpu().numpy(), dx) <= tol
+
