@@ -71,6 +71,9 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="time every pattern of the square sweep (n = 4096, 16,384 rows) and print "
                          "one line per pattern plus a JSON summary; not the single-line contract run")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the gradients (ks_matmul_dx, ks_matmul_dw) of every factor of the "
+                         "workload and print one JSON line; not the contract run")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of a "
                          "`--calib-copy` run into profiles/traffic_counters.json and exit")
@@ -182,6 +185,8 @@ def main():
         return 2
     if args.sweep:
         return sweep(args)
+    if args.backward:
+        return backward(args)
 
     import numpy as np
     import torch
@@ -398,6 +403,84 @@ def main():
     if per_factor is not None:
         out["per_factor"] = per_factor
     print(json.dumps(out), flush=True)
+    return 0
+
+
+def backward(args) -> int:
+    """Gradients of each factor of the workload on synthetic dY (fp32) and
+    inputs: dX = dY W (the transposing launch plus the forward product of the
+    transposed pattern) and dK, each timed back to back over rotated buffers
+    after warm-up. Bytes as run: dX reads dY and W (twice: transpose, then
+    the product) and writes dX and the transposed W; dK reads dY and X,
+    writes the partial sums and reads them back, and writes dK."""
+    import numpy as np
+    import torch
+    from kronecker_sparse_structured_amd import datagen, libks
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    wl = datagen.get(args.workload)
+    bf16 = args.dtype == "bf16"
+    batch = wl.batch
+    sx = 2 if bf16 else 4
+    stream = torch.cuda.current_stream(dev)
+    rng = np.random.default_rng(11)
+    rows = []
+    for k, p in enumerate(wl.patterns):
+        a, b, c, d = p
+        n_in, n_out, nnz = a * c * d, a * b * d, a * b * c * d
+        # inputs of factor k > 0 are fp32 intermediates in a chain
+        xdt = torch.bfloat16 if (bf16 and k == 0) else torch.float32
+        W = torch.from_numpy(rng.standard_normal((a, d, b, c), dtype=np.float32)).to(dev)
+        if bf16:
+            W = W.to(torch.bfloat16)
+        nset = 2
+        Xs = [torch.randn((batch, n_in), device=dev).to(xdt) for _ in range(nset)]
+        dYs = [torch.randn((batch, n_out), device=dev) for _ in range(nset)]
+        dXs = [torch.empty((batch, n_in), device=dev) for _ in range(nset)]
+        dWs = [torch.empty((a, d, b, c), device=dev) for _ in range(nset)]
+        dt_x = libks.DTYPE_BF16W if bf16 else libks.DTYPE_F32
+        dt_w = libks.DTYPE_BF16 if xdt == torch.bfloat16 else libks.DTYPE_F32
+        wsx_b = libks.ks_matmul_dx_workspace_size(p, dt_x)
+        wsw_b = libks.ks_matmul_dw_workspace_size(p, batch, dt_w)
+        wsx = torch.empty(max(wsx_b, 1), dtype=torch.uint8, device=dev)
+        wsw = torch.empty(max(wsw_b, 1), dtype=torch.uint8, device=dev)
+        run_dx = lambda i: libks.ks_matmul_dx(p, W, dYs[i % nset], dXs[i % nset], batch, dt_x, wsx, wsx_b, stream)
+        run_dw = lambda i: libks.ks_matmul_dw(p, dYs[i % nset], Xs[i % nset], dWs[i % nset], batch, dt_w,
+                                              wsw if wsw_b else None, wsw_b, stream)
+
+        def timed(fn):
+            t0 = time.time()
+            while time.time() - t0 < 0.2:
+                fn(0)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            reps = 20
+            for i in range(reps):
+                fn(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps * 1e-3
+
+        sw = 2 if bf16 else 4
+        t_dx, t_dw = timed(run_dx), timed(run_dw)
+        by_dx = 4 * batch * n_out + 4 * batch * n_in + 3 * sw * nnz
+        by_dw = 4 * batch * n_out + (sx if xdt == torch.bfloat16 else 4) * batch * n_in + 4 * nnz + 2 * wsw_b
+        flops = 2 * batch * nnz
+        fr = lambda by, s: max(by / 8.0e12, flops / 157.3e12) / s
+        rows.append({"pattern": list(p),
+                     "dx_ms": round(t_dx * 1e3, 5), "dx_GB/s": round(by_dx / t_dx / 1e9, 1),
+                     "dx_roofline_frac": round(fr(by_dx, t_dx), 4),
+                     "dx_plan": libks.ks_plan_describe((a, c, b, d), batch, dt_x),
+                     "dw_ms": round(t_dw * 1e3, 5), "dw_GB/s": round(by_dw / t_dw / 1e9, 1),
+                     "dw_roofline_frac": round(fr(by_dw, t_dw), 4), "dw_workspace_bytes": wsw_b})
+    print(json.dumps({"metric": "KS matmul gradients (dX, dK) per factor, % of roofline, 1xMI355X",
+                      "workload": wl.name, "batch": batch, "dtype": args.dtype, "data": "synthetic",
+                      "factors": rows}), flush=True)
     return 0
 
 

@@ -297,7 +297,7 @@ ks_status_t ks_matmul_dw_workspace_size(ks_pattern_t p, int64_t batch, ks_dtype_
     int xt = 0, wt = 0;
     st = factor_types(dt, &xt, &wt);
     if (st != KS_OK) return st;
-    *bytes = ks::dw_workspace_bytes(s, batch);
+    *bytes = ks::dw_workspace_bytes(s, xt, batch);
     return KS_OK;
 }
 
@@ -313,7 +313,7 @@ ks_status_t ks_matmul_dw(ks_pattern_t p, const void* dY, const void* X, void* dW
     if (st != KS_OK) return st;
     if (!dW) return KS_ERR_NULL;
     if (batch > 0 && (!dY || !X)) return KS_ERR_NULL;
-    const size_t need = ks::dw_workspace_bytes(s, batch);
+    const size_t need = ks::dw_workspace_bytes(s, xt, batch);
     if (need > 0 && (!ws || ws_bytes < need)) return KS_ERR_WORKSPACE;
     if (!aligned(dW, 4) || (batch > 0 && (!aligned(dY, 4) || !aligned(X, ks::elem_bytes(xt)))) ||
         (need > 0 && !aligned(ws, 16)))

@@ -8,15 +8,18 @@
 //        the caller's workspace) and the forward kernels do the rest.
 //   dK[alpha][delta][beta][gamma] = sum_n dY[n][alpha][beta][delta]
 //                                         * X[n][alpha][gamma][delta]
-//        (each K entry sits in W once). The generic kernel here gives every
-//        thread one K entry and one range of rows; per-range partial sums go
-//        to the workspace and a second kernel adds them in range order, so
-//        the result does not depend on scheduling.
+//        (each K entry sits in W once). Blocks with b and c multiples of 16
+//        run on the matrix cores (below); any other pattern on a generic
+//        kernel that gives every thread one K entry. Both write partial sums
+//        per range of rows to the workspace, which a second kernel adds in
+//        range order, so the result does not depend on scheduling.
 
 #include <algorithm>
+#include <cstdio>
 
 #include "ks_device.h"
 #include "ks_internal.h"
+#include "ks_stream.h"
 
 namespace ks {
 namespace {
@@ -78,6 +81,242 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__
 
 unsigned grid_for(int64_t n) { return static_cast<unsigned>((n + kThreads - 1) / kThreads); }
 
+
+// ---------------------------------------------------------------------------
+// dK on the matrix cores, for blocks with b and c multiples of 16.
+//
+// For a fixed (alpha, delta), dK[alpha][delta] (b x c) = dY_blk^T X_blk summed
+// over rows: M = beta, N = gamma, K = rows, four rows per
+// v_mfma_f32_16x16x4_f32. A workgroup owns a tile -- one alpha, dt deltas
+// (all d, or segments of dt), bt of the b outputs -- and a range of rows; one
+// loader wave streams both the tile's part of X and of dY, 16 rows a stage,
+// into an LDS ring (ks_stream.h); four compute waves keep the tile's
+// dt * (bt / 16) * (c / 16) accumulator tiles (at most 64) in registers over
+// all the rows, then write them as the range's partial sums. Rows past the
+// batch in the last stage contribute zero (both operands are masked).
+
+typedef float floatx4_dw __attribute__((ext_vector_type(4)));
+
+constexpr int kDwRows = 16;          // rows per stage
+constexpr int kDwMaxInsts = 40;      // loader instructions per stage, each of X and dY
+constexpr int kDwTilesPerWave = 16;  // accumulator tiles per compute wave (64 VGPRs)
+
+struct DwArgs {
+    int a, b, c, d;
+    int64_t n_in, n_out, batch;
+    int bt, dt;                  // outputs and deltas per tile
+    int tiles_beta, tiles_delta, n_tiles;
+    int ntiles_acc;              // dt * (bt / 16) * (c / 16)
+    int rows_per_split;          // multiple of kDwRows
+    int contiguous;              // 1: dt == d (whole alpha slabs of X and of dY's beta range)
+    int insts_x, insts_y, stages;
+    StageMap xmap, ymap;
+    int64_t out_stride;          // elements between the partial sums of consecutive splits (0: one split)
+};
+
+template <typename TX>
+__global__ __launch_bounds__(kStreamThreads) void dw_mfma_kernel(const float* __restrict__ dY, const TX* __restrict__ X,
+                                                                  float* __restrict__ out, DwArgs args) {
+    constexpr int EB = int(sizeof(TX));
+    constexpr int VWX = 16 / EB;
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int stage_bytes = (args.insts_x + args.insts_y) * 1024;
+    const int t = threadIdx.x;
+    const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int tile = blk % args.n_tiles;
+    const int split = blk / args.n_tiles;
+    const int tb = tile % args.tiles_beta;          // beta splits of one (alpha, delta range) are neighbours
+    const int rest = tile / args.tiles_beta;
+    const int td = rest % args.tiles_delta;
+    const int alpha = rest / args.tiles_delta;
+    const int beta0 = tb * args.bt;
+    const int delta0 = td * args.dt;
+    const int d = args.d;
+    const bool contig = args.contiguous != 0;
+    // the tile's part of a row: X[alpha][gamma][delta0 ..], dY[alpha][beta0 ..][delta0 ..]
+    const int64_t xg0 = int64_t(alpha) * args.c * d + (contig ? 0 : delta0);
+    const int64_t yg0 = (int64_t(alpha) * args.b + beta0) * d + (contig ? 0 : delta0);
+
+    const int64_t row_begin = int64_t(split) * args.rows_per_split;
+    if (row_begin >= args.batch) return;
+    const int64_t row_end = min(args.batch, row_begin + int64_t(args.rows_per_split));
+    const int nsteps = static_cast<int>((row_end - row_begin + kDwRows - 1) / kDwRows);
+    const int S = args.stages;
+
+    if (t >= kConsumerThreads) {
+        // ------------------------------------------------------ loader wave
+        LoaderPlan<kDwMaxInsts> lx, ly;
+        const int lane = t - kConsumerThreads;
+        make_loader_plan<kDwMaxInsts>(args.xmap, args.insts_x, VWX, EB, args.n_in, args.xmap.blocks,
+                                      args.xmap.blk_vec, lane, &lx);
+        make_loader_plan<kDwMaxInsts>(args.ymap, args.insts_y, 4, 4, args.n_out, args.ymap.blocks,
+                                      args.ymap.blk_vec, lane, &ly);
+        auto issue = [&](int s) {
+            const int64_t n0 = row_begin + int64_t(s) * kDwRows;
+            unsigned char* st = lds + (s % S) * stage_bytes;
+            issue_stage<kDwMaxInsts>(lx, args.insts_x, X + n0 * args.n_in + xg0,
+                                     stage_limit(n0, row_end, args.n_in, EB), st);
+            issue_stage<kDwMaxInsts>(ly, args.insts_y, dY + n0 * args.n_out + yg0,
+                                     stage_limit(n0, row_end, args.n_out, 4), st + args.insts_x * 1024);
+        };
+        for (int s = 0; s < S - 1 && s < nsteps; ++s) issue(s);
+        for (int s = 0; s < nsteps; ++s) {
+            wait_vmcnt_upto(min(S - 2, nsteps - 1 - s) * (args.insts_x + args.insts_y));
+            lds_barrier();                                   // stage s ready
+            if (s + S - 1 < nsteps) issue(s + S - 1);
+            lds_barrier();                                   // stage s consumed
+        }
+        return;
+    }
+
+    // ---------------------------------------------------------- consumers
+    // v_mfma_f32_16x16x4_f32: lane l supplies A[l % 16][l / 16] and
+    // B[l / 16][l % 16] and receives D[4 (l / 16) + i][l % 16] in register i.
+    // A = dY^T (M = beta, K = row), B = X (K = row, N = gamma).
+    const int w = t >> 6;
+    const int lane = t & 63;
+    const int mn = lane & 15;
+    const int kk = lane >> 4;
+    const int MT = args.bt / 16, NT = args.c / 16;
+    const int xs = contig ? d : args.dt;                     // element stride of gamma in an X stage row
+    const int ys = contig ? d : args.dt;                     // element stride of beta in a dY stage row
+    const int xrow = args.xmap.row_vec * 16, yrow = args.ymap.row_vec * 16;
+    int aoff[kDwTilesPerWave], boff[kDwTilesPerWave];       // byte offsets within a stage row
+    bool tv[kDwTilesPerWave];
+#pragma unroll
+    for (int j = 0; j < kDwTilesPerWave; ++j) {
+        const int ti = w + 4 * j;
+        tv[j] = ti < args.ntiles_acc;
+        const int dl = ti / (MT * NT);
+        const int mt = (ti / NT) % MT;
+        const int nt = ti % NT;
+        aoff[j] = ((16 * mt + mn) * ys + dl) * 4;
+        boff[j] = ((16 * nt + mn) * xs + dl) * EB;
+    }
+    floatx4_dw acc[kDwTilesPerWave];
+#pragma unroll
+    for (int j = 0; j < kDwTilesPerWave; ++j) acc[j] = floatx4_dw{0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (int s = 0; s < nsteps; ++s) {
+        lds_barrier();                                                   // stage s ready
+        const unsigned char* xst = lds + (s % S) * stage_bytes;
+        const unsigned char* yst = xst + args.insts_x * 1024;
+        const int rows = static_cast<int>(min(int64_t(kDwRows), row_end - row_begin - int64_t(s) * kDwRows));
+#pragma unroll
+        for (int ks = 0; ks < kDwRows / 4; ++ks) {
+            const int r = 4 * ks + kk;
+            const bool rv = r < rows;
+            const unsigned char* yr = yst + r * yrow;
+            const unsigned char* xr = xst + r * xrow;
+#pragma unroll
+            for (int j = 0; j < kDwTilesPerWave; ++j) {
+                if (!tv[j]) continue;
+                const float av = rv ? *reinterpret_cast<const float*>(yr + aoff[j]) : 0.0f;
+                const float bv = rv ? to_f32(*reinterpret_cast<const TX*>(xr + boff[j])) : 0.0f;
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[j], 0, 0, 0);
+            }
+        }
+        lds_barrier();                                                   // stage s consumed
+    }
+    // partial sums of this row range: dK[alpha][delta][beta][gamma]
+    float* o = out + int64_t(split) * args.out_stride;
+#pragma unroll
+    for (int j = 0; j < kDwTilesPerWave; ++j) {
+        if (!tv[j]) continue;
+        const int ti = w + 4 * j;
+        const int dl = ti / (MT * NT);
+        const int mt = (ti / NT) % MT;
+        const int nt = ti % NT;
+        const int gamma = 16 * nt + mn;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int beta = beta0 + 16 * mt + 4 * kk + i;
+            o[((int64_t(alpha) * d + delta0 + dl) * args.b + beta) * args.c + gamma] = acc[j][i];
+        }
+    }
+}
+
+
+// Tile of the matrix-core dK kernel for pattern s and X element size eb.
+struct DwGeom {
+    int bt, dt, contiguous, tiles_beta, tiles_delta, n_tiles, ntiles_acc, insts_x, insts_y, stages;
+    StageMap xmap, ymap;
+    size_t lds;
+};
+
+// Odd number of 16-byte vectors per row: 16 rows start in distinct bank groups.
+int odd_pitch(int vec) { return vec % 2 ? vec : vec + 1; }
+
+bool dw_geom(const Shape& s, int xt, DwGeom* g) {
+    const int b = s.b, c = s.c, d = s.d;
+    if (b % 16 != 0 || c % 16 != 0) return false;
+    const int eb = elem_bytes(xt), vwx = 16 / eb;
+    const int nt = c / 16;
+    auto finish = [&](int bt, int dt, bool contig) {
+        g->bt = bt;
+        g->dt = dt;
+        g->contiguous = contig ? 1 : 0;
+        g->tiles_beta = b / bt;
+        g->tiles_delta = contig ? 1 : d / dt;
+        const int64_t ntl = int64_t(s.a) * g->tiles_delta * g->tiles_beta;
+        if (ntl > (int64_t(1) << 30)) return false;
+        g->n_tiles = static_cast<int>(ntl);
+        g->ntiles_acc = dt * (bt / 16) * nt;
+        StageMap& xm = g->xmap;
+        StageMap& ym = g->ymap;
+        xm.rows = ym.rows = kDwRows;
+        xm.pad_vec = ym.pad_vec = 0;
+        if (contig) {
+            xm.blocks = 1; xm.blk_vec = c * d / vwx; xm.gstride = 0;
+            ym.blocks = 1; ym.blk_vec = bt * d / 4; ym.gstride = 0;
+        } else {
+            xm.blocks = c; xm.blk_vec = dt / vwx; xm.gstride = d;
+            ym.blocks = bt; ym.blk_vec = dt / 4; ym.gstride = d;
+        }
+        xm.row_vec = odd_pitch(xm.blocks * xm.blk_vec);
+        ym.row_vec = odd_pitch(ym.blocks * ym.blk_vec);
+        g->insts_x = (kDwRows * xm.row_vec + 63) / 64;
+        g->insts_y = (kDwRows * ym.row_vec + 63) / 64;
+        const int insts = g->insts_x + g->insts_y;
+        if (g->insts_x > kDwMaxInsts || g->insts_y > kDwMaxInsts || insts > 63) return false;
+        // the loader addresses a stage with 32-bit byte offsets
+        if (int64_t(kDwRows) * std::max(s.n_in * eb, s.n_out * 4) >= (int64_t(1) << 31)) return false;
+        int st = std::max(3, std::min(8, (150 * 1024) / (insts * 1024)));
+        while (st > 3 && (st - 2) * insts > 63) --st;
+        g->stages = st;
+        g->lds = size_t(st) * insts * 1024;
+        return g->lds <= 160 * 1024;
+    };
+    // whole alpha slabs when the accumulators of every delta fit
+    for (int bt = b; bt >= 16; bt /= 2) {
+        if (b % bt != 0 || bt % 16 != 0) continue;
+        if (d * (bt / 16) * nt <= 4 * kDwTilesPerWave && (c * d * eb) % 16 == 0 && (bt * d * 4) % 16 == 0 &&
+            finish(bt, d, true))
+            return true;
+    }
+    // else segments of dt deltas (16-byte runs at least), longest first
+    const int dtmin = std::max(4, vwx);
+    for (int dt = 64; dt >= dtmin; dt /= 2) {
+        if (d % dt != 0) continue;
+        for (int bt = b; bt >= 16; bt /= 2) {
+            if (b % bt != 0 || bt % 16 != 0) continue;
+            if (dt * (bt / 16) * nt <= 4 * kDwTilesPerWave && finish(bt, dt, false)) return true;
+        }
+    }
+    return false;
+}
+
+// Row ranges: about 512 workgroups (a fixed target, so that the workspace
+// size is known without asking the device), at most 256 ranges, partial
+// sums within 64 MB.
+int dw_ranges(const Shape& s, int64_t batch, int64_t tiles, int rows_step) {
+    const int64_t steps = (batch + rows_step - 1) / rows_step;
+    int64_t r = std::max<int64_t>(1, 512 / std::max<int64_t>(tiles, 1));
+    r = std::min<int64_t>(r, std::min<int64_t>(steps, 256));
+    r = std::min<int64_t>(r, std::max<int64_t>(1, (int64_t(64) << 20) / (s.nnz * 4)));
+    return static_cast<int>(std::max<int64_t>(1, r));
+}
+
 }  // namespace
 
 ks_status_t launch_transpose_blocks(const Shape& s, int wt, const void* W, void* Wt, hipStream_t stream) {
@@ -89,40 +328,91 @@ ks_status_t launch_transpose_blocks(const Shape& s, int wt, const void* W, void*
                          static_cast<const bf16_t*>(W), static_cast<bf16_t*>(Wt), s.b, s.c, s.nnz);
 }
 
-int dw_splits(const Shape& s, int64_t batch) {
-    if (batch <= 1) return 1;
-    // about 2048 workgroups, at most 256 ranges of rows, and partial sums
-    // within 64 MB of workspace
-    const int64_t groups = (s.nnz + kThreads - 1) / kThreads;
-    int64_t splits = std::max<int64_t>(1, (2048 + groups - 1) / groups);
-    splits = std::min<int64_t>(splits, std::min<int64_t>(batch, 256));
-    splits = std::min<int64_t>(splits, std::max<int64_t>(1, (int64_t(64) << 20) / (s.nnz * 4)));
-    return static_cast<int>(splits);
+// Plan of one dK call: the kernel family and its ranges of rows.
+struct DwPlan {
+    bool mfma;
+    DwGeom g;
+    int ranges;
+    int64_t rows_per_range;
+};
+
+DwPlan dw_plan(const Shape& s, int xt, int64_t batch) {
+    DwPlan pl;
+    pl.mfma = dw_geom(s, xt, &pl.g);
+    if (batch <= 1) {
+        pl.ranges = 1;
+    } else if (pl.mfma) {
+        pl.ranges = dw_ranges(s, batch, pl.g.n_tiles, kDwRows);
+    } else {
+        // generic: about 2048 workgroups of one K entry per thread
+        const int64_t groups = (s.nnz + kThreads - 1) / kThreads;
+        pl.ranges = dw_ranges(s, batch, std::max<int64_t>(1, groups / 4), 1);
+    }
+    const int step = pl.mfma ? kDwRows : 1;
+    const int64_t steps = (batch + step - 1) / step;
+    pl.rows_per_range = std::max<int64_t>(1, (steps + pl.ranges - 1) / pl.ranges) * step;
+    if (batch > 0) pl.ranges = static_cast<int>((batch + pl.rows_per_range - 1) / pl.rows_per_range);
+    return pl;
 }
 
-size_t dw_workspace_bytes(const Shape& s, int64_t batch) {
-    const int splits = dw_splits(s, batch);
-    return splits <= 1 ? 0 : (static_cast<size_t>(splits) * s.nnz * 4 + 255) / 256 * 256;
+size_t dw_workspace_bytes(const Shape& s, int xt, int64_t batch) {
+    const DwPlan pl = dw_plan(s, xt, batch);
+    return pl.ranges <= 1 ? 0 : (static_cast<size_t>(pl.ranges) * s.nnz * 4 + 255) / 256 * 256;
 }
 
 ks_status_t launch_dw(const Shape& s, int xt, const float* dY, const void* X, float* dK, int64_t batch, void* ws,
                       hipStream_t stream) {
     if (batch == 0)
         return launch_kernel(fill_zero_kernel, dim3(grid_for(s.nnz)), dim3(kThreads), 0, stream, dK, s.nnz);
-    const int splits = dw_splits(s, batch);
-    const int64_t rps = (batch + splits - 1) / splits;
-    float* out = splits > 1 ? static_cast<float*>(ws) : dK;
-    const dim3 grid(grid_for(s.nnz), static_cast<unsigned>(splits));
+    const DwPlan pl = dw_plan(s, xt, batch);
+    float* out = pl.ranges > 1 ? static_cast<float*>(ws) : dK;
     ks_status_t st;
-    if (xt == kF32)
-        st = launch_kernel(dw_generic_kernel<float>, grid, dim3(kThreads), 0, stream, dY, static_cast<const float*>(X),
-                           out, s.a, s.b, s.c, s.d, batch, rps, s.nnz);
-    else
-        st = launch_kernel(dw_generic_kernel<bf16_t>, grid, dim3(kThreads), 0, stream, dY,
-                           static_cast<const bf16_t*>(X), out, s.a, s.b, s.c, s.d, batch, rps, s.nnz);
-    if (st != KS_OK || splits == 1) return st;
+    if (pl.mfma) {
+        DwArgs args;
+        args.a = s.a; args.b = s.b; args.c = s.c; args.d = s.d;
+        args.n_in = s.n_in; args.n_out = s.n_out; args.batch = batch;
+        args.bt = pl.g.bt; args.dt = pl.g.dt;
+        args.tiles_beta = pl.g.tiles_beta; args.tiles_delta = pl.g.tiles_delta; args.n_tiles = pl.g.n_tiles;
+        args.ntiles_acc = pl.g.ntiles_acc;
+        args.rows_per_split = static_cast<int>(pl.rows_per_range);
+        args.contiguous = pl.g.contiguous;
+        args.insts_x = pl.g.insts_x; args.insts_y = pl.g.insts_y; args.stages = pl.g.stages;
+        args.xmap = pl.g.xmap; args.ymap = pl.g.ymap;
+        args.out_stride = pl.ranges > 1 ? s.nnz : 0;
+        const int64_t blocks = int64_t(pl.g.n_tiles) * pl.ranges;
+        if (blocks > 0x7fffffff) return KS_ERR_UNSUPPORTED;
+        if (xt == kF32)
+            st = launch_kernel(dw_mfma_kernel<float>, dim3(static_cast<unsigned>(blocks)), dim3(kStreamThreads),
+                               pl.g.lds, stream, dY, static_cast<const float*>(X), out, args);
+        else
+            st = launch_kernel(dw_mfma_kernel<bf16_t>, dim3(static_cast<unsigned>(blocks)), dim3(kStreamThreads),
+                               pl.g.lds, stream, dY, static_cast<const bf16_t*>(X), out, args);
+    } else {
+        const dim3 grid(grid_for(s.nnz), static_cast<unsigned>(pl.ranges));
+        if (xt == kF32)
+            st = launch_kernel(dw_generic_kernel<float>, grid, dim3(kThreads), 0, stream, dY,
+                               static_cast<const float*>(X), out, s.a, s.b, s.c, s.d, batch, pl.rows_per_range, s.nnz);
+        else
+            st = launch_kernel(dw_generic_kernel<bf16_t>, grid, dim3(kThreads), 0, stream, dY,
+                               static_cast<const bf16_t*>(X), out, s.a, s.b, s.c, s.d, batch, pl.rows_per_range,
+                               s.nnz);
+    }
+    if (st != KS_OK || pl.ranges == 1) return st;
     return launch_kernel(dw_reduce_kernel, dim3(grid_for(s.nnz)), dim3(kThreads), 0, stream,
-                         static_cast<const float*>(ws), dK, splits, s.nnz);
+                         static_cast<const float*>(ws), dK, pl.ranges, s.nnz);
+}
+
+int dw_describe(const Shape& s, int xt, int64_t batch, char* buf, size_t len) {
+    const DwPlan pl = dw_plan(s, xt, batch);
+    if (!pl.mfma)
+        return std::snprintf(buf, len, "dw generic: one K entry per thread, ranges=%d", pl.ranges);
+    return std::snprintf(buf, len,
+                         "dw mfma 16x16x4f32: deltas/tile=%d (%s) outputs/tile=%d of %d acc tiles=%d ranges=%d "
+                         "rows/range=%lld wgs=%lld stages=%d x %d KB",
+                         pl.g.dt, pl.g.contiguous ? "contiguous" : "segmented", pl.g.bt, s.b, pl.g.ntiles_acc,
+                         pl.ranges, static_cast<long long>(pl.rows_per_range),
+                         static_cast<long long>(int64_t(pl.g.n_tiles) * pl.ranges), pl.g.stages,
+                         pl.g.insts_x + pl.g.insts_y);
 }
 
 }  // namespace ks

@@ -95,7 +95,8 @@ ks_status_t launch_slab_pair(const Shape& s0, const Shape& s1, int xt, int wt0, 
 // type); dK partial sums over row ranges in the workspace, then added in
 // order (dw_workspace_bytes: 0 when one range covers the batch).
 ks_status_t launch_transpose_blocks(const Shape& s, int wt, const void* W, void* Wt, hipStream_t stream);
-size_t dw_workspace_bytes(const Shape& s, int64_t batch);
+size_t dw_workspace_bytes(const Shape& s, int xt, int64_t batch);
+int dw_describe(const Shape& s, int xt, int64_t batch, char* buf, size_t len);
 ks_status_t launch_dw(const Shape& s, int xt, const float* dY, const void* X, float* dK, int64_t batch, void* ws,
                       hipStream_t stream);
 
