@@ -64,6 +64,48 @@ __global__ __launch_bounds__(kThreads) void dw_generic_kernel(const float* __res
     out[int64_t(blockIdx.y) * nnz + e] = acc;
 }
 
+// Small blocks (b, c in {2, 4, 8, 16}, not both 16): one (alpha, delta)
+// block per thread with its b x c sums in registers, rows
+// [split * rows_per_split, ...). Per row a thread loads the block's b
+// values of dY and c values of X once (lanes run over delta, then alpha, so
+// the loads of a wave are runs of consecutive elements), so the kernel
+// reads each element of dY and X once per row range.
+template <typename TX, int B, int C>
+__global__ __launch_bounds__(kThreads) void dw_small_kernel(const float* __restrict__ dY, const TX* __restrict__ X,
+                                                            float* __restrict__ out, int a, int d, int64_t batch,
+                                                            int64_t rows_per_split, int64_t nnz) {
+    const int64_t blk = int64_t(blockIdx.x) * kThreads + threadIdx.x;   // alpha * d + delta
+    if (blk >= int64_t(a) * d) return;
+    const int alpha = static_cast<int>(blk / d);
+    const int delta = static_cast<int>(blk - int64_t(alpha) * d);
+    const int64_t n_in = int64_t(a) * C * d, n_out = int64_t(a) * B * d;
+    const int64_t n0 = int64_t(blockIdx.y) * rows_per_split;
+    const int64_t n1 = min(batch, n0 + rows_per_split);
+    const float* gy = dY + int64_t(alpha) * B * d + delta;      // + beta * d
+    const TX* gx = X + int64_t(alpha) * C * d + delta;          // + gamma * d
+    float acc[B][C];
+#pragma unroll
+    for (int i = 0; i < B; ++i)
+#pragma unroll
+        for (int j = 0; j < C; ++j) acc[i][j] = 0.0f;
+    for (int64_t n = n0; n < n1; ++n) {
+        float yv[B], xv[C];
+#pragma unroll
+        for (int i = 0; i < B; ++i) yv[i] = gy[n * n_out + i * d];
+#pragma unroll
+        for (int j = 0; j < C; ++j) xv[j] = to_f32(gx[n * n_in + j * d]);
+#pragma unroll
+        for (int i = 0; i < B; ++i)
+#pragma unroll
+            for (int j = 0; j < C; ++j) acc[i][j] = fmaf(yv[i], xv[j], acc[i][j]);
+    }
+    float* o = out + int64_t(blockIdx.y) * nnz + blk * (B * C);   // dK[alpha][delta][beta][gamma]
+#pragma unroll
+    for (int i = 0; i < B; ++i)
+#pragma unroll
+        for (int j = 0; j < C; ++j) o[i * C + j] = acc[i][j];
+}
+
 // dK[e] = sum over splits s (ascending) of part[s * nnz + e].
 __global__ __launch_bounds__(kThreads) void dw_reduce_kernel(const float* __restrict__ part, float* __restrict__ dK,
                                                              int nsplit, int64_t nnz) {
@@ -329,8 +371,51 @@ ks_status_t launch_transpose_blocks(const Shape& s, int wt, const void* W, void*
 }
 
 // Plan of one dK call: the kernel family and its ranges of rows.
+bool small_size(int v) { return v == 2 || v == 4 || v == 8 || v == 16; }
+
+template <typename TX, int B, int C>
+ks_status_t launch_small_bc(const Shape& s, const float* dY, const void* X, float* out, int64_t batch, int64_t rps,
+                            int ranges, hipStream_t stream) {
+    const dim3 grid(grid_for(int64_t(s.a) * s.d), static_cast<unsigned>(ranges));
+    return launch_kernel(dw_small_kernel<TX, B, C>, grid, dim3(kThreads), 0, stream, dY, static_cast<const TX*>(X), out,
+                         s.a, s.d, batch, rps, s.nnz);
+}
+
+template <typename TX, int B>
+ks_status_t launch_small_b(const Shape& s, const float* dY, const void* X, float* out, int64_t batch, int64_t rps,
+                           int ranges, hipStream_t stream) {
+    switch (s.c) {
+        case 2: return launch_small_bc<TX, B, 2>(s, dY, X, out, batch, rps, ranges, stream);
+        case 4: return launch_small_bc<TX, B, 4>(s, dY, X, out, batch, rps, ranges, stream);
+        case 8: return launch_small_bc<TX, B, 8>(s, dY, X, out, batch, rps, ranges, stream);
+        case 16:
+            if constexpr (B <= 8) return launch_small_bc<TX, B, 16>(s, dY, X, out, batch, rps, ranges, stream);
+            break;
+    }
+    return KS_ERR_UNSUPPORTED;
+}
+
+template <typename TX>
+ks_status_t launch_small_t(const Shape& s, const float* dY, const void* X, float* out, int64_t batch, int64_t rps,
+                           int ranges, hipStream_t stream) {
+    switch (s.b) {
+        case 2: return launch_small_b<TX, 2>(s, dY, X, out, batch, rps, ranges, stream);
+        case 4: return launch_small_b<TX, 4>(s, dY, X, out, batch, rps, ranges, stream);
+        case 8: return launch_small_b<TX, 8>(s, dY, X, out, batch, rps, ranges, stream);
+        case 16: return launch_small_b<TX, 16>(s, dY, X, out, batch, rps, ranges, stream);
+    }
+    return KS_ERR_UNSUPPORTED;
+}
+
+ks_status_t launch_small(const Shape& s, int xt, const float* dY, const void* X, float* out, int64_t batch,
+                         int64_t rps, int ranges, hipStream_t stream) {
+    if (xt == kF32) return launch_small_t<float>(s, dY, X, out, batch, rps, ranges, stream);
+    return launch_small_t<bf16_t>(s, dY, X, out, batch, rps, ranges, stream);
+}
+
 struct DwPlan {
     bool mfma;
+    bool small;      // dw_small_kernel
     DwGeom g;
     int ranges;
     int64_t rows_per_range;
@@ -339,10 +424,15 @@ struct DwPlan {
 DwPlan dw_plan(const Shape& s, int xt, int64_t batch) {
     DwPlan pl;
     pl.mfma = dw_geom(s, xt, &pl.g);
+    pl.small = !pl.mfma && small_size(s.b) && small_size(s.c) && s.b * s.c <= 128;
     if (batch <= 1) {
         pl.ranges = 1;
     } else if (pl.mfma) {
         pl.ranges = dw_ranges(s, batch, pl.g.n_tiles, kDwRows);
+    } else if (pl.small) {
+        // about 64 K threads (one per block and row range)
+        const int64_t blocks = int64_t(s.a) * s.d;
+        pl.ranges = dw_ranges(s, batch, std::max<int64_t>(1, blocks * 512 / 65536), 1);
     } else {
         // generic: about 2048 workgroups of one K entry per thread
         const int64_t groups = (s.nnz + kThreads - 1) / kThreads;
@@ -387,6 +477,8 @@ ks_status_t launch_dw(const Shape& s, int xt, const float* dY, const void* X, fl
         else
             st = launch_kernel(dw_mfma_kernel<bf16_t>, dim3(static_cast<unsigned>(blocks)), dim3(kStreamThreads),
                                pl.g.lds, stream, dY, static_cast<const bf16_t*>(X), out, args);
+    } else if (pl.small) {
+        st = launch_small(s, xt, dY, X, out, batch, pl.rows_per_range, pl.ranges, stream);
     } else {
         const dim3 grid(grid_for(s.nnz), static_cast<unsigned>(pl.ranges));
         if (xt == kF32)
@@ -404,6 +496,8 @@ ks_status_t launch_dw(const Shape& s, int xt, const float* dY, const void* X, fl
 
 int dw_describe(const Shape& s, int xt, int64_t batch, char* buf, size_t len) {
     const DwPlan pl = dw_plan(s, xt, batch);
+    if (pl.small)
+        return std::snprintf(buf, len, "dw small: one block per thread, ranges=%d", pl.ranges);
     if (!pl.mfma)
         return std::snprintf(buf, len, "dw generic: one K entry per thread, ranges=%d", pl.ranges);
     return std::snprintf(buf, len,
