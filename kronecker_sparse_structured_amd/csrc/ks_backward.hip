@@ -351,9 +351,9 @@ bool dw_geom(const Shape& s, int xt, DwGeom* g) {
 // Row ranges: about 512 workgroups (a fixed target, so that the workspace
 // size is known without asking the device), at most 256 ranges, partial
 // sums within 64 MB.
-int dw_ranges(const Shape& s, int64_t batch, int64_t tiles, int rows_step) {
+int dw_ranges(const Shape& s, int64_t batch, int64_t tiles, int rows_step, int64_t target = 512) {
     const int64_t steps = (batch + rows_step - 1) / rows_step;
-    int64_t r = std::max<int64_t>(1, 512 / std::max<int64_t>(tiles, 1));
+    int64_t r = std::max<int64_t>(1, target / std::max<int64_t>(tiles, 1));
     r = std::min<int64_t>(r, std::min<int64_t>(steps, 256));
     r = std::min<int64_t>(r, std::max<int64_t>(1, (int64_t(64) << 20) / (s.nnz * 4)));
     return static_cast<int>(std::max<int64_t>(1, r));
@@ -428,7 +428,10 @@ DwPlan dw_plan(const Shape& s, int xt, int64_t batch) {
     if (batch <= 1) {
         pl.ranges = 1;
     } else if (pl.mfma) {
-        pl.ranges = dw_ranges(s, batch, pl.g.n_tiles, kDwRows);
+        // one resident round of workgroups on a 256-unit device (a fixed
+        // count keeps the workspace size device-independent)
+        const int64_t per_cu = std::max<size_t>(1, std::min<size_t>(2, (160 * 1024) / pl.g.lds));
+        pl.ranges = dw_ranges(s, batch, pl.g.n_tiles, kDwRows, 256 * per_cu);
     } else if (pl.small) {
         // about 64 K threads (one per block and row range)
         const int64_t blocks = int64_t(s.a) * s.d;
