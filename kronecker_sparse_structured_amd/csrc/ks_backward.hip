@@ -106,14 +106,23 @@ __global__ __launch_bounds__(kThreads) void dw_small_kernel(const float* __restr
         for (int j = 0; j < C; ++j) o[i * C + j] = acc[i][j];
 }
 
-// dK[e] = sum over splits s (ascending) of part[s * nnz + e].
+// dK[e] = sum of part[s * nnz + e] over the splits s: a workgroup takes 64
+// entries, each with four threads that add a quarter of the splits in
+// ascending order; the quarters are then added in order (0 + 1) + (2 + 3),
+// so the result does not depend on scheduling.
 __global__ __launch_bounds__(kThreads) void dw_reduce_kernel(const float* __restrict__ part, float* __restrict__ dK,
                                                              int nsplit, int64_t nnz) {
-    const int64_t e = int64_t(blockIdx.x) * kThreads + threadIdx.x;
-    if (e >= nnz) return;
+    __shared__ float q[4][64];
+    const int lane = threadIdx.x & 63, qi = threadIdx.x >> 6;
+    const int64_t e = int64_t(blockIdx.x) * 64 + lane;
+    const int per = (nsplit + 3) / 4;
+    const int s0 = qi * per, s1 = min(nsplit, s0 + per);
     float acc = 0.0f;
-    for (int s = 0; s < nsplit; ++s) acc += part[int64_t(s) * nnz + e];
-    dK[e] = acc;
+    if (e < nnz)
+        for (int s = s0; s < s1; ++s) acc += part[int64_t(s) * nnz + e];
+    q[qi][lane] = acc;
+    __syncthreads();
+    if (qi == 0 && e < nnz) dK[e] = (q[0][lane] + q[1][lane]) + (q[2][lane] + q[3][lane]);
 }
 
 __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
@@ -493,7 +502,7 @@ ks_status_t launch_dw(const Shape& s, int xt, const float* dY, const void* X, fl
                                s.nnz);
     }
     if (st != KS_OK || pl.ranges == 1) return st;
-    return launch_kernel(dw_reduce_kernel, dim3(grid_for(s.nnz)), dim3(kThreads), 0, stream,
+    return launch_kernel(dw_reduce_kernel, dim3(static_cast<unsigned>((s.nnz + 63) / 64)), dim3(kThreads), 0, stream,
                          static_cast<const float*>(ws), dK, pl.ranges, s.nnz);
 }
 
