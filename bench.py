@@ -76,6 +76,9 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="time every pattern of the square sweep (n = 4096, 16,384 rows) and print "
                          "one line per pattern plus a JSON summary; not the single-line contract run")
+    ap.add_argument("--comparator", action="store_true",
+                    help="with --sweep (fp32): also time the permute / batched GEMM / permute formulation "
+                         "(torch permute copies and torch.bmm) on the same inputs and report the speedup")
     ap.add_argument("--backward", action="store_true",
                     help="time the gradients (ks_matmul_dx, ks_matmul_dw) of every factor of the "
                          "workload and print one JSON line; not the contract run")
@@ -564,17 +567,59 @@ def sweep(args) -> int:
                "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / peak_flops, 4),
                "roofline_frac": round(t_roof / (ms * 1e-3), 4),
                "plan": libks.ks_plan_describe(p, batch, dt)}
+        if args.comparator and not bf16:
+            row.update(comparator(p, batch, Xt, Wt, Yt, nset, ms, stream, torch))
         rows.append(row)
         print("%-18s %9.1f us %8.1f GB/s %7.2f TFLOP/s  %s  roofline %.3f   %s" % (
-            str(tuple(p)), ms * 1e3, row["GB/s"], row["TFLOP/s"], bound, row["roofline_frac"], row["plan"][:60]),
-            flush=True)
+            str(tuple(p)), ms * 1e3, row["GB/s"], row["TFLOP/s"], bound, row["roofline_frac"],
+            ("permute-bmm %.1f us, x%.2f  " % (row["comparator_ms"] * 1e3, row["speedup"])
+             if "speedup" in row else "") + row["plan"][:60]), flush=True)
         del Xt, Yt, Wt, X, Ws
     fr = [r["roofline_frac"] for r in rows]
-    print(json.dumps({"sweep": "square n=4096, 16384 rows", "dtype": args.dtype, "patterns": len(rows),
+    extra = {}
+    sp_all = [r["speedup"] for r in rows if "speedup" in r]
+    if sp_all:
+        extra = {"speedup_vs_permute_bmm_median": round(float(np.median(sp_all)), 3),
+                 "speedup_min": round(float(np.min(sp_all)), 3), "speedup_max": round(float(np.max(sp_all)), 3),
+                 "faster_than_permute_bmm": int(sum(s > 1.0 for s in sp_all))}
+    print(json.dumps({"sweep": "square n=4096, 16384 rows", "dtype": args.dtype, "patterns": len(rows), **extra,
                       "roofline_frac_median": round(float(np.median(fr)), 4),
                       "roofline_frac_min": round(float(np.min(fr)), 4),
                       "roofline_frac_max": round(float(np.max(fr)), 4), "rows": rows}), flush=True)
     return 0
+
+
+def comparator(p, batch, Xt, Wt, Yt, nset, ms_ours, stream, torch):
+    """The formulation the KS abstract page (first paragraph) ascribes to
+    existing kernels: permute X so that each (alpha, delta) block's rows are
+    contiguous, one batched GEMM over the a*d blocks (torch.bmm, i.e. the
+    vendor BLAS), permute the result back into Y's layout. Weights are
+    rearranged once, outside the timed region. Returns its time per call,
+    the speedup of the fused kernel over it, and the largest relative
+    difference between the two outputs on one input set."""
+    a, b, c, d = p
+    Kt = Wt.view(a * d, b, c).transpose(1, 2).contiguous()        # (a*d, c, b)
+    ref = Yt[0].clone()
+
+    def run(k):
+        Xp = Xt[k].view(batch, a, c, d).permute(1, 3, 0, 2).contiguous().view(a * d, batch, c)
+        Z = torch.bmm(Xp, Kt)                                        # (a*d, batch, b)
+        Yt[k].view(batch, a, b, d).copy_(Z.view(a, d, batch, b).permute(2, 0, 3, 1))
+
+    warm_up(lambda i: run(i % nset), 3, torch)
+    run(0)
+    torch.cuda.synchronize()
+    diff = float((Yt[0] - ref).abs().max() / ref.abs().max().clamp_min(1e-30))
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    steps = 10
+    e0.record(stream)
+    for i in range(steps):
+        run(i % nset)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"comparator_ms": round(ms, 5), "speedup": round(ms / ms_ours, 3), "comparator_max_rel_diff": diff}
 
 
 def cpu_baseline(wl, bf16, target_s):
