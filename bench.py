@@ -79,6 +79,9 @@ def parse():
     ap.add_argument("--comparator", action="store_true",
                     help="with --sweep (fp32): also time the permute / batched GEMM / permute formulation "
                          "(torch permute copies and torch.bmm) on the same inputs and report the speedup")
+    ap.add_argument("--energy", action="store_true",
+                    help="GPU energy per call (amdsmi energy counter over ~2 s loops) of the fused kernel and "
+                         "of the permute / batched GEMM / permute comparator, fp32; one JSON line")
     ap.add_argument("--backward", action="store_true",
                     help="time the gradients (ks_matmul_dx, ks_matmul_dw) of every factor of the "
                          "workload and print one JSON line; not the contract run")
@@ -195,6 +198,8 @@ def main():
         return sweep(args)
     if args.backward:
         return backward(args)
+    if args.energy:
+        return energy(args)
 
     import numpy as np
     import torch
@@ -589,6 +594,72 @@ def sweep(args) -> int:
     return 0
 
 
+def comparator_fn(p, batch, Xt, Wt, Yt, torch):
+    """run(k): Y[k] from X[k] by permute / torch.bmm / permute (see comparator)."""
+    a, b, c, d = p
+    Kt = Wt.view(a * d, b, c).transpose(1, 2).contiguous()        # (a*d, c, b)
+
+    def run(k):
+        Xp = Xt[k].view(batch, a, c, d).permute(1, 3, 0, 2).contiguous().view(a * d, batch, c)
+        Z = torch.bmm(Xp, Kt)                                        # (a*d, batch, b)
+        Yt[k].view(batch, a, b, d).copy_(Z.view(a, d, batch, b).permute(2, 0, 3, 1))
+
+    return run
+
+
+def energy(args) -> int:
+    """Energy per call from the device's energy accumulator (amdsmi, counter
+    x its resolution), read around ~2 s of back-to-back calls after warm-up,
+    for the fused kernel and the comparator on the same inputs; fp32. The
+    average power over the loop is reported too. Context only: the counter
+    covers the whole device (idle draw included)."""
+    import numpy as np
+    import torch
+    from kronecker_sparse_structured_amd import datagen, libks
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception as exc:                       # no energy counter on this machine
+        print(json.dumps({"metric": "energy", "error": str(exc)}), flush=True)
+        return 1
+
+    def joules():
+        e = amdsmi.amdsmi_get_energy_count(handle)
+        return e["energy_accumulator"] * e["counter_resolution"] * 1e-6
+
+    dev = torch.device("cuda:0")
+    rows = []
+    for name in ["vit_mlp", "square_16_16_16_16", "square_32_128_128_1"]:
+        wl = datagen.get(name)
+        p = wl.patterns[0]
+        X, Ws = datagen.draw(wl)
+        nset = 2
+        Xt = [torch.from_numpy(X).to(dev) for _ in range(nset)]
+        Wt = torch.from_numpy(Ws[0]).to(dev)
+        Yt = [torch.empty((wl.batch, wl.n_out), device=dev) for _ in range(nset)]
+        fused = lambda k: libks.ks_matmul(p, Wt, Xt[k], Yt[k], wl.batch, libks.DTYPE_F32)
+        comp = comparator_fn(p, wl.batch, Xt, Wt, Yt, torch)
+        row = {"workload": name, "pattern": list(p)}
+        for label, fn in (("fused", fused), ("permute_bmm", comp)):
+            warm_up(lambda i: fn(i % nset), 5, torch)
+            j0, t0, n = joules(), time.perf_counter(), 0
+            while time.perf_counter() - t0 < 2.0:
+                for _ in range(10):
+                    fn(n % nset)
+                    n += 1
+                torch.cuda.synchronize()
+            j1, t1 = joules(), time.perf_counter()
+            row[label] = {"calls": n, "mJ_per_call": round((j1 - j0) / n * 1e3, 4),
+                          "avg_W": round((j1 - j0) / (t1 - t0), 1), "us_per_call": round((t1 - t0) / n * 1e6, 2)}
+        row["energy_ratio"] = round(row["permute_bmm"]["mJ_per_call"] / max(row["fused"]["mJ_per_call"], 1e-12), 3)
+        rows.append(row)
+        del Xt, Yt, Wt
+    print(json.dumps({"metric": "GPU energy per call (amdsmi energy accumulator), fused vs permute/bmm/permute",
+                      "dtype": "f32", "data": "synthetic", "rows": rows}), flush=True)
+    return 0
+
+
 def comparator(p, batch, Xt, Wt, Yt, nset, ms_ours, stream, torch):
     """The formulation the KS abstract page (first paragraph) ascribes to
     existing kernels: permute X so that each (alpha, delta) block's rows are
@@ -597,14 +668,8 @@ def comparator(p, batch, Xt, Wt, Yt, nset, ms_ours, stream, torch):
     rearranged once, outside the timed region. Returns its time per call,
     the speedup of the fused kernel over it, and the largest relative
     difference between the two outputs on one input set."""
-    a, b, c, d = p
-    Kt = Wt.view(a * d, b, c).transpose(1, 2).contiguous()        # (a*d, c, b)
     ref = Yt[0].clone()
-
-    def run(k):
-        Xp = Xt[k].view(batch, a, c, d).permute(1, 3, 0, 2).contiguous().view(a * d, batch, c)
-        Z = torch.bmm(Xp, Kt)                                        # (a*d, batch, b)
-        Yt[k].view(batch, a, b, d).copy_(Z.view(a, d, batch, b).permute(2, 0, 3, 1))
+    run = comparator_fn(p, batch, Xt, Wt, Yt, torch)
 
     warm_up(lambda i: run(i % nset), 3, torch)
     run(0)
