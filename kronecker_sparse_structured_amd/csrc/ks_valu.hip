@@ -391,6 +391,13 @@ int64_t rows_per_split(const ValuGeom& gm, int64_t batch, int num_cus, int rows_
         const int64_t resident = int64_t(std::max(num_cus, 1)) * per_cu;
         const int64_t splits = std::max<int64_t>(1, resident / std::max(gm.n_tiles, 1));
         steps = (steps_total + splits - 1) / splits;
+        // Stages of three rows (16 alpha slabs of 4 KB or 64 of 1 KB per
+        // row): two rounds of half-size workgroups ran faster than one round
+        // (measured with forced rows per workgroup: (64, 8, 8, 8) 132 -> 109
+        // us, (256, 4, 4, 4) 132 -> 107 us at 16,384 rows, 43 steps per
+        // workgroup); with a dozen steps per workgroup (4,096 rows) and for
+        // other stage shapes it did not gain or lost.
+        if (R == 3 && steps >= 32) steps = (steps + 1) / 2;
     }
     steps = std::max<int64_t>(1, std::min(steps, steps_total));
     return steps * R;
