@@ -506,6 +506,8 @@ def chain_plan_text(patterns, batch, dt, flags, bf16) -> str:
         if len(grp) == 2:
             parts.append("fused pair %s -> %s (one launch, intermediate in LDS)"
                          % (tuple(patterns[grp[0]]), tuple(patterns[grp[1]])))
+        elif len(grp) > 2:
+            parts.append("fused run of factors %d..%d (one launch, rows resident in LDS)" % (grp[0], grp[-1]))
         else:
             k = grp[0]
             fdt = libks.DTYPE_F32 if not bf16 else (libks.DTYPE_BF16 if k == 0 else libks.DTYPE_BF16W)

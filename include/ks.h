@@ -218,14 +218,19 @@ ks_status_t ks_chain_workspace_size(const ks_pattern_t* p, int n, int64_t batch,
  *          may be NULL when that size is 0. 16-byte aligned. Must not
  *          overlap X, Y or any W.
  *   flags  KS_CHAIN_AUTO: consecutive factors whose joint tile fits on chip
- *          run as one fused launch with the intermediate kept in LDS. Two
- *          pair families are fused, scanning the chain from factor 0:
- *          (1, b0, 16, 64) -> (b0, 8, 8, 8) with b0 % 8 == 0 (a group of
- *          beta0 needs whole rows of X and yields a slab of Y's row), and
- *          (a, 16, 16, 16) -> (16a, 16, 16, 1) (the second factor works
- *          inside the first one's per-alpha output slabs; the last two
- *          factors of the 16-ary butterfly). KS_CHAIN_NO_FUSE: one launch
- *          per factor. Results of the two modes agree to rounding.
+ *          run as one fused launch with the intermediates kept in LDS.
+ *          Scanning the chain from factor 0, at each factor the planner
+ *          takes the first that applies of: the pair (1, b0, 16, 64) ->
+ *          (b0, 8, 8, 8) with b0 % 8 == 0 (a group of beta0 needs whole
+ *          rows of X and yields a slab of Y's row); the pair (a, 16, 16, 16)
+ *          -> (16a, 16, 16, 1) (the second factor works inside the first
+ *          one's per-alpha output slabs; the last two factors of the 16-ary
+ *          butterfly); the longest run of at least two factors with blocks
+ *          of b, c <= 16 (b * c <= 128), at most 64 KB of weights each and
+ *          rows of at most 4096 elements, applied to whole rows held in LDS
+ *          (radix-2/4 butterflies, Walsh-Hadamard products); else the factor
+ *          alone. KS_CHAIN_NO_FUSE: one launch per factor. Results of the
+ *          two modes agree to rounding.
  * All launches go to `stream` in order; there is no host synchronisation.
  */
 ks_status_t ks_chain_matmul(const ks_pattern_t* p, int n, const void* const* W,
@@ -236,7 +241,7 @@ ks_status_t ks_chain_matmul(const ks_pattern_t* p, int n, const void* const* W,
 /*
  * ks_chain_plan: the launch groups ks_chain_matmul uses for these arguments.
  * Writes the number of groups to *groups and, for each group in order, the
- * number of consecutive factors it runs (1, or 2 for a fused pair) to
+ * number of consecutive factors it runs (1, or more for a fused group) to
  * group_len[0 .. min(*groups, cap) - 1]. Pure host code; no HIP call. Same
  * validation statuses as ks_chain_workspace_size; KS_ERR_NULL if groups is
  * NULL (group_len may be NULL when cap is 0).

@@ -118,8 +118,9 @@ ks_status_t run_factor(int kernel, const ks::FactorCall& f) {
 struct ChainPlan {
     std::vector<Shape> shapes;
     std::vector<int> group_start;  // first factor of each launch group
-    std::vector<int> group_len;    // 1 (single factor) or 2 (fused pair)
-    std::vector<int> group_kind;   // 0 single factor, 1 row-fused pair, 2 slab-fused pair
+    std::vector<int> group_len;    // factors in the group (one launch)
+    std::vector<int> group_kind;   // 0 single factor, 1 row-fused pair, 2 slab-fused pair,
+                                   // 3 run of factors with rows resident in LDS
     int xt0 = ks::kF32, wt = ks::kF32;
     int64_t max_mid = 0;           // widest intermediate between groups
     int nbuf = 0;                  // workspace buffers (0, 1 or 2)
@@ -152,6 +153,15 @@ ks_status_t plan_chain(const ks_pattern_t* p, int n, int64_t batch, ks_dtype_t d
             } else if (ks::slab_pair_supports(plan->shapes[k], plan->shapes[k + 1], xt, plan->wt, plan->wt)) {
                 len = 2;
                 kind = 2;
+            } else {
+                // the longest run from k whose rows fit on chip
+                for (int m = n - k; m >= 2; --m) {
+                    if (ks::row_chain_supports(&plan->shapes[k], m, xt, plan->wt)) {
+                        len = m;
+                        kind = 3;
+                        break;
+                    }
+                }
             }
         }
         plan->group_start.push_back(k);
@@ -394,6 +404,9 @@ ks_status_t ks_chain_matmul(const ks_pattern_t* p, int n, const void* const* W,
         } else if (plan.group_kind[g] == 2) {
             st = ks::launch_slab_pair(plan.shapes[k], plan.shapes[k + 1], cur_t, plan.wt, plan.wt,
                                       W[k], W[k + 1], cur, out, batch, stream, cus);
+        } else if (plan.group_kind[g] == 3) {
+            st = ks::launch_row_chain(&plan.shapes[k], plan.group_len[g], cur_t, plan.wt, W + k, cur, out, batch,
+                                      stream);
         } else {
             ks::FactorCall f;
             f.s = plan.shapes[k]; f.xt = cur_t; f.wt = plan.wt; f.W = W[k]; f.X = cur; f.Y = out;

@@ -91,6 +91,12 @@ ks_status_t launch_slab_pair(const Shape& s0, const Shape& s1, int xt, int wt0, 
                              const void* W0, const void* W1, const void* X, float* Y,
                              int64_t batch, hipStream_t stream, int num_cus);
 
+// A run of factors with whole rows resident in LDS (ks_rowchain.hip): n >= 2
+// factors of small blocks whose widest row fits on chip. s, W: n entries.
+bool row_chain_supports(const Shape* s, int n, int xt, int wt);
+ks_status_t launch_row_chain(const Shape* s, int n, int xt, int wt, const void* const* W, const void* X, float* Y,
+                             int64_t batch, hipStream_t stream);
+int row_chain_describe(const Shape* s, int n, char* buf, size_t len);
 // Gradients (ks_backward.hip). Blocks of W transposed into Wt (same element
 // type); dK partial sums over row ranges in the workspace, then added in
 // order (dw_workspace_bytes: 0 when one range covers the batch).

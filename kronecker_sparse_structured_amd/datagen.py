@@ -114,6 +114,16 @@ def workloads() -> dict:
     w["butterfly65536"] = Workload("butterfly65536", [(16 ** k, 16, 16, 16 ** (3 - k)) for k in range(4)],
                                    4096, [0.25] * 4, 5,
                                    note="four butterfly factors at n = 65,536")
+    # deep chains of small blocks (one row-resident launch when fused)
+    w["radix2_n1024"] = Workload("radix2_n1024", [(2 ** k, 2, 2, 2 ** (9 - k)) for k in range(10)], 16384,
+                                 [1.0 / np.sqrt(2.0)] * 10, 6,
+                                 note="radix-2 butterfly, ten factors at n = 1024")
+    w["radix4_n4096"] = Workload("radix4_n4096", [(4 ** k, 4, 4, 4 ** (5 - k)) for k in range(6)], 16384,
+                                 [0.5] * 6, 7,
+                                 note="radix-4 butterfly, six factors at n = 4096")
+    w["radix8_n4096"] = Workload("radix8_n4096", [(8 ** k, 8, 8, 8 ** (3 - k)) for k in range(4)], 16384,
+                                 [1.0 / np.sqrt(8.0)] * 4, 8,
+                                 note="radix-8 butterfly, four factors at n = 4096")
     for p_idx, p in enumerate(square_sweep_patterns()):
         name = "square_%d_%d_%d_%d" % p
         w[name] = Workload(name, [p], 16384, [1.0 / np.sqrt(p[2])], 3000 + p_idx,

@@ -160,8 +160,24 @@ def test_chain_plan():
     three = [(1, 6, 2, 3), (3, 2, 3, 2), (2, 2, 3, 2)]
     assert libks.ks_chain_plan(three, 10, libks.DTYPE_F32, libks.CHAIN_NO_FUSE) == [1, 1, 1]
     assert libks.ks_chain_groups(three, 10, libks.DTYPE_F32, libks.CHAIN_NO_FUSE) == [[0], [1], [2]]
-    groups = libks.ks_chain_groups(three, 10, libks.DTYPE_F32, libks.CHAIN_AUTO)
-    assert sum(len(g) for g in groups) == 3 and all(len(g) in (1, 2) for g in groups)
+    # small blocks, rows of at most 4096: the whole chain is one row-resident launch
+    assert libks.ks_chain_groups(three, 10, libks.DTYPE_F32, libks.CHAIN_AUTO) == [[0, 1, 2]]
+
+
+def test_chain_plan_row_resident_runs():
+    """Runs of small-block factors whose rows fit on chip become one launch;
+    a factor with large blocks, weights over 64 KB or rows over 4096
+    elements ends the run."""
+    radix2 = [(2 ** k, 2, 2, 2 ** (11 - k)) for k in range(12)]       # n = 4096
+    assert libks.ks_chain_groups(radix2, 100, libks.DTYPE_F32) == [list(range(12))]
+    assert libks.ks_chain_groups(radix2, 100, libks.DTYPE_F32, libks.CHAIN_NO_FUSE) == [[k] for k in range(12)]
+    wide = [(2 ** k, 2, 2, 2 ** (12 - k)) for k in range(13)]          # n = 8192
+    assert libks.ks_chain_groups(wide, 100, libks.DTYPE_F32) == [[k] for k in range(13)]
+    mixed = [(64, 4, 4, 4), (1, 64, 16, 64), (256, 4, 4, 4), (256, 4, 4, 4)]
+    assert libks.ks_chain_groups(mixed, 100, libks.DTYPE_F32) == [[0], [1], [2, 3]]
+    big_w = [(1, 16, 8, 256), (16, 2, 2, 128)]                          # 128 KB of fp32 weights
+    assert libks.ks_chain_groups(big_w, 100, libks.DTYPE_F32) == [[0], [1]]
+    assert libks.ks_chain_groups(big_w, 100, libks.DTYPE_BF16) == [[0, 1]]
 
 
 def test_chain_plan_fuses_known_pairs():

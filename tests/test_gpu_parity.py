@@ -332,6 +332,64 @@ def test_slab_pair_shapes(a, lead, bf16):
     chain_check(wl.patterns, X, Ws, Y.cpu().numpy(), bf16)
 
 
+def _radix(r, L):
+    """Factors (r^k, r, r, r^(L-1-k)), k = 0..L-1: a radix-r butterfly on n = r^L."""
+    return [(r ** k, r, r, r ** (L - 1 - k)) for k in range(L)]
+
+
+# chains the planner runs as one row-resident launch: (patterns, rows)
+ROW_CHAINS = {
+    "radix2_n1024": (_radix(2, 10), 1000),
+    "radix2_n4096": (_radix(2, 12), 5),
+    "radix4_n4096": (_radix(4, 6), 37),
+    "radix8_n512": (_radix(8, 3), 203),
+    "blocks8_n256": ([(8, 8, 8, 4), (4, 8, 8, 8)], 77),
+    "odd_c3": ([(1, 6, 2, 3), (3, 2, 3, 2), (2, 2, 3, 2)], 203),
+}
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("name", sorted(ROW_CHAINS))
+def test_row_chain(name, bf16):
+    """A whole chain of small blocks in one launch, rows resident in LDS
+    (widths up to 4096, ragged row counts, c = 3 on the general path); the
+    same chain one launch per factor agrees with it and with the oracle."""
+    pats, batch = ROW_CHAINS[name]
+    wl = datagen.Workload("rowchain", pats, batch, [1.0 / np.sqrt(p[2]) for p in pats], 90 + len(pats))
+    dt = libks.DTYPE_BF16 if bf16 else libks.DTYPE_F32
+    assert libks.ks_chain_groups(pats, batch, dt) == [list(range(len(pats)))]
+    X, Ws = datagen.draw(wl)
+    Xt, Wts = to_dev(X, bf16), [to_dev(W, bf16) for W in Ws]
+    Y = libks.chain_matmul(Xt, Wts, pats)
+    Yu = libks.chain_matmul(Xt, Wts, pats, fuse=False)
+    torch.cuda.synchronize()
+    chain_check(pats, X, Ws, Y.cpu().numpy(), bf16)
+    chain_check(pats, X, Ws, Yu.cpu().numpy(), bf16)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_row_chain_unaligned_rows(bf16):
+    """X and Y at 4-byte (not 16-byte) offsets: the element-wise load and
+    store paths of the row-resident chain."""
+    pats, batch = _radix(2, 8), 99
+    wl = datagen.Workload("rowchain", pats, batch, [1.0 / np.sqrt(2.0)] * len(pats), 17)
+    X, Ws = datagen.draw(wl)
+    Xd = to_dev(X, bf16)
+    xbuf = torch.empty(Xd.numel() + 8, dtype=Xd.dtype, device=Xd.device)
+    Xo = xbuf[1:1 + Xd.numel()].view(Xd.shape)
+    Xo.copy_(Xd)
+    ybuf = torch.empty(batch * 256 + 8, dtype=torch.float32, device=Xd.device)
+    Yo = ybuf[1:1 + batch * 256].view(batch, 256)
+    libks.chain_matmul(Xo, [to_dev(W, bf16) for W in Ws], pats, out=Yo)
+    torch.cuda.synchronize()
+    chain_check(pats, X, Ws, Yo.cpu().numpy(), bf16)
+
+
+def test_hadamard_chain_is_one_launch():
+    wl = datagen.get("hadamard16")
+    assert libks.ks_chain_groups(wl.patterns, wl.batch, libks.DTYPE_F32) == [[0, 1, 2, 3]]
+
+
 def test_gpt2_factors_single():
     wl = datagen.get("gpt2_mlp")
     wl = datagen.scaled(wl, 257)
