@@ -89,7 +89,6 @@ __device__ __forceinline__ void apply_block(const float* src, float* dst, int pi
             for (int gm = 0; gm < C; ++gm) w[be][gm] = to_f32(kp[be * C + gm]);
         const float* s = src + alpha * C * d + delta;
         float* o = dst + alpha * B * d + delta;
-#pragma unroll 4
         for (int r = m.r0; r < nr; r += m.rstep) {
             float x[C];
 #pragma unroll
