@@ -226,9 +226,9 @@ ks_status_t ks_chain_workspace_size(const ks_pattern_t* p, int n, int64_t batch,
  *          -> (16a, 16, 16, 1) (the second factor works inside the first
  *          one's per-alpha output slabs; the last two factors of the 16-ary
  *          butterfly); the longest run of at least two factors with blocks
- *          of b, c <= 16 (b * c <= 128), at most 64 KB of weights each and
- *          rows of at most 4096 elements, applied to whole rows held in LDS
- *          (radix-2/4 butterflies, Walsh-Hadamard products); else the factor
+ *          of b * c <= 16, at most 64 KB of weights each and rows of at most
+ *          4096 elements, applied to whole rows held in LDS (radix-2 and
+ *          radix-4 butterflies, Walsh-Hadamard products); else the factor
  *          alone. KS_CHAIN_NO_FUSE: one launch per factor. Results of the
  *          two modes agree to rounding.
  * All launches go to `stream` in order; there is no host synchronisation.

@@ -38,7 +38,7 @@ constexpr int kMaxFactors = 16;              // factors per launch
 constexpr int kMaxWidth = 4096;              // widest row of the run (elements)
 constexpr int kLdsTarget = 32 * 1024;        // LDS of the two row buffers (rows of 4096: 2 rows)
 constexpr int64_t kMaxWeightBytes = 64 * 1024;
-constexpr int kMaxBlock = 128;              // b * c held in registers
+constexpr int kMaxBlock = 16;               // b * c held in registers
 
 struct RowChainArgs {
     int nf;                  // factors in the run
@@ -127,8 +127,8 @@ __device__ __forceinline__ void apply_any(const float* src, float* dst, int pitc
 }
 
 // B x C blocks up to MAXBC weights take the register path (a kernel's VGPR
-// count follows its largest block, so runs of small blocks get a kernel of
-// their own with more waves per SIMD).
+// count follows its largest block: MAXBC = 16 keeps it near 54 VGPRs, eight
+// waves per SIMD).
 template <int MAXBC, int B, int C, typename TW>
 __device__ __forceinline__ bool try_block(const float* src, float* dst, int pitch, int nr, int a, int d,
                                           const TW* __restrict__ K) {
@@ -172,7 +172,9 @@ __global__ __launch_bounds__(kThreads) void row_chain_kernel(const TX* __restric
                                                              RowChainArgs args) {
     extern __shared__ __align__(16) float zbuf[];
     const int pitch = args.pitch;
-    float* buf[2] = {zbuf, zbuf + args.rows * pitch};
+    // buffers as offsets from the LDS array itself (a pointer picked from an
+    // array of pointers would lose its address space: generic accesses)
+    const int bufsz = args.rows * pitch;
     const int64_t n0 = int64_t(blockIdx.x) * args.rows;
     const int nr = static_cast<int>(min(int64_t(args.rows), args.batch - n0));
     const int t = threadIdx.x;
@@ -185,12 +187,12 @@ __global__ __launch_bounds__(kThreads) void row_chain_kernel(const TX* __restric
             const int r = i / q, j = i - r * q;
             float v[4];
             load4_f32(xs + int64_t(r) * args.n_in + 4 * j, v);
-            *reinterpret_cast<floatx4_t*>(buf[0] + r * pitch + 4 * j) = floatx4_t{v[0], v[1], v[2], v[3]};
+            *reinterpret_cast<floatx4_t*>(zbuf + r * pitch + 4 * j) = floatx4_t{v[0], v[1], v[2], v[3]};
         }
     } else {
         for (int i = t; i < nr * args.n_in; i += kThreads) {
             const int r = i / args.n_in, j = i - r * args.n_in;
-            buf[0][r * pitch + j] = to_f32(xs[int64_t(r) * args.n_in + j]);
+            zbuf[r * pitch + j] = to_f32(xs[int64_t(r) * args.n_in + j]);
         }
     }
     __syncthreads();
@@ -198,14 +200,14 @@ __global__ __launch_bounds__(kThreads) void row_chain_kernel(const TX* __restric
     for (int f = 0; f < args.nf; ++f) {
         const int a = args.pat[f][0], b = args.pat[f][1], c = args.pat[f][2], d = args.pat[f][3];
         const TW* K = static_cast<const TW*>(args.w[f]);
-        const float* src = buf[f & 1];
-        float* dst = buf[(f + 1) & 1];
+        const float* src = zbuf + (f & 1) * bufsz;
+        float* dst = zbuf + ((f + 1) & 1) * bufsz;
         apply_factor<MAXBC>(src, dst, pitch, nr, a, b, c, d, K);
         __syncthreads();
     }
 
     // the last buffer to Y
-    const float* z = buf[args.nf & 1];
+    const float* z = zbuf + (args.nf & 1) * bufsz;
     float* ys = Y + n0 * args.n_out;
     if (args.vec_y) {
         const int q = args.n_out / 4;
@@ -241,8 +243,9 @@ bool row_chain_supports(const Shape* s, int n, int xt, int wt) {
     if (n < 2 || n > kMaxFactors) return false;
     int64_t w = s[0].n_in;
     for (int k = 0; k < n; ++k) {
-        // small blocks only: larger ones belong on the matrix cores
-        if (s[k].b > 16 || s[k].c > 16 || s[k].b * s[k].c > kMaxBlock) return false;
+        // small blocks only: with b * c = 64 the run measured no faster than one
+        // launch per factor, with 128 2.4 times slower (VALU work and VGPRs)
+        if (s[k].b * s[k].c > kMaxBlock) return false;
         if (s[k].nnz * elem_bytes(wt) > kMaxWeightBytes) return false;
         w = std::max<int64_t>(w, s[k].n_out);
     }
@@ -253,7 +256,7 @@ template <typename TX, typename TW>
 ks_status_t launch_rc(int maxbc, dim3 grid, size_t lds, hipStream_t stream, const void* X, float* Y,
                       const RowChainArgs& args) {
     const TX* x = static_cast<const TX*>(X);
-    if (maxbc <= 16) return launch_kernel(row_chain_kernel<TX, TW, 16>, grid, dim3(kThreads), lds, stream, x, Y, args);
+    if (maxbc > kMaxBlock) return KS_ERR_UNSUPPORTED;
     return launch_kernel(row_chain_kernel<TX, TW, kMaxBlock>, grid, dim3(kThreads), lds, stream, x, Y, args);
 }
 

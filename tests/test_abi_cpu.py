@@ -165,8 +165,8 @@ def test_chain_plan():
 
 
 def test_chain_plan_row_resident_runs():
-    """Runs of small-block factors whose rows fit on chip become one launch;
-    a factor with large blocks, weights over 64 KB or rows over 4096
+    """Runs of small-block factors (b * c <= 16) whose rows fit on chip
+    become one launch; a factor with larger blocks or rows over 4096
     elements ends the run."""
     radix2 = [(2 ** k, 2, 2, 2 ** (11 - k)) for k in range(12)]       # n = 4096
     assert libks.ks_chain_groups(radix2, 100, libks.DTYPE_F32) == [list(range(12))]
@@ -175,9 +175,10 @@ def test_chain_plan_row_resident_runs():
     assert libks.ks_chain_groups(wide, 100, libks.DTYPE_F32) == [[k] for k in range(13)]
     mixed = [(64, 4, 4, 4), (1, 64, 16, 64), (256, 4, 4, 4), (256, 4, 4, 4)]
     assert libks.ks_chain_groups(mixed, 100, libks.DTYPE_F32) == [[0], [1], [2, 3]]
-    big_w = [(1, 16, 8, 256), (16, 2, 2, 128)]                          # 128 KB of fp32 weights
-    assert libks.ks_chain_groups(big_w, 100, libks.DTYPE_F32) == [[0], [1]]
-    assert libks.ks_chain_groups(big_w, 100, libks.DTYPE_BF16) == [[0, 1]]
+    big_blocks = [(1, 16, 8, 256), (16, 2, 2, 128), (32, 2, 2, 64)]    # 16 x 8 blocks first
+    for dt in (libks.DTYPE_F32, libks.DTYPE_BF16):
+        assert libks.ks_chain_groups(big_blocks, 100, dt) == [[0], [1, 2]]
+    assert libks.ks_chain_groups([(16, 8, 8, 8), (128, 8, 8, 1)], 100, libks.DTYPE_F32) == [[0], [1]]
 
 
 def test_chain_plan_fuses_known_pairs():

@@ -342,8 +342,8 @@ ROW_CHAINS = {
     "radix2_n1024": (_radix(2, 10), 1000),
     "radix2_n4096": (_radix(2, 12), 5),
     "radix4_n4096": (_radix(4, 6), 37),
-    "radix8_n512": (_radix(8, 3), 203),
-    "blocks8_n256": ([(8, 8, 8, 4), (4, 8, 8, 8)], 77),
+    "radix4_n64": (_radix(4, 3), 1000),
+    "uneven_blocks": ([(4, 2, 8, 16), (8, 8, 2, 8), (32, 1, 16, 1)], 77),
     "odd_c3": ([(1, 6, 2, 3), (3, 2, 3, 2), (2, 2, 3, 2)], 203),
 }
 
