@@ -8,8 +8,8 @@
 // of the run in LDS (two row buffers, ping-pong) and write the R rows of Y:
 // HBM sees X and Y once, whatever the number of factors, where one launch per
 // factor moves every intermediate out and back. This is the case of deep
-// chains of small blocks: radix-2 and radix-4 butterflies, Walsh-Hadamard
-// products, small Monarch layers.
+// chains of small blocks (b * c <= 16): radix-2 and radix-4 butterflies,
+// Walsh-Hadamard products.
 //
 // Per factor (a, b, c, d), a thread owns (alpha, delta) groups: it loads the
 // group's b x c weight block into registers once and, for each of its rows,
@@ -17,10 +17,10 @@
 // outputs Z'[r][alpha][beta][delta] = sum_gamma K[alpha][delta][beta][gamma]
 // * Z[r][alpha][gamma][delta] to the other buffer. Consecutive threads take
 // consecutive delta, so LDS reads and writes of a wave are consecutive words
-// (or broadcasts when d is small). A factor's weights (at most 64 KB here)
-// are read once per workgroup, from the L2 cache after the first. fp32
-// accumulation; intermediates are fp32 (bf16 X and weights are widened
-// exactly).
+// when d >= 64 (strided by c or b words when d is small). A factor's
+// weights (at most 64 KB here) are read once per workgroup, from the L2
+// cache after the first. fp32 accumulation; intermediates are fp32 (bf16 X
+// and weights are widened exactly).
 
 #include <algorithm>
 #include <cstdio>
@@ -38,7 +38,7 @@ constexpr int kMaxFactors = 16;              // factors per launch
 constexpr int kMaxWidth = 4096;              // widest row of the run (elements)
 constexpr int kLdsTarget = 32 * 1024;        // LDS of the two row buffers (rows of 4096: 2 rows)
 constexpr int64_t kMaxWeightBytes = 64 * 1024;
-constexpr int kMaxBlock = 16;               // b * c held in registers
+constexpr int kMaxBlock = 16;                // b * c held in registers
 
 struct RowChainArgs {
     int nf;                  // factors in the run
