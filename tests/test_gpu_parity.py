@@ -602,3 +602,25 @@ def test_kslinear_layer_gradients(bf16):
     assert _rel(L.weights[0].grad.float().cpu().numpy(), dK0) <= tol
     assert _rel(x.grad.float().reshape(-1, L.n_in).cpu().numpy(), dx) <= tol
 
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_kslinear_inference_row_chain(bf16):
+    """Without gradients the layer runs its chain through chain_matmul: a
+    radix-4 butterfly on n = 256 becomes one row-resident launch, and its
+    output matches the oracle chain on the layer's own weights."""
+    from kronecker_sparse_structured_amd import layer
+    pats = _radix(4, 4)
+    assert libks.ks_chain_groups(pats, 64, libks.DTYPE_BF16 if bf16 else libks.DTYPE_F32) == [[0, 1, 2, 3]]
+    dtype = torch.bfloat16 if bf16 else torch.float32
+    L = layer.KSLinear(pats, dtype=dtype, device=DEV, seed=5)
+    x_np = np.random.default_rng(12).standard_normal((3, 21, L.n_in), dtype=np.float32)
+    x = to_dev(x_np.reshape(-1, L.n_in), bf16).reshape(3, 21, L.n_in)
+    with torch.no_grad():
+        y = L(x)
+    torch.cuda.synchronize()
+    assert y.shape == (3, 21, L.n_out) and y.dtype == torch.float32
+    Ks = [oracle.widen(w.detach().view(torch.int16).cpu().numpy().view(np.uint16), "bf16") if bf16 else
+          oracle.widen(w.detach().cpu().numpy(), "f32") for w in L.weights]
+    ref = oracle.ks_chain_matmul(pats, Ks, host_values(x_np.reshape(-1, L.n_in), bf16))
+    assert _rel(y.reshape(-1, L.n_out).cpu().numpy(), ref) <= FP32_REL_TOL
