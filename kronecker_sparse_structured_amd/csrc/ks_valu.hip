@@ -53,15 +53,21 @@ __host__ __device__ constexpr int nb_rule(int b, int c, int dv) {
     return nb;
 }
 
-// Betas per thread for a mapping. In slab mode with d = 4, one thread per
-// alpha (all b betas) stores b strided 16-byte vectors; one beta per thread
-// instead makes consecutive lanes store consecutive vectors (the lanes of
-// one alpha share its X slab, an LDS broadcast). Measured on (256, 4, 4, 4):
-// 3.9 against 2.5 TB/s; for other slab shapes the register rule is as fast
-// or faster.
+// Betas per thread for a mapping. In slab mode a thread's outputs are
+// nb * d consecutive floats; when that run is longer than one 16-byte
+// vector, a wave's store instruction writes vectors 16 * nb * d / 4 bytes
+// apart and no instruction covers whole lines. Runs of exactly 4 floats
+// (nb = 4 / d; the threads of one alpha share its X slab, an LDS broadcast)
+// make consecutive lanes store consecutive vectors. Measured: (256, 4, 4, 4)
+// 3.9 against 2.5 TB/s (nb 4 -> 1); with c >= 8, (256, 8, 8, 2) +26 %,
+// (128, 8, 8, 4) +14 %, (512, 8, 8, 1) +7 % (bf16 +81 %); with c = 4 and
+// d = 2 the register rule was 4 % faster, so it stays.
 __host__ __device__ constexpr int nb_pick(int b, int c, int dv, bool lane) {
     const int nb = nb_rule(b, c, dv);
-    return (!lane && dv == 4 && nb == b) ? 1 : nb;
+    if (lane) return nb;
+    if (dv == 4 && nb == b) return 1;
+    if (c >= 8 && dv <= 4 && nb * dv > 4 && b % (4 / dv) == 0) return 4 / dv;
+    return nb;
 }
 
 struct ValuArgs {
