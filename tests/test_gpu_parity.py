@@ -118,7 +118,8 @@ def test_fuzz_patterns_all_families(p, batch):
         check_factor(p, X, W, Y.cpu().numpy())
 
 
-@pytest.mark.parametrize("p", [(2, 16, 16, 8), (64, 8, 8, 8), (256, 16, 16, 16), (2, 64, 16, 6)],
+@pytest.mark.parametrize("p", [(2, 16, 16, 8), (64, 8, 8, 8), (256, 16, 16, 16), (2, 64, 16, 6),
+                               (512, 8, 8, 1), (256, 8, 8, 2), (128, 8, 8, 4), (512, 4, 4, 2)],
                          ids=lambda p: "%d_%d_%d_%d" % p)
 def test_bf16_and_mixed_inputs(p):
     X, W = datagen.random_pattern_inputs(p, 70, seed=99)
