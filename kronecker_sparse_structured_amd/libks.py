@@ -240,7 +240,8 @@ def ks_chain_matmul(ps: Sequence, Ws: Sequence, X, Y, batch: int, dtype: int, ws
 
 
 def ks_chain_plan(ps: Sequence, batch: int, dtype: int, flags: int = CHAIN_AUTO) -> list:
-    """Group lengths (1 = single factor, 2 = fused pair) of a chain's launches."""
+    """Group lengths of a chain's launches (1 = single factor, 2 = fused pair or a
+    run of two, more = a row-resident run)."""
     cap = max(len(ps), 1)
     lens = (ctypes.c_int * cap)()
     ng = ctypes.c_int(0)
