@@ -11,14 +11,26 @@ outputs rotate so that each step reads data that is not in the 256 MB
 Infinity Cache or the L2 (the working set of a step is re-read only after
 more than 288 MB of other traffic).
 
-Default workload: the ViT-S/16 MLP up-projection as one KS factor, pattern
-(4, 64, 16, 6) mapping 384 -> 1536, 25,216 rows (128 images x 197 tokens),
-fp32.
+Default workload: the largest configuration, the 65,536-point butterfly
+chain -- four factors (16^k, 16, 16, 16^(3-k)), k = 0..3, on 4,096 rows, fp32
+(`--dtype bf16`: bf16 X and weights, fp32 accumulation and outputs) -- run
+through ks_chain_matmul with fusion where the planner finds it. Other
+workloads (`--workload vit_mlp`, `gpt2_mlp`, ...) are available.
 
-Printed: one JSON line with the throughput (algorithmic GB/s), TFLOP/s, the
-roofline of the dominant kernel (its average launch duration from HIP events
-on the launch stream around the timed launches) and the fp64 oracle timed on
-this host's cores on a bounded sample of the same workload.
+Printed: one JSON line with
+  value      algorithmic GB/s of a step as run (each launch group reads its
+             input and weights and writes its output once) over the wall time
+             of the K timed steps;
+  roofline   the dominant kernel: the launch group that takes the most time,
+             timed on its own with HIP events on the launch stream (back to
+             back, rotated inputs), its algorithmic bytes per launch over its
+             average launch duration; also the whole step against the bytes
+             it moves and against the fully fused minimum |X| + |Y| + weights,
+             and a plain device copy's rate as the practical ceiling;
+  per_group / per_factor   every launch group, and every factor as a single
+             launch, timed the same way;
+  cpu_baseline   the fp64 oracle timed on this host's cores on a bounded
+             sample of the same workload.
 """
 from __future__ import annotations
 
@@ -64,7 +76,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="vit_mlp")
+    ap.add_argument("--workload", default="butterfly65536")
     ap.add_argument("--dtype", default="f32", choices=["f32", "bf16"])
     ap.add_argument("--kernel", default="auto", choices=["auto", "generic", "valu", "mfma", "mfma_lds"])
     ap.add_argument("--no-fuse", action="store_true", help="chains: one launch per factor")
@@ -97,12 +109,13 @@ CALIB_BYTES = 256 * 2 ** 20      # the --calib-copy device copy reads and writes
 
 
 def ingest_counters(args) -> int:
-    """HBM bytes per step of the workload's KS kernel(s) from two counter
-    runs of the same command. FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
-    are each scaled by what the same counter reads for the calibration copy
-    (CALIB_BYTES read and written) and summed over the KS dispatches, then
-    divided by the number of steps (one dispatch per step for a single
-    factor, one per launch group for a chain)."""
+    """HBM bytes per launch group (and per step) of the workload's KS kernels
+    from two counter runs of the same command (`--no-factors --calib-copy`).
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are each scaled by what the
+    same counter reads for the calibration copy (CALIB_BYTES read and
+    written). The KS dispatches come in whole steps, one per launch group in
+    group order, so group g's bytes are the mean over the dispatches at
+    positions g, g + groups, ..."""
     import csv
     from collections import defaultdict
     from kronecker_sparse_structured_amd import datagen, libks
@@ -128,34 +141,35 @@ def ingest_counters(args) -> int:
         return vals, names
 
     out = {}
-    scaled = {}
+    per_group = {}
     for path, counter in ((args.ingest_counters[0], "FETCH_SIZE"), (args.ingest_counters[1], "WRITE_SIZE")):
         vals, names = per_dispatch(path, counter)
-        ks_ids = [k for k, n in names.items() if "ks::" in n]
+        ks_ids = sorted((k for k, n in names.items() if "ks::" in n), key=int)
         last_ks = max((int(k) for k in ks_ids), default=-1)
         # the calibration copies run after the timed KS launches (earlier
         # copies are the bench's input replication, of other sizes)
         calib = [vals[k] for k, n in names.items()
                  if ("copyBuffer" in n or "copy_kernel" in n) and int(k) > last_ks]
-        ks = [vals[k] for k in ks_ids]
-        if not calib or not ks:
+        if not calib or not ks_ids:
             print("no calibration copy or no KS dispatch in %s" % path, file=sys.stderr)
             return 1
-        if len(ks) % per_step != 0:
-            print("%d KS dispatches is not a whole number of %d-launch steps" % (len(ks), per_step),
+        if len(ks_ids) % per_step != 0:
+            print("%d KS dispatches is not a whole number of %d-launch steps" % (len(ks_ids), per_step),
                   file=sys.stderr)
             return 1
-        steps = len(ks) // per_step
+        steps = len(ks_ids) // per_step
         factor = CALIB_BYTES / (max(calib) * 1024.0)
-        scaled[counter] = (sum(ks) / steps) * 1024.0 * factor
+        per_group[counter] = [sum(vals[ks_ids[i]] for i in range(g, len(ks_ids), per_step)) / steps * 1024.0 * factor
+                              for g in range(per_step)]
         out[counter.lower() + "_factor"] = round(factor, 4)
-        out[counter.lower() + "_kib_per_step"] = round(sum(ks) / steps, 1)
-        out[counter.lower() + "_launches"] = len(ks)
-    key = args.workload + ":" + args.dtype + (":nofuse" if args.no_fuse else "")
+        out[counter.lower() + "_kib_per_step"] = round(sum(vals[k] for k in ks_ids) / steps, 1)
+        out[counter.lower() + "_launches"] = len(ks_ids)
+    key = traffic_key(args)
     db = {}
     if os.path.exists(TRAFFIC_FILE):
         db = json.load(open(TRAFFIC_FILE))
-    out["bytes_per_step"] = int(scaled["FETCH_SIZE"] + scaled["WRITE_SIZE"])
+    out["group_bytes"] = [int(f + w) for f, w in zip(per_group["FETCH_SIZE"], per_group["WRITE_SIZE"])]
+    out["bytes_per_step"] = int(sum(out["group_bytes"]))
     out["launches_per_step"] = per_step
     out["source_hash"] = kernel_source_hash()
     db[key] = out
@@ -242,22 +256,20 @@ def main():
     wst = [torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None for _ in range(nset)]
     del X
 
-    # algorithmic bytes and flops of one step, as run
+    # launch groups of one step (a single factor is one group) and their
+    # algorithmic bytes as run: each group reads its input and writes its
+    # output once (fp32 between groups) and reads its weights once
     flops = sum(2 * batch * datagen.nnz(p) for p in wl.patterns)
-    if chain:
-        # as run: each launch group reads its input and writes its output
-        # once (fp32 between groups) and reads its weights once.
-        bytes_run = 0
-        x_sz = xb
-        for grp in libks.ks_chain_groups(wl.patterns, batch, dt, flags):
-            bytes_run += x_sz * batch * datagen.n_in(wl.patterns[grp[0]])
-            bytes_run += 4 * batch * datagen.n_out(wl.patterns[grp[-1]])
-            bytes_run += sum(wbytes * datagen.nnz(wl.patterns[k]) for k in grp)
-            x_sz = 4
-        bytes_min = step_bytes + sum(wbytes * datagen.nnz(p) for p in wl.patterns)
-    else:
-        bytes_run = factor_bytes(wl.patterns[0], xb, wbytes, batch)
-        bytes_min = bytes_run
+    groups = libks.ks_chain_groups(wl.patterns, batch, dt, flags) if chain else [[0]]
+    group_bytes = []
+    x_sz = xb
+    for grp in groups:
+        gb = x_sz * batch * datagen.n_in(wl.patterns[grp[0]]) + 4 * batch * datagen.n_out(wl.patterns[grp[-1]])
+        gb += sum(wbytes * datagen.nnz(wl.patterns[k]) for k in grp)
+        group_bytes.append(gb)
+        x_sz = 4
+    bytes_run = sum(group_bytes)
+    bytes_min = step_bytes + sum(wbytes * datagen.nnz(p) for p in wl.patterns)
 
     stream = torch.cuda.current_stream(dev)
 
@@ -301,24 +313,44 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # average GPU time of one step (one launch for a single factor), from
-    # HIP events on the launch stream around the timed launches
+    # average GPU time of one step, from HIP events on the launch stream
+    # around the timed launches
     mean_ms = ev0.elapsed_time(ev1) / args.steps
 
     value = bytes_run * args.steps / wall / 1e9
-    achieved = bytes_run / (mean_ms * 1e-3) / 1e9
     peak_flops = BF16_PEAK_TFLOPS if bf16 else FP32_PEAK_TFLOPS
     tflops = flops / (mean_ms * 1e-3) / 1e12
-    t_roof = max(bytes_run / (HBM_PEAK_GBS * 1e9), flops / (peak_flops * 1e12))
-    bound = "hbm" if bytes_run / (HBM_PEAK_GBS * 1e9) >= flops / (peak_flops * 1e12) else "mfma"
+
+    # Each launch group of a chain timed on its own: back-to-back launches of
+    # that group's kernel on inputs of its shape, HIP events on the launch
+    # stream. The dominant kernel is the group that takes the most time; the
+    # roofline is its algorithmic bytes (or flops) per launch over its
+    # average launch duration.
+    per_group = None
+    if chain and not args.no_factors and not args.calib_copy:
+        per_group = time_groups(args, wl, groups, group_bytes, Wt, Xt[0], bf16, flags, lib, sp, stream, torch,
+                                np, datagen, libks)
+    if per_group:
+        dom = max(range(len(per_group)), key=lambda g: per_group[g]["ms"])
+        dom_ms, dom_bytes = per_group[dom]["ms"], group_bytes[dom]
+        dom_flops = sum(2 * batch * datagen.nnz(wl.patterns[k]) for k in groups[dom])
+        dom_label = per_group[dom]["kernel"]
+    else:
+        dom = 0 if not chain else None
+        dom_ms, dom_bytes, dom_flops = mean_ms, bytes_run, flops
+        dom_label = (libks.ks_plan_describe(wl.patterns[0], batch, dt) if not chain
+                     else "whole step (launch groups not timed on their own)")
+    dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
+    dom_tflops = dom_flops / (dom_ms * 1e-3) / 1e12
+    bound = "hbm" if dom_bytes / (HBM_PEAK_GBS * 1e9) >= dom_flops / (peak_flops * 1e12) else "mfma"
+    t_roof = max(dom_bytes / (HBM_PEAK_GBS * 1e9), dom_flops / (peak_flops * 1e12))
 
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
+    if os.path.exists(TRAFFIC_FILE) and dom is not None:
         try:
-            rec = json.load(open(TRAFFIC_FILE)).get(args.workload + ":" + args.dtype +
-                                                     (":nofuse" if args.no_fuse else ""))
-            if rec and rec.get("source_hash") == kernel_source_hash():
-                traffic = rec.get("bytes_per_step")
+            rec = json.load(open(TRAFFIC_FILE)).get(traffic_key(args))
+            if rec and rec.get("source_hash") == kernel_source_hash() and len(rec.get("group_bytes", [])) > dom:
+                traffic = rec["group_bytes"][dom]
         except (ValueError, OSError):
             traffic = None
 
@@ -331,55 +363,34 @@ def main():
 
     roofline = {
         "bound": bound,
-        "achieved": round(achieved if bound == "hbm" else tflops, 2),
+        "achieved": round(dom_gbs if bound == "hbm" else dom_tflops, 2),
         "peak": HBM_PEAK_GBS if bound == "hbm" else peak_flops,
         "unit": "GB/s" if bound == "hbm" else "TFLOP/s",
-        "frac": round((achieved / HBM_PEAK_GBS) if bound == "hbm" else (tflops / peak_flops), 4),
+        "frac": round((dom_gbs / HBM_PEAK_GBS) if bound == "hbm" else (dom_tflops / peak_flops), 4),
         "traffic": traffic,
-        "roofline_time_frac": round(t_roof / (mean_ms * 1e-3), 4),
+        "kernel": dom_label,
+        "launch_ms": round(dom_ms, 5),
+        "bytes_per_launch": dom_bytes,
+        "flops_per_launch": dom_flops,
+        "roofline_time_frac": round(t_roof / (dom_ms * 1e-3), 4),
+        # the whole step (every launch group) against the bytes it moves as
+        # run, and against the fully fused minimum |X| + |Y| + weights
+        "step_frac_as_run": round(bytes_run / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "frac_vs_fused_minimum": round(bytes_min / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
     }
+    if not args.calib_copy and not args.no_factors:
+        roofline["copy_ceiling_gbs"] = copy_ceiling(dev, stream, torch)
 
-    # chains: each factor timed on its own (back-to-back launches of its
-    # kernel on inputs of its shape), and the chain's fraction also against
-    # the fully fused minimum |X| + |Y| + weights
+    # chains: each factor also timed as a single launch (not fused)
     per_factor = None
     if chain and not args.no_factors and not args.calib_copy:
-        per_factor = []
-        for k, p in enumerate(wl.patterns):
-            dtk = dt if k == 0 else (libks.DTYPE_BF16W if bf16 else libks.DTYPE_F32)
-            xbk = xb if k == 0 else 4
-            fbytes = factor_bytes(p, xbk, wbytes, batch)
-            ksets = max(1, int(np.ceil(CACHE_BYTES / fbytes)) + 1)
-            xs = [Xt[0] if k == 0 else torch.randn((batch, datagen.n_in(p)), device=dev)]
-            for _ in range(ksets - 1):
-                xs.append(xs[0].clone())
-            ys = [torch.empty((batch, datagen.n_out(p)), dtype=torch.float32, device=dev) for _ in range(ksets)]
-            opt = libks.ks_options_t()
-            pat = libks.ks_pattern_t(*p)
-            fcalls = [(pat, ctypes.c_void_p(Wt[k].data_ptr()), ctypes.c_void_p(xs[j].data_ptr()),
-                       ctypes.c_void_p(ys[j].data_ptr()), batch, dtk, sp, ctypes.byref(opt)) for j in range(ksets)]
-            reps = 20
-            warm_up(lambda j: lib.ks_matmul_ex(*fcalls[j % ksets]), 3, torch)
-            f0 = torch.cuda.Event(enable_timing=True)
-            f1 = torch.cuda.Event(enable_timing=True)
-            f0.record(stream)
-            for j in range(reps):
-                st = lib.ks_matmul_ex(*fcalls[j % ksets])
-                if st != 0:
-                    raise libks.KSError(st, "bench factor")
-            f1.record(stream)
-            torch.cuda.synchronize()
-            fms = f0.elapsed_time(f1) / reps
-            per_factor.append({"pattern": list(p), "ms": round(fms, 5),
-                               "GB/s": round(fbytes / (fms * 1e-3) / 1e9, 1),
-                               "frac": round(fbytes / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                               "plan": libks.ks_plan_describe(p, batch, dtk)})
-            del xs, ys
-        roofline["frac_vs_fused_minimum"] = round(bytes_min / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        per_factor = time_factors(wl, Wt, Xt[0], bf16, lib, sp, stream, torch, np, datagen, libks)
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(wl, bf16, args.cpu_seconds)
+        # same unit as value: the GPU step's as-run bytes per row
+        cpu = cpu_baseline(wl, bf16, args.cpu_seconds, row_bytes=(bytes_run - sum(
+            wbytes * datagen.nnz(p) for p in wl.patterns)) / batch)
 
     out = {
         "metric": METRIC,
@@ -387,7 +398,9 @@ def main():
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": warm_steps,
+        "warmup": args.warmup,
+        "warmup_steps_run": warm_steps,
+        "warmup_min_seconds": WARM_SECONDS,
         "ms_per_step": round(wall * 1e3 / args.steps, 5),
         "kernel_ms_mean": round(mean_ms, 5),
         "tflops": round(tflops, 3),
@@ -406,6 +419,7 @@ def main():
             "bytes_min": bytes_min,
             "flops_per_step": flops,
             "chain_fused": bool(chain and not args.no_fuse),
+            "launch_groups": [list(g) for g in groups],
             "kernel": args.kernel if not chain else "chain",
             "plan": chain_plan_text(wl.patterns, batch, dt, flags, bf16) if chain else
                     libks.ks_plan_describe(wl.patterns[0], batch, dt),
@@ -415,10 +429,142 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if per_group is not None:
+        out["per_group"] = per_group
     if per_factor is not None:
         out["per_factor"] = per_factor
     print(json.dumps(out), flush=True)
     return 0
+
+
+def traffic_key(args) -> str:
+    return args.workload + ":" + args.dtype + (":nofuse" if args.no_fuse else "")
+
+
+def time_groups(args, wl, groups, group_bytes, Wt, X0, bf16, flags, lib, sp, stream, torch, np, datagen, libks):
+    """Each launch group of the chain on its own, as the chain runs it: the
+    first group on the workload's X, later ones on fp32 inputs of their
+    shape (with bf16 weights in a bf16 chain); a single factor through
+    ks_matmul_ex with the planner's choice, a fused group through
+    ks_chain_matmul on its factors (one launch, no workspace)."""
+    dev = X0.device
+    batch = wl.batch
+    out = []
+    for g, grp in enumerate(groups):
+        k0, k1 = grp[0], grp[-1]
+        pats = wl.patterns[k0:k1 + 1]
+        if k0 == 0:
+            gdt = libks.DTYPE_BF16 if bf16 else libks.DTYPE_F32
+        else:
+            gdt = libks.DTYPE_BF16W if bf16 else libks.DTYPE_F32
+        sets = max(2, int(np.ceil(CACHE_BYTES / group_bytes[g])) + 1)
+        xs = [X0 if k0 == 0 else torch.randn((batch, datagen.n_in(pats[0])), device=dev)]
+        for _ in range(sets - 1):
+            xs.append(xs[0].clone())
+        ys = [torch.empty((batch, datagen.n_out(pats[-1])), dtype=torch.float32, device=dev) for _ in range(sets)]
+        if len(grp) == 1:
+            opt = libks.ks_options_t()
+            pat = libks.ks_pattern_t(*pats[0])
+            fn = lib.ks_matmul_ex
+            gcalls = [(pat, ctypes.c_void_p(Wt[k0].data_ptr()), ctypes.c_void_p(xs[j].data_ptr()),
+                       ctypes.c_void_p(ys[j].data_ptr()), batch, gdt, sp, ctypes.byref(opt)) for j in range(sets)]
+            plan = libks.ks_plan_describe(pats[0], batch, gdt)
+        else:
+            if libks.ks_chain_workspace_size(pats, batch, gdt, flags) != 0 or \
+                    libks.ks_chain_groups(pats, batch, gdt, flags) != [list(range(len(pats)))]:
+                raise RuntimeError("launch group %s does not run as one launch on its own" % (grp,))
+            parr = (libks.ks_pattern_t * len(pats))(*[libks.ks_pattern_t(*p) for p in pats])
+            warr = (ctypes.c_void_p * len(pats))(*[Wt[k].data_ptr() for k in grp])
+            fn = lib.ks_chain_matmul
+            gcalls = [(parr, len(pats), warr, ctypes.c_void_p(xs[j].data_ptr()), ctypes.c_void_p(ys[j].data_ptr()),
+                       batch, gdt, None, 0, flags, sp) for j in range(sets)]
+            plan = chain_plan_text(pats, batch, gdt, flags, bf16 and k0 == 0)
+
+        def run(j):
+            st = fn(*gcalls[j % sets])
+            if st != 0:
+                raise libks.KSError(st, "bench group %s" % (grp,))
+
+        warm_up(run, 3, torch)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        reps = 20
+        e0.record(stream)
+        for j in range(reps):
+            run(j)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        gbs = group_bytes[g] / (ms * 1e-3) / 1e9
+        out.append({"factors": list(grp), "ms": round(ms, 5), "bytes": group_bytes[g], "GB/s": round(gbs, 1),
+                    "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": plan})
+        del xs, ys
+    return out
+
+
+def time_factors(wl, Wt, X0, bf16, lib, sp, stream, torch, np, datagen, libks):
+    """Every factor of a chain as a single launch (ks_matmul_ex, the
+    planner's choice) on inputs of its shape, back to back with HIP events."""
+    dev = X0.device
+    batch = wl.batch
+    xb = 2 if bf16 else 4
+    wbytes = 2 if bf16 else 4
+    out = []
+    for k, p in enumerate(wl.patterns):
+        dtk = (libks.DTYPE_BF16 if k == 0 else libks.DTYPE_BF16W) if bf16 else libks.DTYPE_F32
+        xbk = xb if k == 0 else 4
+        fbytes = factor_bytes(p, xbk, wbytes, batch)
+        ksets = max(1, int(np.ceil(CACHE_BYTES / fbytes)) + 1)
+        xs = [X0 if k == 0 else torch.randn((batch, datagen.n_in(p)), device=dev)]
+        for _ in range(ksets - 1):
+            xs.append(xs[0].clone())
+        ys = [torch.empty((batch, datagen.n_out(p)), dtype=torch.float32, device=dev) for _ in range(ksets)]
+        opt = libks.ks_options_t()
+        pat = libks.ks_pattern_t(*p)
+        fcalls = [(pat, ctypes.c_void_p(Wt[k].data_ptr()), ctypes.c_void_p(xs[j].data_ptr()),
+                   ctypes.c_void_p(ys[j].data_ptr()), batch, dtk, sp, ctypes.byref(opt)) for j in range(ksets)]
+        reps = 20
+        warm_up(lambda j: lib.ks_matmul_ex(*fcalls[j % ksets]), 3, torch)
+        f0 = torch.cuda.Event(enable_timing=True)
+        f1 = torch.cuda.Event(enable_timing=True)
+        f0.record(stream)
+        for j in range(reps):
+            st = lib.ks_matmul_ex(*fcalls[j % ksets])
+            if st != 0:
+                raise libks.KSError(st, "bench factor")
+        f1.record(stream)
+        torch.cuda.synchronize()
+        fms = f0.elapsed_time(f1) / reps
+        out.append({"pattern": list(p), "ms": round(fms, 5),
+                    "GB/s": round(fbytes / (fms * 1e-3) / 1e9, 1),
+                    "frac": round(fbytes / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "plan": libks.ks_plan_describe(p, batch, dtk)})
+        del xs, ys
+    return out
+
+
+COPY_BYTES = 2 ** 30     # the device copy of copy_ceiling reads and writes this many bytes
+
+
+def copy_ceiling(dev, stream, torch) -> float:
+    """A plain 1 GiB device-to-device copy (torch's copy kernel), timed with
+    HIP events over back-to-back calls after warm-up: GB/s counting the bytes
+    read plus the bytes written. A practical streaming ceiling of this GPU,
+    reported beside the published 8 TB/s peak."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    warm_up(lambda i: dst.copy_(src), 3, torch)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return round(2 * COPY_BYTES / (ms * 1e-3) / 1e9, 1)
 
 
 def backward(args) -> int:
@@ -691,7 +837,7 @@ def comparator(p, batch, Xt, Wt, Yt, nset, ms_ours, stream, torch):
     return {"comparator_ms": round(ms, 5), "speedup": round(ms / ms_ours, 3), "comparator_max_rel_diff": diff}
 
 
-def cpu_baseline(wl, bf16, target_s):
+def cpu_baseline(wl, bf16, target_s, row_bytes=None):
     """The fp64 oracle as it stands, timed on this host on a bounded number
     of rows of the same workload; reported in the same unit (GB/s of the
     workload's algorithmic bytes per row)."""
@@ -702,7 +848,9 @@ def cpu_baseline(wl, bf16, target_s):
 
     lib = oracle.load()
     xw = "bf16" if bf16 else "f32"
-    small = datagen.scaled(wl, min(wl.batch, 4096))
+    # at most 4,096 rows, and at most 8 M input elements (wide chains), drawn
+    # the same way as the workload; the timed runs repeat over them
+    small = datagen.scaled(wl, max(1, min(wl.batch, 4096, (8 << 20) // wl.n_in)))
     X, Ws = datagen.draw(small)
     Wd = [oracle.widen(datagen.bf16_bits(W), "bf16") if bf16 else oracle.widen(W) for W in Ws]
     Xd_all = oracle.widen(datagen.bf16_bits(X), "bf16") if bf16 else oracle.widen(X)
@@ -727,8 +875,8 @@ def cpu_baseline(wl, bf16, target_s):
     for _ in range(reps):
         total_t += run(want)
     rows_done = want * reps
-    xb = 2 if bf16 else 4
-    row_bytes = xb * wl.n_in + 4 * wl.n_out
+    if row_bytes is None:
+        row_bytes = (2 if bf16 else 4) * wl.n_in + 4 * wl.n_out
     gbs = row_bytes * rows_done / total_t / 1e9
     cores = oracle.num_threads(lib)
 

@@ -72,7 +72,7 @@ typedef enum ks_status_t {
     KS_ERR_NULL = 1,            /* a required pointer is NULL (batch > 0)      */
     KS_ERR_PATTERN = 2,         /* a field < 1, or n_in/n_out/nnz >= 2^31      */
     KS_ERR_BATCH = 3,           /* batch < 0 or batch >= 2^31                  */
-    KS_ERR_DTYPE = 4,           /* unknown dtype (or BF16W as a chain dtype)   */
+    KS_ERR_DTYPE = 4,           /* unknown dtype                               */
     KS_ERR_CHAIN_MISMATCH = 5,  /* n < 1, or n_out(p[k]) != n_in(p[k+1])       */
     KS_ERR_WORKSPACE = 6,       /* workspace NULL or smaller than required     */
     KS_ERR_ALIGN = 7,           /* pointer not aligned to its element size     */
@@ -196,8 +196,8 @@ ks_status_t ks_matmul_dw(ks_pattern_t p, const void* dY, const void* X, void* dW
  * ks_chain_workspace_size: bytes of device workspace ks_chain_matmul needs
  * for these arguments (0 if none), written to *bytes.
  *   p, n   the factors in application order (p[0] is applied to X first).
- *   dt     KS_DTYPE_F32 or KS_DTYPE_BF16 (chain dtype; intermediates are
- *          always fp32).
+ *   dt     KS_DTYPE_F32, KS_DTYPE_BF16 or KS_DTYPE_BF16W (chain dtype: the
+ *          types of X and of every W; intermediates are always fp32).
  *   flags  KS_CHAIN_AUTO or KS_CHAIN_NO_FUSE.
  * Returns the same validation statuses as ks_chain_matmul for p, n, batch,
  * dt and flags; KS_ERR_NULL if bytes is NULL.
@@ -213,7 +213,8 @@ ks_status_t ks_chain_workspace_size(const ks_pattern_t* p, int n, int64_t batch,
  *   X      device, batch x n_in(p[0]); Y device fp32, batch x n_out(p[n-1]).
  *   dt     KS_DTYPE_F32: everything fp32. KS_DTYPE_BF16: X and every W are
  *          bf16; intermediates and Y are fp32, so factors after the first
- *          read fp32 inputs with bf16 weights.
+ *          read fp32 inputs with bf16 weights. KS_DTYPE_BF16W: X fp32 and
+ *          every W bf16 (the tail of a bf16 chain run on its own).
  *   ws     device workspace of ws_bytes >= ks_chain_workspace_size(...);
  *          may be NULL when that size is 0. 16-byte aligned. Must not
  *          overlap X, Y or any W.

@@ -36,7 +36,18 @@ ks_status_t check_batch(int64_t batch) {
     return (batch < 0 || batch >= kLimit) ? KS_ERR_BATCH : KS_OK;
 }
 
-ks_status_t factor_types(ks_dtype_t dt, int* xt, int* wt) {
+// The integer a C caller passed for an enum parameter. C allows any int
+// there; in C++ loading a value outside the enum's range as the enum type is
+// undefined, so the bits are read as an int instead.
+template <typename E>
+int enum_value(const E* e) {
+    static_assert(sizeof(E) == sizeof(int), "C enums are int-sized");
+    int v;
+    std::memcpy(&v, e, sizeof v);
+    return v;
+}
+
+ks_status_t factor_types(int dt, int* xt, int* wt) {
     switch (dt) {
         case KS_DTYPE_F32: *xt = ks::kF32; *wt = ks::kF32; return KS_OK;
         case KS_DTYPE_BF16: *xt = ks::kBF16; *wt = ks::kBF16; return KS_OK;
@@ -127,16 +138,15 @@ struct ChainPlan {
     size_t buf_bytes = 0;          // bytes per workspace buffer
 };
 
-ks_status_t plan_chain(const ks_pattern_t* p, int n, int64_t batch, ks_dtype_t dt,
+ks_status_t plan_chain(const ks_pattern_t* p, int n, int64_t batch, int dt,
                        unsigned flags, ChainPlan* plan) {
     if (!p) return KS_ERR_NULL;
     if (n < 1) return KS_ERR_CHAIN_MISMATCH;
     if (flags != KS_CHAIN_AUTO && flags != KS_CHAIN_NO_FUSE) return KS_ERR_INVALID;
     ks_status_t st = check_batch(batch);
     if (st != KS_OK) return st;
-    if (dt == KS_DTYPE_F32) { plan->xt0 = ks::kF32; plan->wt = ks::kF32; }
-    else if (dt == KS_DTYPE_BF16) { plan->xt0 = ks::kBF16; plan->wt = ks::kBF16; }
-    else return KS_ERR_DTYPE;
+    st = factor_types(dt, &plan->xt0, &plan->wt);
+    if (st != KS_OK) return st;
     plan->shapes.resize(n);
     for (int k = 0; k < n; ++k) {
         st = shape_of(p[k], &plan->shapes[k]);
@@ -180,33 +190,9 @@ ks_status_t plan_chain(const ks_pattern_t* p, int n, int64_t batch, ks_dtype_t d
     return KS_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* ks_status_string(ks_status_t status) {
-    switch (status) {
-        case KS_OK: return "KS_OK";
-        case KS_ERR_NULL: return "KS_ERR_NULL: a required pointer is NULL";
-        case KS_ERR_PATTERN: return "KS_ERR_PATTERN: pattern field < 1 or size >= 2^31";
-        case KS_ERR_BATCH: return "KS_ERR_BATCH: batch < 0 or >= 2^31";
-        case KS_ERR_DTYPE: return "KS_ERR_DTYPE: unsupported dtype";
-        case KS_ERR_CHAIN_MISMATCH: return "KS_ERR_CHAIN_MISMATCH: chain is empty or widths do not match";
-        case KS_ERR_WORKSPACE: return "KS_ERR_WORKSPACE: workspace missing or too small";
-        case KS_ERR_ALIGN: return "KS_ERR_ALIGN: pointer not aligned to its element size";
-        case KS_ERR_OVERLAP: return "KS_ERR_OVERLAP: output or workspace overlaps an input";
-        case KS_ERR_HIP: return "KS_ERR_HIP: a HIP call failed";
-        case KS_ERR_UNSUPPORTED: return "KS_ERR_UNSUPPORTED: the forced kernel cannot run this pattern";
-        case KS_ERR_INVALID: return "KS_ERR_INVALID: invalid flags or options";
-    }
-    return "KS_ERR_UNKNOWN";
-}
-
-const char* ks_version(void) { return "libks 0.1.0 gfx950"; }
-
-ks_status_t ks_matmul_ex(ks_pattern_t p, const void* W, const void* X, void* Y,
-                         int64_t batch, ks_dtype_t dt, hipStream_t stream,
-                         const ks_options_t* opt) {
+// ks_matmul and ks_matmul_ex with the dtype as the caller's int.
+ks_status_t matmul_impl(ks_pattern_t p, const void* W, const void* X, void* Y, int64_t batch, int dt,
+                        hipStream_t stream, const ks_options_t* opt) {
     ks_status_t st = check_options(opt);
     if (st != KS_OK) return st;
     Shape s;
@@ -241,9 +227,39 @@ ks_status_t ks_matmul_ex(ks_pattern_t p, const void* W, const void* X, void* Y,
     return run_factor(kernel, f);
 }
 
+}  // namespace
+
+extern "C" {
+
+const char* ks_status_string(ks_status_t status) {
+    switch (enum_value(&status)) {
+        case KS_OK: return "KS_OK";
+        case KS_ERR_NULL: return "KS_ERR_NULL: a required pointer is NULL";
+        case KS_ERR_PATTERN: return "KS_ERR_PATTERN: pattern field < 1 or size >= 2^31";
+        case KS_ERR_BATCH: return "KS_ERR_BATCH: batch < 0 or >= 2^31";
+        case KS_ERR_DTYPE: return "KS_ERR_DTYPE: unsupported dtype";
+        case KS_ERR_CHAIN_MISMATCH: return "KS_ERR_CHAIN_MISMATCH: chain is empty or widths do not match";
+        case KS_ERR_WORKSPACE: return "KS_ERR_WORKSPACE: workspace missing or too small";
+        case KS_ERR_ALIGN: return "KS_ERR_ALIGN: pointer not aligned to its element size";
+        case KS_ERR_OVERLAP: return "KS_ERR_OVERLAP: output or workspace overlaps an input";
+        case KS_ERR_HIP: return "KS_ERR_HIP: a HIP call failed";
+        case KS_ERR_UNSUPPORTED: return "KS_ERR_UNSUPPORTED: the forced kernel cannot run this pattern";
+        case KS_ERR_INVALID: return "KS_ERR_INVALID: invalid flags or options";
+    }
+    return "KS_ERR_UNKNOWN";
+}
+
+const char* ks_version(void) { return "libks 0.1.0 gfx950"; }
+
+ks_status_t ks_matmul_ex(ks_pattern_t p, const void* W, const void* X, void* Y,
+                         int64_t batch, ks_dtype_t dt, hipStream_t stream,
+                         const ks_options_t* opt) {
+    return matmul_impl(p, W, X, Y, batch, enum_value(&dt), stream, opt);
+}
+
 ks_status_t ks_matmul(ks_pattern_t p, const void* W, const void* X, void* Y,
                       int64_t batch, ks_dtype_t dt, hipStream_t stream) {
-    return ks_matmul_ex(p, W, X, Y, batch, dt, stream, nullptr);
+    return matmul_impl(p, W, X, Y, batch, enum_value(&dt), stream, nullptr);
 }
 
 ks_status_t ks_matmul_dx_workspace_size(ks_pattern_t p, ks_dtype_t dt, size_t* bytes) {
@@ -252,7 +268,7 @@ ks_status_t ks_matmul_dx_workspace_size(ks_pattern_t p, ks_dtype_t dt, size_t* b
     ks_status_t st = shape_of(p, &s);
     if (st != KS_OK) return st;
     int xt = 0, wt = 0;
-    st = factor_types(dt, &xt, &wt);
+    st = factor_types(enum_value(&dt), &xt, &wt);
     if (st != KS_OK) return st;
     *bytes = (static_cast<size_t>(s.nnz) * ks::elem_bytes(wt) + 255) / 256 * 256;
     return KS_OK;
@@ -266,7 +282,7 @@ ks_status_t ks_matmul_dx(ks_pattern_t p, const void* W, const void* dY, void* dX
     st = check_batch(batch);
     if (st != KS_OK) return st;
     int xt = 0, wt = 0;
-    st = factor_types(dt, &xt, &wt);
+    st = factor_types(enum_value(&dt), &xt, &wt);
     if (st != KS_OK) return st;
     if (batch == 0) return KS_OK;
     if (!W || !dY || !dX) return KS_ERR_NULL;
@@ -305,7 +321,7 @@ ks_status_t ks_matmul_dw_workspace_size(ks_pattern_t p, int64_t batch, ks_dtype_
     st = check_batch(batch);
     if (st != KS_OK) return st;
     int xt = 0, wt = 0;
-    st = factor_types(dt, &xt, &wt);
+    st = factor_types(enum_value(&dt), &xt, &wt);
     if (st != KS_OK) return st;
     *bytes = ks::dw_workspace_bytes(s, xt, batch);
     return KS_OK;
@@ -319,7 +335,7 @@ ks_status_t ks_matmul_dw(ks_pattern_t p, const void* dY, const void* X, void* dW
     st = check_batch(batch);
     if (st != KS_OK) return st;
     int xt = 0, wt = 0;
-    st = factor_types(dt, &xt, &wt);
+    st = factor_types(enum_value(&dt), &xt, &wt);
     if (st != KS_OK) return st;
     if (!dW) return KS_ERR_NULL;
     if (batch > 0 && (!dY || !X)) return KS_ERR_NULL;
@@ -341,7 +357,7 @@ ks_status_t ks_chain_workspace_size(const ks_pattern_t* p, int n, int64_t batch,
                                     ks_dtype_t dt, unsigned flags, size_t* bytes) {
     if (!bytes) return KS_ERR_NULL;
     ChainPlan plan;
-    ks_status_t st = plan_chain(p, n, batch, dt, flags, &plan);
+    ks_status_t st = plan_chain(p, n, batch, enum_value(&dt), flags, &plan);
     if (st != KS_OK) return st;
     *bytes = (batch == 0) ? 0 : static_cast<size_t>(plan.nbuf) * plan.buf_bytes;
     return KS_OK;
@@ -351,7 +367,7 @@ ks_status_t ks_chain_plan(const ks_pattern_t* p, int n, int64_t batch, ks_dtype_
                           unsigned flags, int* group_len, int cap, int* groups) {
     if (!groups || (cap > 0 && !group_len)) return KS_ERR_NULL;
     ChainPlan plan;
-    ks_status_t st = plan_chain(p, n, batch, dt, flags, &plan);
+    ks_status_t st = plan_chain(p, n, batch, enum_value(&dt), flags, &plan);
     if (st != KS_OK) return st;
     const int ng = static_cast<int>(plan.group_len.size());
     *groups = ng;
@@ -364,7 +380,7 @@ ks_status_t ks_chain_matmul(const ks_pattern_t* p, int n, const void* const* W,
                             void* ws, size_t ws_bytes, unsigned flags,
                             hipStream_t stream) {
     ChainPlan plan;
-    ks_status_t st = plan_chain(p, n, batch, dt, flags, &plan);
+    ks_status_t st = plan_chain(p, n, batch, enum_value(&dt), flags, &plan);
     if (st != KS_OK) return st;
     if (batch == 0) return KS_OK;
     if (!W || !X || !Y) return KS_ERR_NULL;
@@ -429,7 +445,7 @@ ks_status_t ks_plan_describe(ks_pattern_t p, int64_t batch, ks_dtype_t dt, char*
     st = check_batch(batch);
     if (st != KS_OK) return st;
     int xt = 0, wt = 0;
-    st = factor_types(dt, &xt, &wt);
+    st = factor_types(enum_value(&dt), &xt, &wt);
     if (st != KS_OK) return st;
     const int kernel = choose_kernel(s, xt, wt);
     const int cus = 256;  // description only; launches use the device's count

@@ -468,8 +468,12 @@ ks_status_t launch_dw(const Shape& s, int xt, const float* dY, const void* X, fl
         return launch_kernel(fill_zero_kernel, dim3(grid_for(s.nnz)), dim3(kThreads), 0, stream, dK, s.nnz);
     const DwPlan pl = dw_plan(s, xt, batch);
     float* out = pl.ranges > 1 ? static_cast<float*>(ws) : dK;
+    // The matrix-core kernel streams X and dY in 16-byte vectors; for
+    // pointers aligned only to their element size the generic kernel runs
+    // over the same row ranges, so the partial sums fit the same workspace.
+    const bool vec_ok = (reinterpret_cast<uintptr_t>(X) & 15u) == 0 && (reinterpret_cast<uintptr_t>(dY) & 15u) == 0;
     ks_status_t st;
-    if (pl.mfma) {
+    if (pl.mfma && vec_ok) {
         DwArgs args;
         args.a = s.a; args.b = s.b; args.c = s.c; args.d = s.d;
         args.n_in = s.n_in; args.n_out = s.n_out; args.batch = batch;

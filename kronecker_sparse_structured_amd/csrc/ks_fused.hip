@@ -28,6 +28,14 @@
 // One LDS barrier per stage separates the two.
 // Z never leaves the chip: the pair moves |X| + |Y| + weights through HBM
 // instead of |X| + 2|Z| + |Y|.
+//
+// Alignment. X and Y need only be aligned to their element size. When X
+// starts xshift elements past a 16-byte boundary, the loader streams the
+// 16-byte granules that cover each row, from the boundary below it (a
+// granule never crosses a page, so the extra bytes are always readable), one
+// granule more per row (it lands in the row's padding), and the consumers
+// read every element xshift places further on. When Y is not 16-byte
+// aligned, phase B stores single elements.
 
 #include <algorithm>
 #include <cstdio>
@@ -83,9 +91,18 @@ struct FusedArgs {
     int64_t batch;
     int n_tiles;            // b0 / kBT
     int rows_per_split;     // multiple of kRows
+    int xshift;             // elements from the 16-byte boundary below X to X (the same in every row)
 };
 
-template <typename TX, typename TW>
+// The byte limit of issue_stage when rows start xshift elements past a
+// 16-byte boundary: the granule holding the last elements of the stage's last
+// row is one past the usual limit.
+__device__ __forceinline__ uint32_t shifted_limit(uint32_t limit, int xshift) {
+    return (xshift == 0 || limit > kNoVector - 16u) ? limit : limit + 16u;
+}
+
+// kYVec: Y is 16-byte aligned (vector stores in the fp32 phase B).
+template <typename TX, typename TW, bool kYVec>
 __global__ __launch_bounds__(kFusedThreads) void fused_pair_kernel(const TX* __restrict__ X,
                                                                    const TW* __restrict__ K0,
                                                                    const TW* __restrict__ K1,
@@ -115,15 +132,20 @@ __global__ __launch_bounds__(kFusedThreads) void fused_pair_kernel(const TX* __r
         StageMap m;
         m.rows = kRows;
         m.blocks = 1;
-        m.blk_vec = kC0 * kD0 / VW;                        // one whole row of X
-        m.pad_vec = kXPadBytes / 16;
+        // one whole row of X, and the granule past it when X is not 16-byte
+        // aligned (it takes the first vector of the row's padding)
+        const int extra = args.xshift != 0 ? 1 : 0;
+        m.blk_vec = kC0 * kD0 / VW + extra;
+        m.pad_vec = kXPadBytes / 16 - extra;
         m.row_vec = m.blk_vec + m.pad_vec;
         m.gstride = 0;
         LoaderPlan<INSTS> lp;
         make_loader_plan<INSTS>(m, INSTS, VW, EB, args.n_in, 1, m.blk_vec, t - kFusedConsumers * 64, &lp);
+        const TX* xbase = X - args.xshift;                 // 16-byte aligned
         auto issue = [&](int s) {
             const int64_t n0 = row_begin + int64_t(s) * kRows;
-            issue_stage<INSTS>(lp, INSTS, X + n0 * args.n_in, stage_limit(n0, row_end, args.n_in, EB),
+            issue_stage<INSTS>(lp, INSTS, xbase + n0 * args.n_in,
+                               shifted_limit(stage_limit(n0, row_end, args.n_in, EB), args.xshift),
                                lds + (s % kStages) * kStageBytes);
         };
         for (int s = 0; s < kStages - 1 && s < nsteps; ++s) issue(s);
@@ -162,7 +184,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_pair_kernel(const TX* __r
         const unsigned char* xs = lds + (s % kStages) * kStageBytes;
 #pragma unroll
         for (int rg = 0; rg < kRows; rg += 4) {
-            const TX* xa = reinterpret_cast<const TX*>(xs + (rg + q) * kRowBytes) + a_d0;
+            const TX* xa = reinterpret_cast<const TX*>(xs + (rg + q) * kRowBytes) + args.xshift + a_d0;
             floatx4 z[kSetsPerWave];
 #pragma unroll
             for (int j = 0; j < kSetsPerWave; ++j) z[j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -259,8 +281,15 @@ __global__ __launch_bounds__(kFusedThreads) void fused_pair_kernel(const TX* __r
 #pragma unroll
                     for (int k = 0; k < 4; ++k) y[k] = fmaf(k1r[k][g], z[k], y[k]);
                 }
-                if (r < rows)
-                    __builtin_nontemporal_store(y, reinterpret_cast<floatx4*>(Y + (n0 + r) * args.n_out + yoff));
+                if (r < rows) {
+                    float* yr = Y + (n0 + r) * args.n_out + yoff;
+                    if constexpr (kYVec) {
+                        __builtin_nontemporal_store(y, reinterpret_cast<floatx4*>(yr));
+                    } else {
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) __builtin_nontemporal_store(y[k], yr + k);
+                    }
+                }
             }
         };
         pipeline(phase_b);
@@ -282,6 +311,7 @@ ks_status_t launch_typed(const Shape& s0, const Shape& s1, const void* W0, const
     args.n_out = s1.n_out;
     args.batch = batch;
     args.n_tiles = s0.b / kBT;
+    args.xshift = static_cast<int>((reinterpret_cast<uintptr_t>(X) & 15u) / sizeof(TX));
     // about one resident wave of workgroups (as many per compute unit as fit its 160 KB of LDS)
     const size_t lds = fused_lds_bytes(int(sizeof(TX)));
     const int per_cu = std::max(1, std::min(4, int((160 * 1024) / lds)));
@@ -292,12 +322,11 @@ ks_status_t launch_typed(const Shape& s0, const Shape& s1, const void* W0, const
     const int64_t nsplit = (batch + args.rows_per_split - 1) / args.rows_per_split;
     const int64_t blocks = nsplit * args.n_tiles;
     if (blocks > 0x7fffffff) return KS_ERR_UNSUPPORTED;
-    return launch_kernel(fused_pair_kernel<TX, TW>, dim3(static_cast<unsigned>(blocks)), dim3(kFusedThreads),
-                         lds, stream, static_cast<const TX*>(X), static_cast<const TW*>(W0),
-                         static_cast<const TW*>(W1), Y, args);
+    const bool y_vec = (reinterpret_cast<uintptr_t>(Y) & 15u) == 0;
+    auto kernel = y_vec ? fused_pair_kernel<TX, TW, true> : fused_pair_kernel<TX, TW, false>;
+    return launch_kernel(kernel, dim3(static_cast<unsigned>(blocks)), dim3(kFusedThreads), lds, stream,
+                         static_cast<const TX*>(X), static_cast<const TW*>(W0), static_cast<const TW*>(W1), Y, args);
 }
-
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
 
@@ -313,7 +342,11 @@ ks_status_t launch_fused_pair(const Shape& s0, const Shape& s1, int xt, int wt0,
                               const void* W1, const void* X, float* Y, int64_t batch, hipStream_t stream,
                               int num_cus) {
     if (!fused_pair_supports(s0, s1, xt, wt0, wt1)) return KS_ERR_UNSUPPORTED;
-    if (!aligned16(X)) return KS_ERR_UNSUPPORTED;
+    // X and Y aligned to their element size (checked by the caller); rows
+    // are whole 16-byte granules apart, so every row has X's misalignment
+    if ((reinterpret_cast<uintptr_t>(X) % elem_bytes(xt)) != 0 || (reinterpret_cast<uintptr_t>(Y) & 3u) != 0 ||
+        (s0.n_in * elem_bytes(xt)) % 16 != 0)
+        return KS_ERR_UNSUPPORTED;
     if (xt == kF32 && wt0 == kF32) return launch_typed<float, float>(s0, s1, W0, W1, X, Y, batch, stream, num_cus);
     if (xt == kBF16 && wt0 == kBF16) return launch_typed<bf16_t, bf16_t>(s0, s1, W0, W1, X, Y, batch, stream, num_cus);
     if (xt == kF32 && wt0 == kBF16) return launch_typed<float, bf16_t>(s0, s1, W0, W1, X, Y, batch, stream, num_cus);

@@ -25,6 +25,14 @@
 //      K_G[16 alpha + beta][0]^T; wave w takes betas 4w .. 4w + 3;
 // and a storer wave writes the previous stage's Y tile from the other of
 // two LDS buffers as 16-byte vectors covering whole 1 KB row slabs.
+//
+// Alignment. X and Y need only be aligned to their element size. When X
+// starts xshift elements past a 16-byte boundary, the loader streams the
+// 16-byte granules that cover each slab from the boundary below it (a
+// granule never crosses a page, so the extra bytes are always readable), one
+// granule more per row (it takes the row's pad vector), and phase A reads
+// single elements xshift places further on; when Y is not 16-byte aligned
+// the storer writes single elements.
 
 #include <algorithm>
 #include <cstdio>
@@ -55,9 +63,12 @@ struct SlabArgs {
     int rows_per_split;      // a multiple of kR
     int insts, stages;       // loader instructions per stage, ring depth
     StageMap xmap;           // LDS layout of an X stage
+    int xshift;              // elements from the 16-byte boundary below X to X (the same in every row)
 };
 
-template <typename TX, typename TW>
+// kVec: X and Y are 16-byte aligned (xshift == 0): 16-byte LDS reads of X
+// and 16-byte stores of Y.
+template <typename TX, typename TW, bool kVec>
 __global__ __launch_bounds__(kStreamThreads + 64) void slab_pair_kernel(const TX* __restrict__ X,
                                                                         const TW* __restrict__ KF,
                                                                         const TW* __restrict__ KG,
@@ -96,8 +107,16 @@ __global__ __launch_bounds__(kStreamThreads + 64) void slab_pair_kernel(const TX
 #pragma unroll
             for (int r = 0; r < kR; ++r) v[r] = *reinterpret_cast<const floatx4*>(yt + r * kTileRow);
 #pragma unroll
-            for (int r = 0; r < kR; ++r)
-                if (r < rows) __builtin_nontemporal_store(v[r], reinterpret_cast<floatx4*>(yg + r * args.n_out));
+            for (int r = 0; r < kR; ++r) {
+                if (r < rows) {
+                    if constexpr (kVec) {
+                        __builtin_nontemporal_store(v[r], reinterpret_cast<floatx4*>(yg + r * args.n_out));
+                    } else {
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) __builtin_nontemporal_store(v[r][k], yg + r * args.n_out + k);
+                    }
+                }
+            }
         };
         for (int s = 0; s < nsteps; ++s) {
             lds_barrier();                                   // stage s ready
@@ -114,11 +133,14 @@ __global__ __launch_bounds__(kStreamThreads + 64) void slab_pair_kernel(const TX
         LoaderPlan<kMaxInsts> lp;
         make_loader_plan<kMaxInsts>(args.xmap, args.insts, VW, EB, args.n_in, 1, args.xmap.blk_vec,
                                     t - kConsumerThreads, &lp);
-        const TX* xbase = X + int64_t(alpha) * kSlab;
+        const TX* xbase = X - args.xshift + int64_t(alpha) * kSlab;   // 16-byte aligned
         auto issue = [&](int s) {
             const int64_t n0 = row_begin + int64_t(s) * kR;
-            issue_stage<kMaxInsts>(lp, args.insts, xbase + n0 * args.n_in, stage_limit(n0, row_end, args.n_in, EB),
-                                   lds + (s % kStages) * kStageBytes);
+            // vectors at or past the end of the last row's slab (and the
+            // granule holding its last elements, when shifted) load a dummy
+            const int64_t end = ((row_end - n0 - 1) * args.n_in + kSlab) * EB + (args.xshift != 0 ? 16 : 0);
+            const uint32_t limit = end >= int64_t(kNoVector) ? kNoVector : static_cast<uint32_t>(end);
+            issue_stage<kMaxInsts>(lp, args.insts, xbase + n0 * args.n_in, limit, lds + (s % kStages) * kStageBytes);
         };
         for (int s = 0; s < kStages - 1 && s < nsteps; ++s) issue(s);
         for (int s = 0; s < nsteps; ++s) {
@@ -160,14 +182,19 @@ __global__ __launch_bounds__(kStreamThreads + 64) void slab_pair_kernel(const TX
         const unsigned char* xs = lds + (s % kStages) * kStageBytes;
         // (A) Z[row][beta][delta] = sum_gamma K_F[alpha][delta][beta][gamma] X[row][alpha][gamma][delta]
         {
-            const TX* xa = reinterpret_cast<const TX*>(xs + col * xrow_bytes) + grp * kN + 4 * w;
+            const TX* xa = reinterpret_cast<const TX*>(xs + col * xrow_bytes) + args.xshift + grp * kN + 4 * w;
             floatx4 z[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) z[u] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 float av[4];
-                load4_f32(xa + ks * 4 * kN, av);                         // deltas 4w .. 4w + 3 of one gamma
+                if constexpr (kVec) {
+                    load4_f32(xa + ks * 4 * kN, av);                     // deltas 4w .. 4w + 3 of one gamma
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) av[u] = to_f32(xa[ks * 4 * kN + u]);
+                }
 #pragma unroll
                 for (int u = 0; u < 4; ++u) z[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], kf[u][ks], z[u], 0, 0, 0);
             }
@@ -204,15 +231,19 @@ ks_status_t launch_typed(const Shape& s0, const void* W0, const void* W1, const 
                          hipStream_t stream, int num_cus) {
     constexpr int EB = int(sizeof(TX));
     SlabArgs args;
+    args.xshift = static_cast<int>((reinterpret_cast<uintptr_t>(X) & 15u) / EB);
+    const bool vec = args.xshift == 0 && (reinterpret_cast<uintptr_t>(Y) & 15u) == 0;
     args.a = s0.a;
     args.n_in = s0.n_in;
     args.n_out = s0.n_out;
     args.batch = batch;
     args.xmap.rows = kR;
     args.xmap.blocks = 1;
-    args.xmap.blk_vec = kSlab * EB / 16;
+    // one slab per row and one pad vector (rows start in different banks);
+    // a shifted slab spans one granule more, which takes the pad vector
+    args.xmap.blk_vec = kSlab * EB / 16 + (args.xshift != 0 ? 1 : 0);
     args.xmap.pad_vec = 0;
-    args.xmap.row_vec = args.xmap.blk_vec + 1;      // one pad vector per row
+    args.xmap.row_vec = kSlab * EB / 16 + 1;
     args.xmap.gstride = 0;
     args.insts = slab_stage_insts(EB);
     // one workgroup per compute unit: the ring takes what the Z and Y tiles leave of ~150 KB
@@ -228,12 +259,10 @@ ks_status_t launch_typed(const Shape& s0, const void* W0, const void* W1, const 
     const int64_t nsplit = (batch + args.rows_per_split - 1) / args.rows_per_split;
     const int64_t blocks = nsplit * args.a;
     if (blocks > 0x7fffffff) return KS_ERR_UNSUPPORTED;
-    return launch_kernel(slab_pair_kernel<TX, TW>, dim3(static_cast<unsigned>(blocks)), dim3(kStreamThreads + 64),
-                         lds, stream, static_cast<const TX*>(X), static_cast<const TW*>(W0), static_cast<const TW*>(W1),
-                         Y, args);
+    auto kernel = vec ? slab_pair_kernel<TX, TW, true> : slab_pair_kernel<TX, TW, false>;
+    return launch_kernel(kernel, dim3(static_cast<unsigned>(blocks)), dim3(kStreamThreads + 64), lds, stream,
+                         static_cast<const TX*>(X), static_cast<const TW*>(W0), static_cast<const TW*>(W1), Y, args);
 }
-
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
 
@@ -249,7 +278,10 @@ ks_status_t launch_slab_pair(const Shape& s0, const Shape& s1, int xt, int wt0, 
                              const void* W1, const void* X, float* Y, int64_t batch, hipStream_t stream,
                              int num_cus) {
     if (!slab_pair_supports(s0, s1, xt, wt0, wt1)) return KS_ERR_UNSUPPORTED;
-    if (!aligned16(X) || !aligned16(Y)) return KS_ERR_UNSUPPORTED;
+    // X and Y aligned to their element size (checked by the caller); rows
+    // are whole 16-byte granules apart, so every row has X's misalignment
+    if ((reinterpret_cast<uintptr_t>(X) % elem_bytes(xt)) != 0 || (reinterpret_cast<uintptr_t>(Y) & 3u) != 0)
+        return KS_ERR_UNSUPPORTED;
     if (xt == kF32 && wt0 == kF32) return launch_typed<float, float>(s0, W0, W1, X, Y, batch, stream, num_cus);
     if (xt == kBF16 && wt0 == kBF16) return launch_typed<bf16_t, bf16_t>(s0, W0, W1, X, Y, batch, stream, num_cus);
     if (xt == kF32 && wt0 == kBF16) return launch_typed<float, bf16_t>(s0, W0, W1, X, Y, batch, stream, num_cus);

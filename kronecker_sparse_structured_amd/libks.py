@@ -309,8 +309,6 @@ def chain_matmul(X, Ws, patterns, out=None, fuse=True, stream=None):
     for i, w in enumerate(Ws):
         _check_tensor(w, "W[%d]" % i)
     dt = dtype_code(X.dtype, Ws[0].dtype)
-    if dt == DTYPE_BF16W:
-        raise TypeError("a chain is all fp32 or bf16 X with bf16 weights")
     batch = X.shape[0]
     last = patterns[-1]
     if out is None:

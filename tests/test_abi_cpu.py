@@ -114,7 +114,8 @@ def test_chain_validation():
     ok = [(1, 4, 2, 4), (4, 2, 2, 2)]
     assert cst(ok, n=0) == libks.KS_ERR_CHAIN_MISMATCH
     assert cst([(1, 4, 2, 4), (4, 2, 3, 2)]) == libks.KS_ERR_CHAIN_MISMATCH
-    assert cst(ok, dtype=libks.DTYPE_BF16W) == libks.KS_ERR_DTYPE
+    assert cst(ok, dtype=7) == libks.KS_ERR_DTYPE
+    assert cst(ok, dtype=libks.DTYPE_BF16W, X=XP + 2) == libks.KS_ERR_ALIGN     # fp32 X, bf16 weights
     assert cst(ok, flags=7) == libks.KS_ERR_INVALID
     assert cst(ok, batch=-2) == libks.KS_ERR_BATCH
     assert cst([(1, 4, 0, 4)]) == libks.KS_ERR_PATTERN
@@ -143,7 +144,9 @@ def test_chain_workspace_sizes():
     assert libks.ks_chain_workspace_size(three, 100, f32, nf) == 2 * 7424
     # bf16 chains keep fp32 intermediates
     assert libks.ks_chain_workspace_size(two, 10, libks.DTYPE_BF16, nf) == 768
-    st_, _ = libks.ks_chain_workspace_size(two, 10, libks.DTYPE_BF16W, nf, check=False)
+    # fp32 X with bf16 weights: the same fp32 intermediates
+    assert libks.ks_chain_workspace_size(two, 10, libks.DTYPE_BF16W, nf) == 768
+    st_, _ = libks.ks_chain_workspace_size(two, 10, 5, nf, check=False)
     assert st_ == libks.KS_ERR_DTYPE
 
 

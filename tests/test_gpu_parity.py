@@ -1,9 +1,10 @@
 """HIP path vs the fp64 oracle, through the C ABI (needs an MI355X).
 
-Small cases are compared on every output; the full-size workloads (the
-sizes and launch configuration the benchmark uses) on sampled rows that the
-oracle recomputes one by one. Every kernel family that supports a pattern is
-run on the same input.
+Every case is compared on every output: the relative Frobenius error over
+all of Y (the oracle streams the rows for the full-size workloads, at the
+sizes and in the launch configuration the benchmark uses), plus, for single
+factors, a per-element error bound (on sampled rows at full size). Every
+kernel family that supports a pattern is run on the same input.
 """
 from __future__ import annotations
 
@@ -226,6 +227,9 @@ def test_nan_propagates_to_its_support():
 
 
 def _factor_workload(name, batch=None, rows=None, kernel="auto"):
+    """One factor of a named workload. With `rows`: the relative Frobenius
+    error over every output (the oracle streams the rows, nothing stored),
+    and the per-element bound on those sampled rows."""
     wl = datagen.get(name)
     if batch is not None:
         wl = datagen.scaled(wl, batch)
@@ -237,7 +241,8 @@ def _factor_workload(name, batch=None, rows=None, kernel="auto"):
     if rows is None:
         return check_factor(p, X, Ws[0], Y.cpu().numpy())
     r = torch.from_numpy(rows).to(DEV)
-    return check_factor(p, X, Ws[0], Y.index_select(0, r).cpu().numpy(), rows=rows)
+    check_factor(p, X, Ws[0], Y.index_select(0, r).cpu().numpy(), rows=rows)
+    return chain_check([p], X, Ws, Y.cpu().numpy(), False)
 
 
 @pytest.mark.parametrize("batch", [1, 197, 1003])
@@ -245,7 +250,9 @@ def test_vit_mlp_small(batch):
     _factor_workload("vit_mlp", batch=batch)
 
 
-def test_vit_mlp_full_size_sampled():
+def test_vit_mlp_full_size():
+    """25,216 rows in the benchmark's launch configuration: every output
+    within the Frobenius bound, sampled rows within the per-element bound."""
     wl = datagen.get("vit_mlp")
     _factor_workload("vit_mlp", rows=sample_rows(wl.batch))
 
@@ -259,11 +266,15 @@ def test_square_sweep_small(p):
 
 
 @pytest.mark.parametrize("p", SWEEP, ids=lambda p: "%d_%d_%d_%d" % p)
-def test_square_sweep_full_size_sampled(p):
+def test_square_sweep_full_size(p):
+    """16,384 rows: every output within the Frobenius bound, sampled rows
+    within the per-element bound."""
     _factor_workload("square_%d_%d_%d_%d" % p, rows=sample_rows(16384, n=24))
 
 
-def _chain_workload(name, bf16, fuse, batch=None, rows=None):
+def _chain_workload(name, bf16, fuse, batch=None):
+    """A named chain against the oracle over every output (relative
+    Frobenius error, the oracle streaming the rows)."""
     wl = datagen.get(name)
     if batch is not None:
         wl = datagen.scaled(wl, batch)
@@ -272,11 +283,9 @@ def _chain_workload(name, bf16, fuse, batch=None, rows=None):
     Wts = [to_dev(W, bf16) for W in Ws]
     Y = libks.chain_matmul(Xt, Wts, wl.patterns, fuse=fuse)
     torch.cuda.synchronize()
-    if rows is None:
-        Yh = Y.cpu().numpy()
-    else:
-        Yh = Y.index_select(0, torch.from_numpy(rows).to(DEV)).cpu().numpy()
-    return chain_check(wl.patterns, X, Ws, Yh, bf16, rows=rows)
+    Yh = Y.cpu().numpy()
+    del Y, Xt, Wts
+    return chain_check(wl.patterns, X, Ws, Yh, bf16)
 
 
 @pytest.mark.parametrize("fuse", [True, False])
@@ -286,8 +295,9 @@ def test_gpt2_chain_small(fuse, batch):
 
 
 @pytest.mark.parametrize("fuse", [True, False])
-def test_gpt2_chain_full_size_sampled(fuse):
-    _chain_workload("gpt2_mlp", False, fuse, rows=sample_rows(16384))
+def test_gpt2_chain_full_size(fuse):
+    """16,384 rows, fused (one launch) and one launch per factor: every output."""
+    _chain_workload("gpt2_mlp", False, fuse)
 
 
 @pytest.mark.parametrize("bf16", [False, True])
@@ -386,6 +396,80 @@ def test_row_chain_unaligned_rows(bf16):
     chain_check(pats, X, Ws, Yo.cpu().numpy(), bf16)
 
 
+def _offset_copy(t: torch.Tensor, elems: int) -> torch.Tensor:
+    """A copy of t whose storage starts `elems` elements past a 16-byte
+    boundary (torch allocations are 256-byte aligned)."""
+    buf = torch.empty(t.numel() + 16, dtype=t.dtype, device=t.device)
+    v = buf[elems:elems + t.numel()].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+def _offset_out(rows: int, cols: int, elems: int) -> torch.Tensor:
+    buf = torch.full((rows * cols + 16,), float("nan"), dtype=torch.float32, device=DEV)
+    return buf[elems:elems + rows * cols].view(rows, cols)
+
+
+# chains whose first group is a fused pair: (patterns, rows, seed)
+FUSED_CHAINS = {
+    "gpt2_pair": ([(1, 64, 16, 64), (64, 8, 8, 8)], 203, 41),
+    "slab_pair_a1": ([(1, 16, 16, 16), (16, 16, 16, 1)], 77, 42),
+    "slab_pair_a3": ([(3, 16, 16, 16), (48, 16, 16, 1)], 45, 43),
+    "butterfly65536": (datagen.get("butterfly65536").patterns, 5, 44),
+}
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("name", sorted(FUSED_CHAINS))
+def test_fused_chain_unaligned_pointers(name, bf16):
+    """The fused pair kernels with X and Y aligned only to their element
+    size: X at every element offset from a 16-byte boundary that a 4-byte
+    (fp32) or 2-byte (bf16) alignment allows, Y at 4 and 8 bytes past one.
+    The plan keeps its fused groups (16-byte alignment only selects vector
+    loads) and every offset matches the oracle."""
+    pats, batch, seed = FUSED_CHAINS[name]
+    wl = datagen.Workload("unaligned", pats, batch, [1.0 / np.sqrt(p[2]) for p in pats], seed)
+    dt = libks.DTYPE_BF16 if bf16 else libks.DTYPE_F32
+    groups = libks.ks_chain_groups(pats, batch, dt)
+    assert any(len(g) == 2 for g in groups), groups
+    X, Ws = datagen.draw(wl)
+    Xd = to_dev(X, bf16)
+    Wts = [to_dev(W, bf16) for W in Ws]
+    n_out = datagen.n_out(pats[-1])
+    ref = None
+    per16 = 8 if bf16 else 4
+    for xo in range(per16):
+        for yo in ([1, 2] if xo % 2 else [0, 3]):
+            Xo = _offset_copy(Xd, xo)
+            Yo = _offset_out(batch, n_out, yo)
+            libks.chain_matmul(Xo, Wts, pats, out=Yo)
+            torch.cuda.synchronize()
+            Yh = Yo.cpu().numpy()
+            chain_check(pats, X, Ws, Yh, bf16)
+            if ref is None:
+                ref = Yh
+            else:
+                # the same kernels and summation order at every offset
+                assert np.array_equal(Yh, ref), (xo, yo)
+
+
+def test_dw_unaligned_pointers():
+    """dK for a pattern the matrix-core kernel takes, with X and dY 4 bytes
+    past a 16-byte boundary: the generic kernel runs over the same row
+    ranges (same workspace) and matches the oracle."""
+    p = (4, 64, 16, 6)
+    a, b, c, d = p
+    batch = 3001
+    rng = np.random.default_rng(71)
+    X = rng.standard_normal((batch, a * c * d), dtype=np.float32)
+    dY = rng.standard_normal((batch, a * b * d), dtype=np.float32)
+    ref = oracle.ks_matmul_dw(p, host_values(dY, False), host_values(X, False))
+    for xo, go in [(1, 0), (0, 3), (2, 1)]:
+        dW = libks.matmul_dw(_offset_copy(to_dev(dY), go), _offset_copy(to_dev(X), xo), p)
+        torch.cuda.synchronize()
+        assert _rel(dW.cpu().numpy(), ref) <= FP32_REL_TOL, (xo, go)
+
+
 def test_hadamard_chain_is_one_launch():
     wl = datagen.get("hadamard16")
     assert libks.ks_chain_groups(wl.patterns, wl.batch, libks.DTYPE_F32) == [[0, 1, 2, 3]]
@@ -409,8 +493,11 @@ def test_butterfly_chain_small(bf16, fuse):
 
 
 @pytest.mark.parametrize("bf16", [False, True])
-def test_butterfly_chain_full_size_sampled(bf16):
-    _chain_workload("butterfly65536", bf16, True, rows=sample_rows(4096, n=12))
+@pytest.mark.parametrize("fuse", [True, False])
+def test_butterfly_chain_full_size(bf16, fuse):
+    """4,096 rows of 65,536, in the benchmark's launch configuration (fused)
+    and one launch per factor: every output."""
+    _chain_workload("butterfly65536", bf16, fuse)
 
 
 @pytest.mark.parametrize("bf16", [False, True])
@@ -554,8 +641,7 @@ def test_backward_edges():
 
 
 def test_backward_vit_full_size():
-    """The ViT factor's gradients at 25,216 rows: dX on sampled rows, dK in
-    full (the oracle sums all rows)."""
+    """The ViT factor's gradients at 25,216 rows: dX and dK in full."""
     wl = datagen.get("vit_mlp")
     p = wl.patterns[0]
     X, Ws = datagen.draw(wl)
@@ -564,9 +650,8 @@ def test_backward_vit_full_size():
     dXg = libks.matmul_dx(to_dev(dY), to_dev(Ws[0]), p)
     dWg = libks.matmul_dw(to_dev(dY), to_dev(X), p)
     torch.cuda.synchronize()
-    rows = sample_rows(wl.batch)
-    ref_dx = oracle.ks_matmul_dx(p, host_values(Ws[0], False), host_values(dY[rows], False))
-    assert _rel(dXg.index_select(0, torch.from_numpy(rows).to(DEV)).cpu().numpy(), ref_dx) <= FP32_REL_TOL
+    ref_dx = oracle.ks_matmul_dx(p, host_values(Ws[0], False), host_values(dY, False))
+    assert _rel(dXg.cpu().numpy(), ref_dx) <= FP32_REL_TOL
     ref_dw = oracle.ks_matmul_dw(p, host_values(dY, False), host_values(X, False))
     assert _rel(dWg.cpu().numpy(), ref_dw) <= FP32_REL_TOL
 
