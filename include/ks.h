@@ -193,6 +193,24 @@ ks_status_t ks_matmul_dw(ks_pattern_t p, const void* dY, const void* X, void* dW
                          ks_dtype_t dt, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * ks_matmul_dw_noalloc: ks_matmul_dw for callers that cannot allocate device
+ * memory -- code under HIP graph capture, tight training loops, harnesses
+ * that forbid hipMalloc. It allocates nothing and takes no workspace: the
+ * partial sums go to a scratch array of KS_DW_SCRATCH_BYTES that libks
+ * keeps on every GPU it runs on until the process ends. Same arguments,
+ * results (bit for bit: the same kernels and summation order) and statuses
+ * as ks_matmul_dw without ws / ws_bytes; KS_ERR_WORKSPACE if the call would
+ * need more scratch than KS_DW_SCRATCH_BYTES (the planner keeps every dK
+ * call's partial sums within it, so this does not happen for valid
+ * arguments). All calls on one GPU share its scratch: calls that overlap in
+ * time on one GPU (several streams or host threads) race and give wrong
+ * results; calls in sequence on one stream are safe.
+ */
+#define KS_DW_SCRATCH_BYTES (64u << 20)
+ks_status_t ks_matmul_dw_noalloc(ks_pattern_t p, const void* dY, const void* X, void* dW, int64_t batch,
+                                 ks_dtype_t dt, hipStream_t stream);
+
+/*
  * ks_chain_workspace_size: bytes of device workspace ks_chain_matmul needs
  * for these arguments (0 if none), written to *bytes.
  *   p, n   the factors in application order (p[0] is applied to X first).

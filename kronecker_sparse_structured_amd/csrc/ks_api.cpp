@@ -227,6 +227,28 @@ ks_status_t matmul_impl(ks_pattern_t p, const void* W, const void* X, void* Y, i
     return run_factor(kernel, f);
 }
 
+// Arguments of ks_matmul_dw and ks_matmul_dw_noalloc other than the
+// workspace: pattern, batch, dtype, pointers, alignment and overlaps of dW
+// with the inputs. Returns the shape and X's element type.
+ks_status_t dw_check(ks_pattern_t p, const void* dY, const void* X, const void* dW, int64_t batch, int dt, Shape* s,
+                     int* xt) {
+    ks_status_t st = shape_of(p, s);
+    if (st != KS_OK) return st;
+    st = check_batch(batch);
+    if (st != KS_OK) return st;
+    int wt = 0;
+    st = factor_types(dt, xt, &wt);
+    if (st != KS_OK) return st;
+    if (!dW) return KS_ERR_NULL;
+    if (batch > 0 && (!dY || !X)) return KS_ERR_NULL;
+    if (!aligned(dW, 4) || (batch > 0 && (!aligned(dY, 4) || !aligned(X, ks::elem_bytes(*xt))))) return KS_ERR_ALIGN;
+    const uint64_t gb = static_cast<uint64_t>(batch) * s->n_out * 4u;
+    const uint64_t xb = static_cast<uint64_t>(batch) * s->n_in * ks::elem_bytes(*xt);
+    const uint64_t wb = static_cast<uint64_t>(s->nnz) * 4u;
+    if (overlap(dW, wb, dY, gb) || overlap(dW, wb, X, xb)) return KS_ERR_OVERLAP;
+    return KS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -330,26 +352,33 @@ ks_status_t ks_matmul_dw_workspace_size(ks_pattern_t p, int64_t batch, ks_dtype_
 ks_status_t ks_matmul_dw(ks_pattern_t p, const void* dY, const void* X, void* dW, int64_t batch,
                          ks_dtype_t dt, void* ws, size_t ws_bytes, hipStream_t stream) {
     Shape s;
-    ks_status_t st = shape_of(p, &s);
+    int xt = 0;
+    ks_status_t st = dw_check(p, dY, X, dW, batch, enum_value(&dt), &s, &xt);
     if (st != KS_OK) return st;
-    st = check_batch(batch);
-    if (st != KS_OK) return st;
-    int xt = 0, wt = 0;
-    st = factor_types(enum_value(&dt), &xt, &wt);
-    if (st != KS_OK) return st;
-    if (!dW) return KS_ERR_NULL;
-    if (batch > 0 && (!dY || !X)) return KS_ERR_NULL;
     const size_t need = ks::dw_workspace_bytes(s, xt, batch);
     if (need > 0 && (!ws || ws_bytes < need)) return KS_ERR_WORKSPACE;
-    if (!aligned(dW, 4) || (batch > 0 && (!aligned(dY, 4) || !aligned(X, ks::elem_bytes(xt)))) ||
-        (need > 0 && !aligned(ws, 16)))
-        return KS_ERR_ALIGN;
+    if (need > 0 && !aligned(ws, 16)) return KS_ERR_ALIGN;
     const uint64_t gb = static_cast<uint64_t>(batch) * s.n_out * 4u;
     const uint64_t xb = static_cast<uint64_t>(batch) * s.n_in * ks::elem_bytes(xt);
     const uint64_t wb = static_cast<uint64_t>(s.nnz) * 4u;
-    if (overlap(dW, wb, dY, gb) || overlap(dW, wb, X, xb) || overlap(dW, wb, ws, need) ||
-        overlap(ws, need, dY, gb) || overlap(ws, need, X, xb))
-        return KS_ERR_OVERLAP;
+    if (overlap(dW, wb, ws, need) || overlap(ws, need, dY, gb) || overlap(ws, need, X, xb)) return KS_ERR_OVERLAP;
+    return ks::launch_dw(s, xt, static_cast<const float*>(dY), X, static_cast<float*>(dW), batch, ws, stream);
+}
+
+ks_status_t ks_matmul_dw_noalloc(ks_pattern_t p, const void* dY, const void* X, void* dW, int64_t batch,
+                                 ks_dtype_t dt, hipStream_t stream) {
+    Shape s;
+    int xt = 0;
+    ks_status_t st = dw_check(p, dY, X, dW, batch, enum_value(&dt), &s, &xt);
+    if (st != KS_OK) return st;
+    const size_t need = ks::dw_workspace_bytes(s, xt, batch);
+    if (need > ks::dw_scratch_bytes()) return KS_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (need > 0) {
+        // this device's copy of the library's scratch array
+        st = ks::dw_scratch(&ws);
+        if (st != KS_OK) return st;
+    }
     return ks::launch_dw(s, xt, static_cast<const float*>(dY), X, static_cast<float*>(dW), batch, ws, stream);
 }
 

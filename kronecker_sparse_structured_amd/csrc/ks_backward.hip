@@ -16,6 +16,8 @@
 
 #include <algorithm>
 #include <cstdio>
+#include <mutex>
+#include <vector>
 
 #include "ks_device.h"
 #include "ks_internal.h"
@@ -357,18 +359,52 @@ bool dw_geom(const Shape& s, int xt, DwGeom* g) {
     return false;
 }
 
+// The partial sums of every row range stay within this many bytes, so one
+// array of this size serves any call as its workspace.
+constexpr int64_t kDwPartialBytes = int64_t(64) << 20;
+static_assert(kDwPartialBytes == KS_DW_SCRATCH_BYTES, "the documented scratch size");
+
 // Row ranges: about 512 workgroups (a fixed target, so that the workspace
 // size is known without asking the device), at most 256 ranges, partial
-// sums within 64 MB.
+// sums within kDwPartialBytes.
 int dw_ranges(const Shape& s, int64_t batch, int64_t tiles, int rows_step, int64_t target = 512) {
     const int64_t steps = (batch + rows_step - 1) / rows_step;
     int64_t r = std::max<int64_t>(1, target / std::max<int64_t>(tiles, 1));
     r = std::min<int64_t>(r, std::min<int64_t>(steps, 256));
-    r = std::min<int64_t>(r, std::max<int64_t>(1, (int64_t(64) << 20) / (s.nnz * 4)));
+    r = std::min<int64_t>(r, std::max<int64_t>(1, kDwPartialBytes / (s.nnz * 4)));
     return static_cast<int>(std::max<int64_t>(1, r));
 }
 
+// Scratch of ks_matmul_dw_noalloc: the dK partial sums of one call, for
+// callers that cannot allocate. One copy per GPU, held until the process
+// ends; calls on one GPU share it (each call writes every partial sum it
+// reads, so nothing needs clearing between calls; calls that overlap in time
+// on one GPU race).
+static __device__ __align__(256) unsigned char scratch[kDwPartialBytes];
+
 }  // namespace
+
+size_t dw_scratch_bytes() { return static_cast<size_t>(kDwPartialBytes); }
+
+// The device address of `scratch` on the current device. In host code the
+// array's name is only a stand-in for the symbol, so kernels get this
+// address instead; it is looked up once per device, with that device
+// current.
+ks_status_t dw_scratch(void** ptr) {
+    static std::mutex mu;
+    static std::vector<void*> addr;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return KS_ERR_HIP;
+    std::lock_guard<std::mutex> lock(mu);
+    if (dev >= static_cast<int>(addr.size())) addr.resize(dev + 1, nullptr);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return KS_ERR_HIP;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return KS_OK;
+}
 
 ks_status_t launch_transpose_blocks(const Shape& s, int wt, const void* W, void* Wt, hipStream_t stream) {
     if (grid_for(s.nnz) == 0) return KS_OK;

@@ -105,5 +105,10 @@ size_t dw_workspace_bytes(const Shape& s, int xt, int64_t batch);
 int dw_describe(const Shape& s, int xt, int64_t batch, char* buf, size_t len);
 ks_status_t launch_dw(const Shape& s, int xt, const float* dY, const void* X, float* dK, int64_t batch, void* ws,
                       hipStream_t stream);
+// The dK partial-sum scratch that ks_matmul_dw_noalloc uses instead of a
+// caller's workspace: its size (every dw_workspace_bytes fits it), and this
+// device's address of it (looked up once per device, on that device).
+size_t dw_scratch_bytes();
+ks_status_t dw_scratch(void** ptr);
 
 }  // namespace ks

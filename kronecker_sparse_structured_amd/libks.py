@@ -114,6 +114,8 @@ def load(path: str = LIB_PATH):
     lib.ks_matmul_dw_workspace_size.restype = i32
     lib.ks_matmul_dw.argtypes = [ks_pattern_t, vp, vp, vp, i64, i32, vp, ctypes.c_size_t, vp]
     lib.ks_matmul_dw.restype = i32
+    lib.ks_matmul_dw_noalloc.argtypes = [ks_pattern_t, vp, vp, vp, i64, i32, vp]
+    lib.ks_matmul_dw_noalloc.restype = i32
     _lib = lib
     return lib
 
@@ -208,6 +210,12 @@ def ks_matmul_dw(p, dY, X, dW, batch: int, dtype: int, ws, ws_bytes: int, stream
     st = load().ks_matmul_dw(_pattern(p), _ptr(dY), _ptr(X), _ptr(dW), int(batch), int(dtype), _ptr(ws),
                              int(ws_bytes), _stream(stream, dW, dY, X))
     return _raise(st, "ks_matmul_dw", check)
+
+
+def ks_matmul_dw_noalloc(p, dY, X, dW, batch: int, dtype: int, stream=None, check: bool = True) -> int:
+    st = load().ks_matmul_dw_noalloc(_pattern(p), _ptr(dY), _ptr(X), _ptr(dW), int(batch), int(dtype),
+                                     _stream(stream, dW, dY, X))
+    return _raise(st, "ks_matmul_dw_noalloc", check)
 
 
 def _patterns(ps: Sequence):

@@ -258,3 +258,28 @@ def test_backward_argument_errors():
     assert need_w > 0
     assert dw(p=big, batch=4096, ws=None, wsb=0) == libks.KS_ERR_WORKSPACE
     assert dw(p=big, batch=4096, ws=WSP, wsb=need_w - 1) == libks.KS_ERR_WORKSPACE
+
+
+def test_dw_noalloc_argument_errors():
+    """The no-allocation dK entry point validates like ks_matmul_dw (no
+    workspace arguments), and every dK call's partial sums fit its scratch."""
+    p = (2, 4, 8, 2)
+    dw = lambda **kw: libks.ks_matmul_dw_noalloc(kw.get("p", p), kw.get("dY", YP), kw.get("X", XP),
+                                                 kw.get("dW", WP), kw.get("batch", 1),
+                                                 kw.get("dt", libks.DTYPE_F32), stream=0, check=False)
+    assert dw(p=(1, 1, 1, 0)) == libks.KS_ERR_PATTERN
+    assert dw(batch=-1) == libks.KS_ERR_BATCH
+    assert dw(dt=5) == libks.KS_ERR_DTYPE
+    assert dw(dW=None) == libks.KS_ERR_NULL
+    assert dw(X=None) == libks.KS_ERR_NULL
+    assert dw(dW=WP + 1) == libks.KS_ERR_ALIGN
+    assert dw(X=XP + 2) == libks.KS_ERR_ALIGN
+    assert dw(dW=XP) == libks.KS_ERR_OVERLAP
+    scratch = 64 << 20   # KS_DW_SCRATCH_BYTES
+    header = open(HEADER).read()
+    assert re.search(r"#define KS_DW_SCRATCH_BYTES \(64u << 20\)", header)
+    for q in [(4, 64, 16, 6), (64, 8, 8, 8), (1, 128, 128, 32), (3, 5, 7, 2), (4096, 16, 16, 1),
+              (1, 16, 16, 4096), (2, 128, 128, 4), (1, 4, 4, 64)]:
+        for batch in (1, 333, 4096, 25216, 1 << 20, (1 << 31) - 1):
+            for dt in (libks.DTYPE_F32, libks.DTYPE_BF16):
+                assert libks.ks_matmul_dw_workspace_size(q, batch, dt) <= scratch, (q, batch, dt)
