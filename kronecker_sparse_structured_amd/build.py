@@ -1,9 +1,11 @@
 """Build libks.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
 
-    python -m kronecker_sparse_structured_amd.build
+    python -m kronecker_sparse_structured_amd.build [--incremental]
 
 Every source in csrc/ is compiled to an object in parallel, then linked into
-kronecker_sparse_structured_amd/lib/libks.so. The build always recompiles.
+kronecker_sparse_structured_amd/lib/libks.so. The build always recompiles
+everything, unless --incremental is given: then only sources whose object is
+older than the source or any header are recompiled.
 """
 from __future__ import annotations
 
@@ -62,12 +64,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int | None = None) -> str:
+def _stale(src: str) -> bool:
+    """The object is missing or older than its source or any header."""
+    obj = os.path.join(OBJ, os.path.basename(src) + ".o")
+    if not os.path.exists(obj):
+        return True
+    headers = [os.path.join(d, f) for d in (CSRC, INCLUDE) for f in os.listdir(d) if f.endswith(".h")]
+    newest = max(os.path.getmtime(p) for p in [src, *headers])
+    return os.path.getmtime(obj) < newest
+
+
+def build(jobs: int | None = None, incremental: bool = False) -> str:
+    """Compile every source (or, with incremental=True, only those whose
+    object is older than the source or a header) and link libks.so."""
     os.makedirs(OBJ, exist_ok=True)
     srcs = sources()
-    jobs = jobs or min(len(srcs), max(1, os.cpu_count() or 1), 16)
+    todo = [s for s in srcs if _stale(s)] if incremental else srcs
+    jobs = jobs or min(max(len(todo), 1), max(1, os.cpu_count() or 1), 16)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
+        list(ex.map(_compile, todo))
+    objs = [os.path.join(OBJ, os.path.basename(s) + ".o") for s in srcs]
     os.makedirs(os.path.dirname(LIB), exist_ok=True)
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
@@ -78,5 +94,5 @@ def build(jobs: int | None = None) -> str:
 
 if __name__ == "__main__":
     t0 = time.time()
-    print(build())
+    print(build(incremental="--incremental" in sys.argv[1:]))
     print("built in %.1fs" % (time.time() - t0))

@@ -6,6 +6,7 @@
 // (KS abstract page, taxoreview.com "dblp:303/4794", first paragraph); see
 // include/ks.h for the layouts.
 
+#include <algorithm>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -131,7 +132,8 @@ struct ChainPlan {
     std::vector<int> group_start;  // first factor of each launch group
     std::vector<int> group_len;    // factors in the group (one launch)
     std::vector<int> group_kind;   // 0 single factor, 1 row-fused pair, 2 slab-fused pair,
-                                   // 3 run of factors with rows resident in LDS
+                                   // 3 run of factors with rows resident in LDS,
+                                   // 4 strided pair (16-byte aligned input and output only)
     int xt0 = ks::kF32, wt = ks::kF32;
     int64_t max_mid = 0;           // widest intermediate between groups
     int nbuf = 0;                  // workspace buffers (0, 1 or 2)
@@ -163,6 +165,9 @@ ks_status_t plan_chain(const ks_pattern_t* p, int n, int64_t batch, int dt,
             } else if (ks::slab_pair_supports(plan->shapes[k], plan->shapes[k + 1], xt, plan->wt, plan->wt)) {
                 len = 2;
                 kind = 2;
+            } else if (ks::strided_pair_supports(plan->shapes[k], plan->shapes[k + 1], xt, plan->wt, plan->wt)) {
+                len = 2;
+                kind = 4;
             } else {
                 // the longest run from k whose rows fit on chip
                 for (int m = n - k; m >= 2; --m) {
@@ -185,6 +190,16 @@ ks_status_t plan_chain(const ks_pattern_t* p, int n, int64_t batch, int dt,
         if (last.n_out > plan->max_mid) plan->max_mid = last.n_out;
     }
     plan->nbuf = groups <= 1 ? 0 : (groups == 2 ? 1 : 2);
+    // A strided pair that reads X or writes Y needs both 16-byte aligned;
+    // otherwise it runs as its two factors, through a buffer that is neither
+    // its input nor its output. The workspace does not depend on the
+    // pointers, so it always has room for that.
+    for (int g = 0; g < groups; ++g) {
+        if (plan->group_kind[g] != 4 || (g != 0 && g != groups - 1)) continue;
+        const Shape& first = plan->shapes[plan->group_start[g]];
+        if (first.n_out > plan->max_mid) plan->max_mid = first.n_out;
+        plan->nbuf = std::max(plan->nbuf, groups == 1 ? 1 : 2);
+    }
     const uint64_t raw = static_cast<uint64_t>(batch) * static_cast<uint64_t>(plan->max_mid) * 4u;
     plan->buf_bytes = static_cast<size_t>((raw + 255u) / 256u * 256u);
     return KS_OK;
@@ -452,6 +467,26 @@ ks_status_t ks_chain_matmul(const ks_pattern_t* p, int n, const void* const* W,
         } else if (plan.group_kind[g] == 3) {
             st = ks::launch_row_chain(&plan.shapes[k], plan.group_len[g], cur_t, plan.wt, W + k, cur, out, batch,
                                       stream);
+        } else if (plan.group_kind[g] == 4 && ks::strided_pair_aligned(cur, out)) {
+            st = ks::launch_strided_pair(plan.shapes[k], plan.shapes[k + 1], cur_t, plan.wt, plan.wt, W[k], W[k + 1],
+                                         cur, out, batch, stream, cus);
+        } else if (plan.group_kind[g] == 4) {
+            // X or Y not 16-byte aligned: the two factors one at a time,
+            // through the buffer that is neither this group's input nor output
+            float* mid = reinterpret_cast<float*>(
+                (cur == bufs[0] || out == reinterpret_cast<float*>(bufs[0])) ? bufs[1] : bufs[0]);
+            // only the first or last group can see an unaligned pointer, and
+            // the plan keeps a spare buffer for it
+            if (plan.nbuf == 0 || static_cast<const void*>(mid) == cur || mid == out) return KS_ERR_UNSUPPORTED;
+            ks::FactorCall f;
+            f.s = plan.shapes[k]; f.xt = cur_t; f.wt = plan.wt; f.W = W[k]; f.X = cur; f.Y = mid;
+            f.batch = batch; f.stream = stream; f.num_cus = cus; f.rows_per_block = 0;
+            f.store_waves = KS_STORE_AUTO;
+            st = run_factor(KS_KERNEL_AUTO, f);
+            if (st == KS_OK) {
+                f.s = plan.shapes[k + 1]; f.xt = ks::kF32; f.W = W[k + 1]; f.X = mid; f.Y = out;
+                st = run_factor(KS_KERNEL_AUTO, f);
+            }
         } else {
             ks::FactorCall f;
             f.s = plan.shapes[k]; f.xt = cur_t; f.wt = plan.wt; f.W = W[k]; f.X = cur; f.Y = out;

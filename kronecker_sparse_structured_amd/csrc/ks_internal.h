@@ -91,6 +91,16 @@ ks_status_t launch_slab_pair(const Shape& s0, const Shape& s1, int xt, int wt0, 
                              const void* W0, const void* W1, const void* X, float* Y,
                              int64_t batch, hipStream_t stream, int num_cus);
 
+// Fused pair of butterfly-type factors F = (a, 16, 16, 16 e) then
+// G = (16 a, 16, 16, e), e a multiple of 4 (ks_pair.hip): closed groups of 256
+// values e apart. fp32 X only; X and Y must be 16-byte aligned
+// (strided_pair_aligned), else the launcher returns KS_ERR_UNSUPPORTED.
+bool strided_pair_supports(const Shape& s0, const Shape& s1, int xt, int wt0, int wt1);
+bool strided_pair_aligned(const void* X, const void* Y);
+ks_status_t launch_strided_pair(const Shape& s0, const Shape& s1, int xt, int wt0, int wt1, const void* W0,
+                                const void* W1, const void* X, float* Y, int64_t batch, hipStream_t stream,
+                                int num_cus);
+
 // A run of factors with whole rows resident in LDS (ks_rowchain.hip): n >= 2
 // factors of small blocks whose widest row fits on chip. s, W: n entries.
 bool row_chain_supports(const Shape* s, int n, int xt, int wt);

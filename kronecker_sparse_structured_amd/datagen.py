@@ -124,6 +124,10 @@ def workloads() -> dict:
     w["radix8_n4096"] = Workload("radix8_n4096", [(8 ** k, 8, 8, 8 ** (3 - k)) for k in range(4)], 16384,
                                  [1.0 / np.sqrt(8.0)] * 4, 8,
                                  note="radix-8 butterfly, four factors at n = 4096")
+    # a radix-16 pair the strided-pair kernel fuses (e = 4): (64, 16, 16, 64)
+    # then (1024, 16, 16, 4) at n = 65,536 (not a configuration of the pages)
+    w["strided_pair_e4"] = Workload("strided_pair_e4", [(64, 16, 16, 64), (1024, 16, 16, 4)], 4096, [0.25] * 2, 9,
+                                    note="two radix-16 factors four elements apart, n = 65,536")
     for p_idx, p in enumerate(square_sweep_patterns()):
         name = "square_%d_%d_%d_%d" % p
         w[name] = Workload(name, [p], 16384, [1.0 / np.sqrt(p[2])], 3000 + p_idx,

@@ -185,15 +185,30 @@ def test_chain_plan_row_resident_runs():
 
 
 def test_chain_plan_fuses_known_pairs():
-    """The planner fuses the GPT-2 pair (rows shared by groups of beta0) and
-    the butterfly's last two factors (the second works inside the first's
-    output slabs); nothing else in those chains, and nothing with NO_FUSE."""
+    """The planner fuses the GPT-2 pair (rows shared by groups of beta0), the
+    butterfly's last two factors (the second works inside the first's output
+    slabs) and, for fp32 rows, a factor with the next one of the strided
+    family (a, 16, 16, 16 e) -> (16 a, 16, 16, e); nothing with NO_FUSE."""
     gpt2 = [(1, 64, 16, 64), (64, 8, 8, 8)]
     bfly = [(16 ** k, 16, 16, 16 ** (3 - k)) for k in range(4)]
     for dt in (libks.DTYPE_F32, libks.DTYPE_BF16):
         assert libks.ks_chain_groups(gpt2, 1000, dt) == [[0, 1]]
-        assert libks.ks_chain_groups(bfly, 1000, dt) == [[0], [1], [2, 3]]
         assert libks.ks_chain_groups(bfly, 1000, dt, libks.CHAIN_NO_FUSE) == [[0], [1], [2], [3]]
+    # the 65,536-point butterfly: e = 256 and 16 between its first three
+    # factors, too far apart for the strided pair
+    for dt in (libks.DTYPE_F32, libks.DTYPE_BF16, libks.DTYPE_BF16W):
+        assert libks.ks_chain_groups(bfly, 1000, dt) == [[0], [1], [2, 3]]
+    # strided family: e = 4 or 8; fp32 rows; the spare buffer for unaligned X or Y
+    for e in (4, 8):
+        pair = [(2, 16, 16, 16 * e), (32, 16, 16, e)]
+        assert libks.ks_chain_groups(pair, 7, libks.DTYPE_F32) == [[0, 1]]
+        assert libks.ks_chain_groups(pair, 7, libks.DTYPE_BF16W) == [[0, 1]]
+        assert libks.ks_chain_groups(pair, 7, libks.DTYPE_BF16) == [[0], [1]]
+        assert libks.ks_chain_workspace_size(pair, 7, libks.DTYPE_F32) == (7 * 512 * e * 4 + 255) // 256 * 256
+    assert libks.ks_chain_groups([(2, 16, 16, 256), (32, 16, 16, 16)], 7, libks.DTYPE_F32) == [[0], [1]]
+    assert libks.ks_chain_groups([(2, 16, 16, 32), (32, 16, 16, 2)], 7, libks.DTYPE_F32) == [[0], [1]]
+    assert libks.ks_chain_groups([(2, 16, 16, 64), (32, 8, 16, 4)], 7, libks.DTYPE_F32) == [[0], [1]]
+    assert libks.ks_chain_workspace_size(bfly, 100, libks.DTYPE_F32) == 2 * 100 * 65536 * 4
     # slab family: (a, 16, 16, 16) -> (16 a, 16, 16, 1) for any a; other shapes stay apart
     assert libks.ks_chain_groups([(3, 16, 16, 16), (48, 16, 16, 1)], 7, libks.DTYPE_F32) == [[0, 1]]
     assert libks.ks_chain_groups([(4, 16, 16, 16), (64, 16, 8, 2)], 7, libks.DTYPE_F32) == [[0], [1]]

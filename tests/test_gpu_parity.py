@@ -343,6 +343,33 @@ def test_slab_pair_shapes(a, lead, bf16):
     chain_check(wl.patterns, X, Ws, Y.cpu().numpy(), bf16)
 
 
+@pytest.mark.parametrize("bf16w", [False, True])
+@pytest.mark.parametrize("lead", [False, True])
+@pytest.mark.parametrize("ae", [(1, 4), (2, 8), (3, 4), (64, 4), (5, 8)], ids=lambda v: "a%d_e%d" % v)
+def test_strided_pair_shapes(ae, lead, bf16w):
+    """The one-launch pair (a, 16, 16, 16 e) -> (16 a, 16, 16, e) (closed
+    groups of 256 values e apart; e <= 8) on ragged row counts, with fp32 or
+    bf16 weights (fp32 X); behind a leading factor the pair reads the
+    workspace."""
+    a, e = ae
+    pats = [(a, 16, 16, 16 * e), (16 * a, 16, 16, e)]
+    if lead:
+        pats = [(a * 16 * e, 4, 4, 4)] + pats
+    batch = 37 if a >= 64 else 203
+    wl = datagen.Workload("strided", pats, batch, [1.0 / np.sqrt(p[2]) for p in pats], 60 + a + e)
+    dt = libks.DTYPE_BF16W if bf16w else libks.DTYPE_F32
+    groups = libks.ks_chain_groups(wl.patterns, wl.batch, dt)
+    assert [len(g) for g in groups] == ([1, 2] if lead else [2]), groups
+    X, Ws = datagen.draw(wl)
+    Wts = [to_dev(W, bf16w) for W in Ws]
+    Y = libks.chain_matmul(to_dev(X), Wts, wl.patterns)
+    torch.cuda.synchronize()
+    Xd = host_values(X, False)
+    Wd = [host_values(W, bf16w) for W in Ws]
+    se, sr, ma = oracle.ks_chain_err(wl.patterns, Wd, Xd, Y.cpu().numpy())
+    assert np.sqrt(se / sr) <= FP32_REL_TOL, (np.sqrt(se / sr), ma)
+
+
 def _radix(r, L):
     """Factors (r^k, r, r, r^(L-1-k)), k = 0..L-1: a radix-r butterfly on n = r^L."""
     return [(r ** k, r, r, r ** (L - 1 - k)) for k in range(L)]
@@ -416,6 +443,7 @@ FUSED_CHAINS = {
     "slab_pair_a1": ([(1, 16, 16, 16), (16, 16, 16, 1)], 77, 42),
     "slab_pair_a3": ([(3, 16, 16, 16), (48, 16, 16, 1)], 45, 43),
     "butterfly65536": (datagen.get("butterfly65536").patterns, 5, 44),
+    "strided_pair_a2_e8": ([(2, 16, 16, 128), (32, 16, 16, 8)], 45, 45),
 }
 
 
@@ -428,6 +456,8 @@ def test_fused_chain_unaligned_pointers(name, bf16):
     The plan keeps its fused groups (16-byte alignment only selects vector
     loads) and every offset matches the oracle."""
     pats, batch, seed = FUSED_CHAINS[name]
+    if bf16 and name.startswith("strided"):
+        pytest.skip("the strided pair reads fp32 X; a bf16 chain runs these factors one at a time")
     wl = datagen.Workload("unaligned", pats, batch, [1.0 / np.sqrt(p[2]) for p in pats], seed)
     dt = libks.DTYPE_BF16 if bf16 else libks.DTYPE_F32
     groups = libks.ks_chain_groups(pats, batch, dt)
