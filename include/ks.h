@@ -88,7 +88,10 @@ typedef enum ks_kernel_t {
     KS_KERNEL_GENERIC = 1,  /* one thread per output, any pattern                */
     KS_KERNEL_VALU = 2,     /* weights in registers, fp32 FMA (b, c <= 16)       */
     KS_KERNEL_MFMA = 3,     /* matrix cores (b, c >= 16), LDS-staged tiles       */
-    KS_KERNEL_MFMA_LDS = 4  /* same kernels as KS_KERNEL_MFMA (kept for ABI)     */
+    KS_KERNEL_MFMA_LDS = 4, /* same kernels as KS_KERNEL_MFMA (kept for ABI)     */
+    KS_KERNEL_COLUMN = 5    /* matrix cores, output computed in place in the
+                               staged X tile: b = c in {16, 32}, d a multiple
+                               of 32 (b = 16) or 16 (b = 32), fp32 X           */
 } ks_kernel_t;
 
 /* Who stores Y in the MFMA kernels, for ks_options_t.store_waves. */

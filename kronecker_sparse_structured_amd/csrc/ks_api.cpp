@@ -68,7 +68,7 @@ bool overlap(const void* p, uint64_t pb, const void* q, uint64_t qb) {
 
 ks_status_t check_options(const ks_options_t* opt) {
     if (!opt) return KS_OK;
-    if (opt->kernel < KS_KERNEL_AUTO || opt->kernel > KS_KERNEL_MFMA_LDS) return KS_ERR_INVALID;
+    if (opt->kernel < KS_KERNEL_AUTO || opt->kernel > KS_KERNEL_COLUMN) return KS_ERR_INVALID;
     if (opt->rows_per_block < 0 || opt->rows_per_block > 4096) return KS_ERR_INVALID;
     if (opt->store_waves < KS_STORE_AUTO || opt->store_waves > KS_STORE_DEDICATED) return KS_ERR_INVALID;
     for (int i = 0; i < 5; ++i)
@@ -100,6 +100,7 @@ ks_status_t current_cus(int* cus) {
 // the blocks fill 16 x 16 tiles (measured faster than the VALU kernel from
 // b = c = 16 up), else the VALU kernel, else the generic one.
 int choose_kernel(const Shape& s, int xt, int wt) {
+    if (ks::col_preferred(s, xt, wt)) return KS_KERNEL_COLUMN;
     if (ks::mfma_supports(s, xt, wt)) return KS_KERNEL_MFMA;
     if (ks::valu_supports(s, xt, wt)) return KS_KERNEL_VALU;
     return KS_KERNEL_GENERIC;
@@ -111,6 +112,7 @@ ks_status_t launch_family(int kernel, const ks::FactorCall& f) {
         case KS_KERNEL_VALU: return ks::launch_valu(f);
         case KS_KERNEL_MFMA: return ks::launch_mfma(f);
         case KS_KERNEL_MFMA_LDS: return ks::launch_mfma_lds(f);
+        case KS_KERNEL_COLUMN: return ks::launch_col(f);
         default: return KS_ERR_INVALID;
     }
 }
@@ -231,6 +233,7 @@ ks_status_t matmul_impl(ks_pattern_t p, const void* W, const void* X, void* Y, i
     if (kernel == KS_KERNEL_VALU && !ks::valu_supports(s, xt, wt)) return KS_ERR_UNSUPPORTED;
     if (kernel == KS_KERNEL_MFMA && !ks::mfma_supports(s, xt, wt)) return KS_ERR_UNSUPPORTED;
     if (kernel == KS_KERNEL_MFMA_LDS && !ks::mfma_lds_supports(s, xt, wt)) return KS_ERR_UNSUPPORTED;
+    if (kernel == KS_KERNEL_COLUMN && !ks::col_supports(s, xt, wt)) return KS_ERR_UNSUPPORTED;
 
     ks::FactorCall f;
     f.s = s; f.xt = xt; f.wt = wt; f.W = W; f.X = X; f.Y = static_cast<float*>(Y);
@@ -513,7 +516,8 @@ ks_status_t ks_plan_describe(ks_pattern_t p, int64_t batch, ks_dtype_t dt, char*
     if (st != KS_OK) return st;
     const int kernel = choose_kernel(s, xt, wt);
     const int cus = 256;  // description only; launches use the device's count
-    if (kernel == KS_KERNEL_VALU) ks::valu_describe(s, xt, wt, batch, cus, buf, len);
+    if (kernel == KS_KERNEL_COLUMN) ks::col_describe(s, xt, wt, batch, cus, buf, len);
+    else if (kernel == KS_KERNEL_VALU) ks::valu_describe(s, xt, wt, batch, cus, buf, len);
     else if (kernel == KS_KERNEL_MFMA) ks::mfma_describe(s, xt, wt, batch, cus, buf, len);
     else std::snprintf(buf, len, "generic: one thread per output");
     return KS_OK;

@@ -67,6 +67,12 @@ ks_status_t launch_valu(const FactorCall& f);
 ks_status_t launch_mfma(const FactorCall& f);
 ks_status_t launch_mfma_lds(const FactorCall& f);   // the same kernels
 
+// In-place column tiles for b = c in {16, 32} (ks_col.hip; fp32 X).
+ks_status_t launch_col(const FactorCall& f);
+bool col_supports(const Shape& s, int xt, int wt);
+bool col_preferred(const Shape& s, int xt, int wt);   // the planner's choice
+int col_describe(const Shape& s, int xt, int wt, int64_t batch, int num_cus, char* buf, size_t len);
+
 // Whether a family can run a factor (pure host; no HIP call).
 bool valu_supports(const Shape& s, int xt, int wt);
 bool mfma_supports(const Shape& s, int xt, int wt);

@@ -23,9 +23,9 @@ LIB_PATH = os.path.join(_PKG, "lib", "libks.so")
 # ks_dtype_t
 DTYPE_F32, DTYPE_BF16, DTYPE_BF16W = 0, 1, 2
 # ks_kernel_t
-KERNEL_AUTO, KERNEL_GENERIC, KERNEL_VALU, KERNEL_MFMA, KERNEL_MFMA_LDS = 0, 1, 2, 3, 4
+KERNEL_AUTO, KERNEL_GENERIC, KERNEL_VALU, KERNEL_MFMA, KERNEL_MFMA_LDS, KERNEL_COLUMN = 0, 1, 2, 3, 4, 5
 KERNELS = {"auto": KERNEL_AUTO, "generic": KERNEL_GENERIC, "valu": KERNEL_VALU, "mfma": KERNEL_MFMA,
-           "mfma_lds": KERNEL_MFMA_LDS}
+           "mfma_lds": KERNEL_MFMA_LDS, "col": KERNEL_COLUMN}
 # ks_store_waves_t
 STORE_AUTO, STORE_COMPUTE, STORE_DEDICATED = 0, 1, 2
 STORE_WAVES = {"auto": STORE_AUTO, "compute": STORE_COMPUTE, "dedicated": STORE_DEDICATED}

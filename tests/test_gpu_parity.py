@@ -38,7 +38,7 @@ def try_family(p, Xt, Wt, kernel):
     return Y
 
 
-ALL_FAMILIES = ["auto", "generic", "valu", "mfma", "mfma_lds"]
+ALL_FAMILIES = ["auto", "generic", "valu", "mfma", "mfma_lds", "col"]
 
 # ---------------------------------------------------------------- small workloads
 
@@ -132,6 +132,26 @@ def test_bf16_and_mixed_inputs(p):
                 continue
             torch.cuda.synchronize()
             check_factor(p, X, W, Y.cpu().numpy(), bf16=xb, w_bf16=wb)
+
+
+COL_PATTERNS = [(1, 16, 16, 64), (3, 16, 16, 32), (5, 16, 16, 96), (2, 32, 32, 16), (1, 32, 32, 48),
+                (1, 16, 16, 4096), (16, 16, 16, 256), (1, 32, 32, 128)]
+
+
+@pytest.mark.parametrize("p", COL_PATTERNS, ids=lambda p: "%d_%d_%d_%d" % p)
+@pytest.mark.parametrize("batch", [1, 17, 131])
+def test_column_kernel(p, batch):
+    """The in-place column kernel (b = c in {16, 32}, fp32 X) on ragged row
+    counts, fp32 and bf16 weights: every output against the oracle and
+    within the per-element bound; equal to the tiled matrix-core kernel to
+    fp32 rounding."""
+    for wb in (False, True):
+        X, W = datagen.random_pattern_inputs(p, batch, seed=sum(p) + batch)
+        Xt, Wt = to_dev(X), to_dev(W, wb)
+        Y = try_family(p, Xt, Wt, "col")
+        assert Y is not None, "the column kernel refused %s" % (p,)
+        torch.cuda.synchronize()
+        check_factor(p, X, W, Y.cpu().numpy(), w_bf16=wb)
 
 
 # ---------------------------------------------------------------- edges
