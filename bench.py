@@ -53,21 +53,31 @@ METRIC = "KS matmul achieved GB/s & TFLOP/s as % of roofline, fp32, 1×MI355X"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
-# Kernel sources that the counted workloads (the ViT factor, the GPT-2 pair,
-# the butterfly chain) never run: the gradient kernels and the row-resident
-# chain kernel. Editing them does not invalidate those workloads' traffic
-# counters.
-_NOT_COUNTED = ("ks_backward.hip", "ks_rowchain.hip")
+# Kernel sources each counted workload runs, beside the C ABI (ks_api.cpp)
+# and the headers: its traffic counters stay valid while these are unchanged.
+# Workloads not listed are keyed on every source.
+WORKLOAD_SOURCES = {
+    "butterfly65536": ("ks_mfma.hip", "ks_slab.hip"),
+    "vit_mlp": ("ks_mfma.hip",),
+    "gpt2_mlp": ("ks_fused.hip",),
+    "gpt2_mlp:nofuse": ("ks_mfma.hip", "ks_valu.hip"),
+}
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
+def kernel_source_hash(workload: str = "", no_fuse: bool = False) -> str:
     csrc = os.path.join(ROOT, "kronecker_sparse_structured_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".cpp", ".h")) and name not in _NOT_COUNTED:
+    names = sorted(os.listdir(csrc))
+    used = WORKLOAD_SOURCES.get(workload + (":nofuse" if no_fuse else ""), WORKLOAD_SOURCES.get(workload))
+    if used is not None:
+        names = [n for n in names if n.endswith(".h") or n == "ks_api.cpp" or n in used]
+    h = hashlib.sha256()
+    for name in names:
+        if name.endswith((".hip", ".cpp", ".h")):
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode())
                 h.update(f.read())
+    with open(os.path.join(ROOT, "include", "ks.h"), "rb") as f:
+        h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -171,7 +181,7 @@ def ingest_counters(args) -> int:
     out["group_bytes"] = [int(f + w) for f, w in zip(per_group["FETCH_SIZE"], per_group["WRITE_SIZE"])]
     out["bytes_per_step"] = int(sum(out["group_bytes"]))
     out["launches_per_step"] = per_step
-    out["source_hash"] = kernel_source_hash()
+    out["source_hash"] = kernel_source_hash(args.workload, args.no_fuse)
     db[key] = out
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(db, f, indent=1, sort_keys=True)
@@ -349,7 +359,8 @@ def main():
     if os.path.exists(TRAFFIC_FILE) and dom is not None:
         try:
             rec = json.load(open(TRAFFIC_FILE)).get(traffic_key(args))
-            if rec and rec.get("source_hash") == kernel_source_hash() and len(rec.get("group_bytes", [])) > dom:
+            if (rec and rec.get("source_hash") == kernel_source_hash(args.workload, args.no_fuse)
+                    and len(rec.get("group_bytes", [])) > dom):
                 traffic = rec["group_bytes"][dom]
         except (ValueError, OSError):
             traffic = None
