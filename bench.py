@@ -109,6 +109,15 @@ def parse():
     ap.add_argument("--backward", action="store_true",
                     help="time the gradients (ks_matmul_dx, ks_matmul_dw) of every factor of the "
                          "workload and print one JSON line; not the contract run")
+    ap.add_argument("--families", action="store_true",
+                    help="with --sweep: also time every kernel family (and store schedule) that runs each "
+                         "pattern and report the fastest (the data the planner's table is fitted on)")
+    ap.add_argument("--comparator-only", action="store_true",
+                    help="run only the permute / batched GEMM / permute comparator on a single-factor "
+                         "workload (for rocprofv3 counters); one JSON line")
+    ap.add_argument("--ingest-comparator", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="HBM bytes per call of the comparator from two --comparator-only counter runs "
+                         "(same --steps / --warmup)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of a "
                          "`--calib-copy` run into profiles/traffic_counters.json and exit")
@@ -215,6 +224,8 @@ def main():
     args = parse()
     if args.ingest_counters:
         return ingest_counters(args)
+    if args.ingest_comparator:
+        return ingest_comparator_counters(args)
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(rows would shard across GPUs with no exchange); run with --gpus 1.",
@@ -222,6 +233,8 @@ def main():
         return 2
     if args.sweep:
         return sweep(args)
+    if args.comparator_only:
+        return comparator_only(args)
     if args.backward:
         return backward(args)
     if args.energy:
@@ -739,6 +752,10 @@ def sweep(args) -> int:
                "plan": libks.ks_plan_describe(p, batch, dt)}
         if args.comparator and not bf16:
             row.update(comparator(p, batch, Xt, Wt, Yt, nset, ms, stream, torch))
+        if args.families:
+            row["families"] = time_families(p, batch, Wt, Xt, Yt, nset, dt, lib, sp, stream, torch, libks)
+            best = min(row["families"], key=lambda f: f["ms"])
+            row["best"] = {"kernel": best["kernel"], "store_waves": best["store_waves"]}
         rows.append(row)
         print("%-18s %9.1f us %8.1f GB/s %7.2f TFLOP/s  %s  roofline %.3f   %s" % (
             str(tuple(p)), ms * 1e3, row["GB/s"], row["TFLOP/s"], bound, row["roofline_frac"],
@@ -756,6 +773,121 @@ def sweep(args) -> int:
                       "roofline_frac_median": round(float(np.median(fr)), 4),
                       "roofline_frac_min": round(float(np.min(fr)), 4),
                       "roofline_frac_max": round(float(np.max(fr)), 4), "rows": rows}), flush=True)
+    return 0
+
+
+# Kernel families (and store schedules of the matrix-core family) timed per
+# pattern by --sweep --families: (name, ks_kernel_t, ks_store_waves_t).
+FAMILY_VARIANTS = [("mfma/compute", 3, 1), ("mfma/dedicated", 3, 2), ("valu", 2, 0), ("col", 5, 0)]
+
+
+def time_families(p, batch, Wt, Xt, Yt, nset, dt, lib, sp, stream, torch, libks):
+    """Every family that runs pattern p, each timed like the sweep's
+    automatic choice (back-to-back launches over the rotated sets after
+    warm-up, HIP events); families that refuse the pattern are skipped."""
+    out = []
+    pat = libks.ks_pattern_t(*p)
+    for name, kernel, store in FAMILY_VARIANTS:
+        opt = libks.ks_options_t()
+        opt.kernel = kernel
+        opt.store_waves = store
+        calls = [(pat, ctypes.c_void_p(Wt.data_ptr()), ctypes.c_void_p(Xt[k].data_ptr()),
+                  ctypes.c_void_p(Yt[k].data_ptr()), batch, dt, sp, ctypes.byref(opt)) for k in range(nset)]
+        st = lib.ks_matmul_ex(*calls[0])
+        if st == libks.KS_ERR_UNSUPPORTED:
+            continue
+        if st != 0:
+            raise libks.KSError(st, "sweep family %s %s" % (name, p))
+        warm_up(lambda i: lib.ks_matmul_ex(*calls[i % nset]), 5, torch)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(30):
+            lib.ks_matmul_ex(*calls[i % nset])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append({"name": name, "kernel": kernel, "store_waves": store, "ms": round(e0.elapsed_time(e1) / 30, 5)})
+    return out
+
+
+def comparator_only(args) -> int:
+    """The permute / batched GEMM / permute comparator alone on a
+    single-factor workload (W + K steps over rotated sets, then, with
+    --calib-copy, the calibration copies), for counting its HBM traffic
+    under rocprofv3 --pmc; prints one JSON line with its time per call."""
+    import numpy as np
+    import torch
+    from kronecker_sparse_structured_amd import datagen
+
+    dev = torch.device("cuda:0")
+    wl = datagen.get(args.workload)
+    p = wl.patterns[0]
+    X, Ws = datagen.draw(wl)
+    batch = wl.batch
+    nbytes = factor_bytes(p, 4, 4, batch)
+    nset = max(2, int(np.ceil(CACHE_BYTES / nbytes)) + 1)
+    Xt = [torch.from_numpy(X).to(dev)]
+    for _ in range(nset - 1):
+        Xt.append(Xt[0].clone())
+    Wt = torch.from_numpy(Ws[0]).to(dev)
+    Yt = [torch.empty((batch, datagen.n_out(p)), dtype=torch.float32, device=dev) for _ in range(nset)]
+    run = comparator_fn(p, batch, Xt, Wt, Yt, torch)
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        run(i % nset)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        run(i % nset)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    if args.calib_copy:
+        src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+    print(json.dumps({"comparator": "permute / torch.bmm / permute", "workload": wl.name, "pattern": list(p),
+                      "calls": args.warmup + args.steps, "ms": round(ms, 5),
+                      "bytes_fused_algorithmic": nbytes}), flush=True)
+    return 0
+
+
+def ingest_comparator_counters(args) -> int:
+    """HBM bytes per call of the comparator from the two counter runs of
+    --comparator-only: every dispatch except device copies (the input
+    replication and the calibration copies) and fills, each counter scaled
+    by its reading on the calibration copy, divided by the calls."""
+    import csv
+    from collections import defaultdict
+    from kronecker_sparse_structured_amd import datagen
+
+    wl = datagen.get(args.workload)
+    p = wl.patterns[0]
+    calls = args.warmup + args.steps
+    res = {}
+    for path, counter in ((args.ingest_comparator[0], "FETCH_SIZE"), (args.ingest_comparator[1], "WRITE_SIZE")):
+        vals, names = defaultdict(float), {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    vals[r["Dispatch_Id"]] += float(r["Counter_Value"])
+                    names[r["Dispatch_Id"]] = r["Kernel_Name"]
+        copies = sorted((k for k, n in names.items() if "copyBuffer" in n), key=int)
+        calib = [vals[k] for k in copies[-3:]]
+        work = [vals[k] for k, n in names.items() if "copyBuffer" not in n and "FillFunctor" not in n]
+        factor = CALIB_BYTES / (max(calib) * 1024.0)
+        res[counter] = sum(work) * 1024.0 * factor / calls
+        res[counter.lower() + "_factor"] = round(factor, 4)
+        res[counter.lower() + "_dispatches_per_call"] = round(len(work) / calls, 2)
+    xy = 4 * wl.batch * (datagen.n_in(p) + datagen.n_out(p))
+    out = {"workload": wl.name, "pattern": list(p), "comparator_bytes_per_call": int(res["FETCH_SIZE"] + res["WRITE_SIZE"]),
+           "X_plus_Y_bytes": xy, "ratio_to_X_plus_Y": round((res["FETCH_SIZE"] + res["WRITE_SIZE"]) / xy, 4),
+           **{k: v for k, v in res.items() if k not in ("FETCH_SIZE", "WRITE_SIZE")}}
+    print(json.dumps(out))
     return 0
 
 

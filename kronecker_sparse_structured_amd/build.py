@@ -69,7 +69,7 @@ def _stale(src: str) -> bool:
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
     if not os.path.exists(obj):
         return True
-    headers = [os.path.join(d, f) for d in (CSRC, INCLUDE) for f in os.listdir(d) if f.endswith(".h")]
+    headers = [os.path.join(d, f) for d in (CSRC, INCLUDE) for f in os.listdir(d) if f.endswith((".h", ".inc"))]
     newest = max(os.path.getmtime(p) for p in [src, *headers])
     return os.path.getmtime(obj) < newest
 

@@ -96,14 +96,47 @@ ks_status_t current_cus(int* cus) {
     return KS_OK;
 }
 
-// The planner's kernel family for one factor: the matrix cores whenever
-// the blocks fill 16 x 16 tiles (measured faster than the VALU kernel from
-// b = c = 16 up), else the VALU kernel, else the generic one.
-int choose_kernel(const Shape& s, int xt, int wt) {
-    if (ks::col_preferred(s, xt, wt)) return KS_KERNEL_COLUMN;
-    if (ks::mfma_supports(s, xt, wt)) return KS_KERNEL_MFMA;
-    if (ks::valu_supports(s, xt, wt)) return KS_KERNEL_VALU;
-    return KS_KERNEL_GENERIC;
+// The planner's table: for the patterns of a measured sweep, the fastest
+// kernel family and store schedule (generated from the measurements by
+// plan_table.py; the pages' "simple heuristic" on the pattern parameters has
+// no published form, so it is fitted here).
+struct PlanEntry {
+    int a, b, c, d, xt, wt, kernel, store_waves;
+};
+const PlanEntry kPlanTable[] = {
+#include "ks_plan_table.inc"
+    {0, 0, 0, 0, 0, 0, 0, 0}  // end
+};
+
+bool family_supports(int kernel, const Shape& s, int xt, int wt) {
+    switch (kernel) {
+        case KS_KERNEL_GENERIC: return true;
+        case KS_KERNEL_VALU: return ks::valu_supports(s, xt, wt);
+        case KS_KERNEL_MFMA: case KS_KERNEL_MFMA_LDS: return ks::mfma_supports(s, xt, wt);
+        case KS_KERNEL_COLUMN: return ks::col_supports(s, xt, wt);
+        default: return false;
+    }
+}
+
+// The planner's kernel family (and, for the matrix-core family, store
+// schedule) for one factor: the table's entry when the pattern and element
+// types are in it; otherwise the column kernel for whole-slab tiles of 16 x
+// 16 or 32 x 32 blocks, the matrix cores whenever the blocks fill 16 x 16
+// tiles (measured faster than the VALU kernel from b = c = 16 up), else the
+// VALU kernel, else the generic one.
+struct Choice {
+    int kernel, store_waves;
+};
+
+Choice choose_kernel(const Shape& s, int xt, int wt) {
+    for (const PlanEntry* e = kPlanTable; e->a != 0; ++e)
+        if (e->a == s.a && e->b == s.b && e->c == s.c && e->d == s.d && e->xt == xt && e->wt == wt &&
+            family_supports(e->kernel, s, xt, wt))
+            return {e->kernel, e->store_waves};
+    if (ks::col_preferred(s, xt, wt)) return {KS_KERNEL_COLUMN, KS_STORE_AUTO};
+    if (ks::mfma_supports(s, xt, wt)) return {KS_KERNEL_MFMA, KS_STORE_AUTO};
+    if (ks::valu_supports(s, xt, wt)) return {KS_KERNEL_VALU, KS_STORE_AUTO};
+    return {KS_KERNEL_GENERIC, KS_STORE_AUTO};
 }
 
 ks_status_t launch_family(int kernel, const ks::FactorCall& f) {
@@ -122,9 +155,12 @@ ks_status_t launch_family(int kernel, const ks::FactorCall& f) {
 // that are not 16-byte aligned).
 ks_status_t run_factor(int kernel, const ks::FactorCall& f) {
     if (kernel != KS_KERNEL_AUTO) return launch_family(kernel, f);
-    const int chosen = choose_kernel(f.s, f.xt, f.wt);
-    ks_status_t st = launch_family(chosen, f);
-    if (st == KS_ERR_UNSUPPORTED && chosen != KS_KERNEL_GENERIC) st = ks::launch_generic(f);
+    const Choice chosen = choose_kernel(f.s, f.xt, f.wt);
+    ks::FactorCall g = f;
+    if (g.store_waves == KS_STORE_AUTO) g.store_waves = chosen.store_waves;
+    ks_status_t st = launch_family(chosen.kernel, g);
+    if (st == KS_ERR_UNSUPPORTED && g.store_waves != f.store_waves) st = launch_family(chosen.kernel, f);
+    if (st == KS_ERR_UNSUPPORTED && chosen.kernel != KS_KERNEL_GENERIC) st = ks::launch_generic(f);
     return st;
 }
 
@@ -514,11 +550,12 @@ ks_status_t ks_plan_describe(ks_pattern_t p, int64_t batch, ks_dtype_t dt, char*
     int xt = 0, wt = 0;
     st = factor_types(enum_value(&dt), &xt, &wt);
     if (st != KS_OK) return st;
-    const int kernel = choose_kernel(s, xt, wt);
+    const Choice choice = choose_kernel(s, xt, wt);
+    const int kernel = choice.kernel;
     const int cus = 256;  // description only; launches use the device's count
     if (kernel == KS_KERNEL_COLUMN) ks::col_describe(s, xt, wt, batch, cus, buf, len);
     else if (kernel == KS_KERNEL_VALU) ks::valu_describe(s, xt, wt, batch, cus, buf, len);
-    else if (kernel == KS_KERNEL_MFMA) ks::mfma_describe(s, xt, wt, batch, cus, buf, len);
+    else if (kernel == KS_KERNEL_MFMA) ks::mfma_describe(s, xt, wt, batch, cus, buf, len, choice.store_waves);
     else std::snprintf(buf, len, "generic: one thread per output");
     return KS_OK;
 }

@@ -80,7 +80,8 @@ bool mfma_lds_supports(const Shape& s, int xt, int wt);
 
 // Planner description of the VALU / MFMA tiles (pure host).
 int valu_describe(const Shape& s, int xt, int wt, int64_t batch, int num_cus, char* buf, size_t len);
-int mfma_describe(const Shape& s, int xt, int wt, int64_t batch, int num_cus, char* buf, size_t len);
+int mfma_describe(const Shape& s, int xt, int wt, int64_t batch, int num_cus, char* buf, size_t len,
+                  int store_waves = KS_STORE_AUTO);
 
 // Fused pair of factors (intermediate kept in LDS). Returns KS_ERR_UNSUPPORTED
 // when the pair does not fit the fused kernel.

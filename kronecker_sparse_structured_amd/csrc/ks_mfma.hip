@@ -669,10 +669,12 @@ bool mfma_supports(const Shape& s, int xt, int wt) {
 
 bool mfma_lds_supports(const Shape& s, int xt, int wt) { return mfma_supports(s, xt, wt); }
 
-int mfma_describe(const Shape& s, int xt, int wt, int64_t batch, int num_cus, char* buf, size_t len) {
+int mfma_describe(const Shape& s, int xt, int wt, int64_t batch, int num_cus, char* buf, size_t len,
+                  int store_waves) {
     (void)wt;
     MfmaGeom g;
-    if (!choose_geom(s, xt, KS_STORE_AUTO, &g)) return std::snprintf(buf, len, "mfma: unsupported");
+    if (!choose_geom(s, xt, store_waves, &g) && !choose_geom(s, xt, KS_STORE_AUTO, &g))
+        return std::snprintf(buf, len, "mfma: unsupported");
     const int64_t rps = rows_per_split(g, batch, num_cus, 0);
     return std::snprintf(buf, len,
                          "mfma 16x16x4f32: pairs/tile=%d (alphas=%d deltas=%d %s) outputs/tile=%d of %d "

@@ -298,3 +298,25 @@ def test_dw_noalloc_argument_errors():
         for batch in (1, 333, 4096, 25216, 1 << 20, (1 << 31) - 1):
             for dt in (libks.DTYPE_F32, libks.DTYPE_BF16):
                 assert libks.ks_matmul_dw_workspace_size(q, batch, dt) <= scratch, (q, batch, dt)
+
+
+def test_planner_follows_fitted_table():
+    """For every pattern of the measured sweep, the planner picks the family
+    the sweep found fastest (the table generated into ks_plan_table.inc);
+    the family's name starts the plan description."""
+    inc = os.path.join(ROOT, "kronecker_sparse_structured_amd", "csrc", "ks_plan_table.inc")
+    prefix = {libks.KERNEL_MFMA: "mfma", libks.KERNEL_VALU: "valu", libks.KERNEL_COLUMN: "col",
+              libks.KERNEL_GENERIC: "generic"}
+    n = 0
+    for line in open(inc):
+        m = re.match(r"\{(\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)\},", line)
+        if not m:
+            continue
+        a, b, c, d, xt, wt, kernel, store = (int(v) for v in m.groups())
+        dt = {(0, 0): libks.DTYPE_F32, (1, 1): libks.DTYPE_BF16, (0, 1): libks.DTYPE_BF16W}[(xt, wt)]
+        desc = libks.ks_plan_describe((a, b, c, d), 16384, dt)
+        assert desc.startswith(prefix[kernel]), ((a, b, c, d), kernel, desc)
+        if kernel == libks.KERNEL_MFMA and store:
+            assert ("storers=1" in desc) == (store == libks.STORE_DEDICATED), ((a, b, c, d), store, desc)
+        n += 1
+    assert n >= 51
