@@ -61,6 +61,7 @@ WORKLOAD_SOURCES = {
     "vit_mlp": ("ks_mfma.hip",),
     "gpt2_mlp": ("ks_fused.hip",),
     "gpt2_mlp:nofuse": ("ks_mfma.hip", "ks_valu.hip"),
+    "monarch_n1024": ("ks_monarch.hip",),
 }
 
 

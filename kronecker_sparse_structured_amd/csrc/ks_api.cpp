@@ -164,6 +164,9 @@ ks_status_t run_factor(int kernel, const ks::FactorCall& f) {
     return st;
 }
 
+// Group kinds whose kernel needs 16-byte aligned input and output.
+bool aligned_pair_kind(int kind) { return kind == 4 || kind == 5; }
+
 // Validated chain: shapes, element types and the fusion grouping.
 struct ChainPlan {
     std::vector<Shape> shapes;
@@ -171,7 +174,8 @@ struct ChainPlan {
     std::vector<int> group_len;    // factors in the group (one launch)
     std::vector<int> group_kind;   // 0 single factor, 1 row-fused pair, 2 slab-fused pair,
                                    // 3 run of factors with rows resident in LDS,
-                                   // 4 strided pair (16-byte aligned input and output only)
+                                   // 4 strided pair, 5 Monarch pair (both: 16-byte aligned
+                                   // input and output only)
     int xt0 = ks::kF32, wt = ks::kF32;
     int64_t max_mid = 0;           // widest intermediate between groups
     int nbuf = 0;                  // workspace buffers (0, 1 or 2)
@@ -206,6 +210,9 @@ ks_status_t plan_chain(const ks_pattern_t* p, int n, int64_t batch, int dt,
             } else if (ks::strided_pair_supports(plan->shapes[k], plan->shapes[k + 1], xt, plan->wt, plan->wt)) {
                 len = 2;
                 kind = 4;
+            } else if (ks::monarch_pair_supports(plan->shapes[k], plan->shapes[k + 1], xt, plan->wt, plan->wt)) {
+                len = 2;
+                kind = 5;
             } else {
                 // the longest run from k whose rows fit on chip
                 for (int m = n - k; m >= 2; --m) {
@@ -228,12 +235,12 @@ ks_status_t plan_chain(const ks_pattern_t* p, int n, int64_t batch, int dt,
         if (last.n_out > plan->max_mid) plan->max_mid = last.n_out;
     }
     plan->nbuf = groups <= 1 ? 0 : (groups == 2 ? 1 : 2);
-    // A strided pair that reads X or writes Y needs both 16-byte aligned;
+    // A strided or Monarch pair that reads X or writes Y needs both 16-byte aligned;
     // otherwise it runs as its two factors, through a buffer that is neither
     // its input nor its output. The workspace does not depend on the
     // pointers, so it always has room for that.
     for (int g = 0; g < groups; ++g) {
-        if (plan->group_kind[g] != 4 || (g != 0 && g != groups - 1)) continue;
+        if (!aligned_pair_kind(plan->group_kind[g]) || (g != 0 && g != groups - 1)) continue;
         const Shape& first = plan->shapes[plan->group_start[g]];
         if (first.n_out > plan->max_mid) plan->max_mid = first.n_out;
         plan->nbuf = std::max(plan->nbuf, groups == 1 ? 1 : 2);
@@ -509,7 +516,10 @@ ks_status_t ks_chain_matmul(const ks_pattern_t* p, int n, const void* const* W,
         } else if (plan.group_kind[g] == 4 && ks::strided_pair_aligned(cur, out)) {
             st = ks::launch_strided_pair(plan.shapes[k], plan.shapes[k + 1], cur_t, plan.wt, plan.wt, W[k], W[k + 1],
                                          cur, out, batch, stream, cus);
-        } else if (plan.group_kind[g] == 4) {
+        } else if (plan.group_kind[g] == 5 && ks::monarch_pair_aligned(cur, out)) {
+            st = ks::launch_monarch_pair(plan.shapes[k], plan.shapes[k + 1], cur_t, plan.wt, plan.wt, W[k], W[k + 1],
+                                         cur, out, batch, stream, cus);
+        } else if (aligned_pair_kind(plan.group_kind[g])) {
             // X or Y not 16-byte aligned: the two factors one at a time,
             // through the buffer that is neither this group's input nor output
             float* mid = reinterpret_cast<float*>(

@@ -108,6 +108,17 @@ ks_status_t launch_strided_pair(const Shape& s0, const Shape& s1, int xt, int wt
                                 const void* W1, const void* X, float* Y, int64_t batch, hipStream_t stream,
                                 int num_cus);
 
+// Monarch-shaped pair F = (M, N, N, 1) then G = (1, M, M, N), M and N in
+// {16, 32} (ks_monarch.hip): whole rows in LDS, weights streamed from L2.
+// fp32 X (fp32 or bf16 weights) or bf16 X with bf16 weights; X and Y must be
+// 16-byte aligned (monarch_pair_aligned), else the launcher returns
+// KS_ERR_UNSUPPORTED.
+bool monarch_pair_supports(const Shape& s0, const Shape& s1, int xt, int wt0, int wt1);
+bool monarch_pair_aligned(const void* X, const void* Y);
+ks_status_t launch_monarch_pair(const Shape& s0, const Shape& s1, int xt, int wt0, int wt1, const void* W0,
+                                const void* W1, const void* X, float* Y, int64_t batch, hipStream_t stream,
+                                int num_cus);
+
 // A run of factors with whole rows resident in LDS (ks_rowchain.hip): n >= 2
 // factors of small blocks whose widest row fits on chip. s, W: n entries.
 bool row_chain_supports(const Shape* s, int n, int xt, int wt);

@@ -1,0 +1,422 @@
+// ks_monarch.hip -- a Monarch-shaped pair of KS factors in one launch:
+// F = (M, N, N, 1), a block-diagonal factor of M blocks of N x N, then
+// G = (1, M, M, N), which mixes the M blocks for each of the N positions.
+//
+// KS matrices underpin Butterfly and Monarch matrices (KS abstract page,
+// taxoreview.com "dblp:303/4794", first paragraph, first sentence). A row of
+// X is X[alpha][gamma] (M x N), F gives Z[alpha][beta] = sum_gamma
+// K_F[alpha][0][beta][gamma] X[alpha][gamma], and G reads Z as
+// Z[gamma' = alpha][delta' = beta] and gives Y[beta'][beta] = sum_alpha
+// K_G[0][beta][beta'][alpha] Z[alpha][beta]. The pair mixes every value of a
+// row, so a workgroup holds 16 whole rows (at most 4 KB each) in an LDS
+// stage; the intermediate never leaves the chip and the pair moves
+// |X| + |Y| + weights through HBM instead of |X| + 2 |Z| + |Y|.
+//
+// Every row needs all of the two factors' weights (M N N + N M M values),
+// and each compute wave needs those of its own groups at every stage: up to
+// 96 registers a lane, which stay resident for the whole launch, or for
+// M = N = 32 (256 KB of fp32, 256 registers a lane) a stream from L2 through
+// a ring of registers, several groups ahead of their use. In both products
+// the k index is assigned so that a lane's k values are consecutive (lane
+// group g takes k = (K / 4) g + ks in step ks; any order of the k sum is the
+// same sum up to rounding), which makes a lane's B operands of one group
+// consecutive weights (16-byte loads) and its A operands consecutive values
+// of the row.
+//
+// Per 16-row stage, in place in LDS:
+//  (A) wave w takes the blocks alpha = w M / 4 ..: Z[rows][alpha][beta] =
+//      X[rows][alpha][.] (16 x N) times the block's transpose, written over
+//      X[rows][alpha][.] (a wave reads and writes only its own blocks);
+//  (B) after an LDS barrier, wave w takes positions beta = w N / 4 .., four
+//      at a time (one 16-byte LDS read gives the A operands of four
+//      positions): Y[rows][beta'][beta] = Z[rows][.][beta] (16 x M) times
+//      K_G[beta]'s transpose, written over Z[rows][.][beta];
+//  (C) after another barrier the compute waves store the rows.
+// A loader wave streams the next stages from HBM meanwhile.
+//
+// LDS row layout (floats): value (x, y) at x * (N + 4) + y, rows
+// M (N + 4) + 4 apart: the 16 rows, the 16 consecutive y or the 16
+// consecutive x that one instruction spreads its lanes over fall in
+// different 16-byte bank groups. bf16 X lands in the first half of each
+// index's slot (value (x, y) at byte 4 x (N + 4) + 2 y); phase A reads a
+// block's inputs before it writes that block's fp32 results over the same
+// slot. X and Y 16-byte aligned. The weights need only their element
+// alignment: their 16-byte loads are valid at any such alignment in the
+// unaligned-access mode that ROCm sets for this GPU family (the compiler
+// merges element loads into the same instructions by itself).
+
+#include <algorithm>
+#include <cstdio>
+
+#include "ks_device.h"
+#include "ks_internal.h"
+#include "ks_stream.h"
+
+namespace ks {
+namespace {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kR = 16;                               // rows per stage: one MFMA M tile
+constexpr int kThreads = kStreamThreads;             // 4 compute waves + 1 loader wave
+
+template <int M, int N>
+struct MonShape {
+    static constexpr int XP = N + 4;                 // floats per index x in LDS
+    static constexpr int RP = M * XP + 4;            // floats per row in LDS
+    static constexpr int XVEC = N / 4;               // 16-byte vectors per x in a row of Y (fp32)
+    static constexpr int STAGE_VEC = kR * RP / 4;    // 16-byte LDS vectors per stage
+    static constexpr int INSTS = (STAGE_VEC + 63) / 64;
+    static constexpr int STAGE_BYTES = INSTS * 1024;
+    static constexpr int STAGES = std::min(4, (150 * 1024) / STAGE_BYTES);
+    static constexpr int KSF = N / 4, NTF = N / 16;  // F: k steps (gamma), N tiles (beta)
+    static constexpr int KSG = M / 4, NTG = M / 16;  // G: k steps (alpha), N tiles (beta')
+    static constexpr int GA = M / 4;                 // F blocks per wave
+    static constexpr int GB = N / 4;                 // G positions per wave (batches of 4)
+    static_assert(STAGES >= 2 && (N == 16 || N == 32) && (M == 16 || M == 32), "shapes");
+    static_assert(RP % 4 == 0 && (RP / 4) % 2 == 1 && XP % 4 == 0, "16-byte rows; odd row pitch in vectors");
+};
+
+struct MonArgs {
+    int64_t n;               // row width M * N
+    int64_t batch;
+    int rows_per_split;      // a multiple of kR
+};
+
+// Four consecutive weights in registers: fp32 as loaded (16 bytes), bf16
+// packed (8 bytes) and widened when used.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+template <typename TW> struct WReg { typedef floatx4 type; };
+template <> struct WReg<bf16_t> { typedef u32x2 type; };
+
+// count consecutive 4-value registers of weights from p (16-byte aligned),
+// one 16-byte load per fp32 register or per two bf16 registers
+__device__ __forceinline__ void load_wr(floatx4* dst, const float* p, int count) {
+    for (int q = 0; q < count; ++q) dst[q] = *reinterpret_cast<const floatx4*>(p + 4 * q);
+}
+__device__ __forceinline__ void load_wr(u32x2* dst, const bf16_t* p, int count) {
+    int q = 0;
+    for (; q + 1 < count; q += 2) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(p + 4 * q);
+        dst[q] = u32x2{v[0], v[1]};
+        dst[q + 1] = u32x2{v[2], v[3]};
+    }
+    if (q < count) dst[q] = *reinterpret_cast<const u32x2*>(p + 4 * q);
+}
+__device__ __forceinline__ float w_at(const floatx4& r, int k) { return r[k]; }
+__device__ __forceinline__ float w_at(const u32x2& r, int k) { return (k & 1) ? bf16_hi(r[k >> 1]) : bf16_lo(r[k >> 1]); }
+
+// Four consecutive stage values of X widened to fp32 (from LDS).
+__device__ __forceinline__ floatx4 lds_x4(const unsigned char* p, float) {
+    return *reinterpret_cast<const floatx4*>(p);
+}
+__device__ __forceinline__ floatx4 lds_x4(const unsigned char* p, bf16_t) {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+    return floatx4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
+}
+
+template <int M, int N, typename TX, typename TW>
+__global__ __launch_bounds__(kThreads) void monarch_pair_kernel(const TX* __restrict__ X,
+                                                                const TW* KF,
+                                                                const TW* KG,
+                                                                float* __restrict__ Y, MonArgs args) {
+    using S = MonShape<M, N>;
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int t = threadIdx.x;
+    const int64_t row_begin = int64_t(blockIdx.x) * args.rows_per_split;
+    if (row_begin >= args.batch) return;
+    const int64_t row_end = min(args.batch, row_begin + int64_t(args.rows_per_split));
+    const int nsteps = static_cast<int>((row_end - row_begin + kR - 1) / kR);
+    auto stage = [&](int s) { return reinterpret_cast<float*>(lds + (s % S::STAGES) * S::STAGE_BYTES); };
+
+    if (t >= kConsumerThreads) {
+        // ------------------------------------------------------ loader wave
+        // instruction i fills LDS vectors [64 i, 64 i + 64) of a stage: row
+        // r, index x, vector v of the row's x-th run of N values (N / 4 fp32
+        // or N / 8 bf16 vectors); padding vectors (and any past the stage)
+        // load the stage's first vector
+        constexpr int EB = sizeof(TX);
+        constexpr int XIN = N * EB / 16;
+        const int lane = t - kConsumerThreads;
+        uint32_t off[S::INSTS];
+#pragma unroll
+        for (int i = 0; i < S::INSTS; ++i) {
+            const int q = 64 * i + lane;
+            const int r = q / (S::RP / 4), u = q - r * (S::RP / 4);
+            const int x = u / (S::XP / 4), v = u - x * (S::XP / 4);
+            off[i] = (r < kR && x < M && v < XIN) ? static_cast<uint32_t>((r * args.n + x * N) * EB + 16 * v) : 0u;
+        }
+        auto issue = [&](int s) {
+            const int64_t n0 = row_begin + int64_t(s) * kR;
+            const uint32_t limit = stage_limit(n0, row_end, args.n, EB);
+            const char* base = reinterpret_cast<const char*>(X + n0 * args.n);
+            unsigned char* st = reinterpret_cast<unsigned char*>(stage(s));
+#pragma unroll
+            for (int i = 0; i < S::INSTS; ++i)
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + (off[i] < limit ? off[i] : 0u)),
+                                                 st + 1024 * i, 16, 0, 0);
+        };
+        for (int s = 0; s < S::STAGES && s < nsteps; ++s) issue(s);
+        for (int s = 0; s < nsteps; ++s) {
+            // stage s has landed once only the stages issued after it remain
+            // (a count above vmcnt's 63 waits a little longer, never less)
+            wait_vmcnt_upto(min(63, min(S::STAGES - 1, nsteps - 1 - s) * S::INSTS));
+            lds_barrier();                                   // stage s ready
+            lds_barrier();                                   // Z written
+            lds_barrier();                                   // Y written
+            lds_barrier();                                   // stage s read out
+            if (s + S::STAGES < nsteps) issue(s + S::STAGES);
+        }
+        return;
+    }
+
+    // ---------------------------------------------------------- consumers
+    // v_mfma_f32_16x16x4_f32: lane l supplies A[l % 16][l / 16] and
+    // B[l / 16][l % 16] and receives D[4 (l / 16) + i][l % 16] in register i.
+    // Lane group g = l / 16 takes k = (K / 4) g + ks in step ks.
+    //
+    // The weights of a wave's groups are the same for every stage. A chunk
+    // is one group's B operands for this lane: F block j (CF 4-value
+    // registers) or G position p (CG). When all of them fit (M N N + N M M
+    // <= 24,576 values, at most 96 registers a lane) they are loaded once and
+    // stay resident. For M = N = 32 (256 registers a lane) each stage
+    // streams its 16 chunks (F blocks 0..7, then G positions 0..7) through
+    // a ring of 8 slots: a slot is refilled as soon as its chunk has been
+    // used, with the chunk 8 places later (F block j is followed by G
+    // position j, G position j by the next stage's F block j). All of a
+    // stage's F blocks are thus requested before the previous stage's rows
+    // are stored: the vector-memory counter completes in order, so a wait
+    // for a chunk requested after those stores would also wait for them.
+    // bf16 weights stay packed and widen at use.
+    using WR = typename WReg<TW>::type;
+    constexpr int CF = S::NTF * (S::KSF / 4);
+    constexpr int CG = S::NTG * (S::KSG / 4);
+    constexpr int kChunks = S::GA + S::GB;
+    constexpr bool kStream = (M * N * N + N * M * M) > 24576;
+    constexpr int kSlots = 8;
+    static_assert(!kStream || (CF == CG && S::GA == kSlots && S::GB == kSlots), "ring layout");
+    constexpr int kRegs = kStream ? kSlots * CF : S::GA * CF + S::GB * CG;
+
+    const int w = t >> 6;
+    const int lane = t & 63;
+    const int col = lane & 15;
+    const int g = lane >> 4;
+
+    WR wr[kRegs];
+    // where chunk c (0 <= c < kChunks of a stage) lives in wr
+    auto chunk_base = [&](int c) constexpr {
+        if (kStream) return (c % kSlots) * CF;
+        return c < S::GA ? c * CF : S::GA * CF + (c - S::GA) * CG;
+    };
+    // load chunk c (of any stage: the same weights) into its registers.
+    // Addresses are a wave-uniform base (scalar registers) plus this lane's
+    // 32-bit byte offset, which keeps per-chunk addresses out of VGPRs.
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const char* kf = reinterpret_cast<const char*>(KF + int64_t(wu) * S::GA * N * N);
+    const char* kg = reinterpret_cast<const char*>(KG + int64_t(wu) * S::GB * M * M);
+    const uint32_t lf = static_cast<uint32_t>((col * N + S::KSF * g) * sizeof(TW));
+    const uint32_t lg = static_cast<uint32_t>((col * M + S::KSG * g) * sizeof(TW));
+    auto load_chunk = [&](int c) {
+        c %= kChunks;
+        const int base = chunk_base(c);
+        if (c < S::GA) {
+            // K_F[alpha = w GA + c][0][beta = 16 nt + col][gamma = KSF g ..]
+#pragma unroll
+            for (int nt = 0; nt < S::NTF; ++nt)
+                load_wr(wr + base + nt * (S::KSF / 4),
+                        reinterpret_cast<const TW*>(kf + (c * N + 16 * nt) * N * sizeof(TW) + lf), S::KSF / 4);
+        } else {
+            // K_G[0][beta = w GB + p][beta' = 16 nt + col][alpha = KSG g ..]
+            const int p = c - S::GA;
+#pragma unroll
+            for (int nt = 0; nt < S::NTG; ++nt)
+                load_wr(wr + base + nt * (S::KSG / 4),
+                        reinterpret_cast<const TW*>(kg + (p * M + 16 * nt) * M * sizeof(TW) + lg), S::KSG / 4);
+        }
+    };
+    // the requests keep their place in the program: no compiler pass may
+    // move memory operations across this point (the scheduler would sink a
+    // prefetch next to its use; earlier passes could merge or reorder loads)
+    auto order_point = [] {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // refill the slot of chunk c, just used, with chunk c + kSlots
+    auto refill = [&](int c) {
+        if (kStream) {
+            order_point();
+            load_chunk(c + kSlots);
+            order_point();
+        }
+    };
+    // the first chunks, in the order the refills keep afterwards (waits are
+    // counted against the order of requests, the first stage's included)
+#pragma unroll
+    for (int c = 0; c < (kStream ? kSlots : kChunks); ++c) {
+        load_chunk(c);
+        if (kStream) order_point();
+    }
+
+    // this lane's X values of F block alpha: X[col][alpha][KSF g ..]
+    auto read_x = [&](const float* st, int alpha, floatx4 (&xv)[S::KSF / 4]) {
+        const unsigned char* xr =
+            reinterpret_cast<const unsigned char*>(st + col * S::RP + alpha * S::XP) + S::KSF * g * sizeof(TX);
+#pragma unroll
+        for (int q = 0; q < S::KSF / 4; ++q) xv[q] = lds_x4(xr + 4 * q * sizeof(TX), TX());
+    };
+    // Z[col][alpha = KSG g + ks][beta0 .. beta0 + 3]
+    auto read_z = [&](const float* st, int ks, int beta0) {
+        return *reinterpret_cast<const floatx4*>(st + col * S::RP + (S::KSG * g + ks) * S::XP + beta0);
+    };
+
+    for (int s = 0; s < nsteps; ++s) {
+        float* st = stage(s);
+        lds_barrier();                                                   // stage s ready
+        // (A) Z[r][alpha][beta] = sum_gamma K_F[alpha][0][beta][gamma] X[r][alpha][gamma].
+        // Block j + 1's inputs are read before block j's results are
+        // written (other slots of the row, so the order is free).
+        floatx4 xn[S::KSF / 4];
+        read_x(st, w * S::GA, xn);
+#pragma unroll
+        for (int j = 0; j < S::GA; ++j) {
+            const int alpha = w * S::GA + j;
+            floatx4 xv[S::KSF / 4];
+#pragma unroll
+            for (int q = 0; q < S::KSF / 4; ++q) xv[q] = xn[q];
+            if (j + 1 < S::GA) read_x(st, alpha + 1, xn);
+            const int base = chunk_base(j);
+            floatx4 acc[S::NTF];
+#pragma unroll
+            for (int nt = 0; nt < S::NTF; ++nt) acc[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ks = 0; ks < S::KSF; ++ks)
+#pragma unroll
+                for (int nt = 0; nt < S::NTF; ++nt)
+                    acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                        xv[ks / 4][ks % 4], w_at(wr[base + nt * (S::KSF / 4) + ks / 4], ks % 4), acc[nt], 0, 0, 0);
+            refill(j);
+#pragma unroll
+            for (int nt = 0; nt < S::NTF; ++nt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) st[(4 * g + i) * S::RP + alpha * S::XP + 16 * nt + col] = acc[nt][i];
+        }
+        lds_barrier();                                                   // Z written
+        // (B) Y[r][beta'][beta] = sum_alpha K_G[0][beta][beta'][alpha] Z[r][alpha][beta], four beta at a time
+#pragma unroll
+        for (int j = 0; j < S::GB; j += 4) {
+            const int beta0 = w * S::GB + j;
+            floatx4 acc[4][S::NTG];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int nt = 0; nt < S::NTG; ++nt) acc[u][nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ks = 0; ks < S::KSG; ++ks) {
+                const floatx4 zv = read_z(st, ks, beta0);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int base = chunk_base(S::GA + j + u);
+#pragma unroll
+                    for (int nt = 0; nt < S::NTG; ++nt)
+                        acc[u][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                            zv[u], w_at(wr[base + nt * (S::KSG / 4) + ks / 4], ks % 4), acc[u][nt], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) refill(S::GA + j + u);
+#pragma unroll
+            for (int nt = 0; nt < S::NTG; ++nt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<floatx4*>(st + (4 * g + i) * S::RP + (16 * nt + col) * S::XP + beta0) =
+                        floatx4{acc[0][nt][i], acc[1][nt][i], acc[2][nt][i], acc[3][nt][i]};
+        }
+        lds_barrier();                                                   // Y written
+        // (C) the rows out: thread t takes 16-byte vectors t, t + 256, .. of
+        // the stage's rows in Y's order, in two halves (half the registers)
+        {
+            const int64_t n0 = row_begin + int64_t(s) * kR;
+            const int rows = static_cast<int>(min(int64_t(kR), row_end - n0));
+            constexpr int VPR = M * S::XVEC;                 // vectors per row of Y
+            constexpr int PER = kR * VPR / kConsumerThreads; // vectors per thread
+            static_assert(PER % 2 == 0, "halves");
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                floatx4 v[PER / 2];
+#pragma unroll
+                for (int j = 0; j < PER / 2; ++j) {
+                    const int q = t + kConsumerThreads * (h * (PER / 2) + j);
+                    const int r = q / VPR, u = q - r * VPR, x = u / S::XVEC, e = u - x * S::XVEC;
+                    v[j] = *reinterpret_cast<const floatx4*>(st + r * S::RP + x * S::XP + 4 * e);
+                }
+#pragma unroll
+                for (int j = 0; j < PER / 2; ++j) {
+                    const int q = t + kConsumerThreads * (h * (PER / 2) + j);
+                    const int r = q / VPR, u = q - r * VPR;
+                    if (r < rows)
+                        __builtin_nontemporal_store(v[j], reinterpret_cast<floatx4*>(Y + (n0 + r) * args.n + 4 * u));
+                }
+            }
+            lds_barrier();                                               // stage s read out
+        }
+    }
+    // the ring's last prefetches (of a stage that does not come) land
+    // before the wave ends
+    wait_vmcnt<0>();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+template <int M, int N, typename TX, typename TW>
+ks_status_t launch_mn(const void* W0, const void* W1, const void* X, float* Y, int64_t batch, hipStream_t stream,
+                      int num_cus) {
+    using S = MonShape<M, N>;
+    MonArgs args;
+    args.n = int64_t(M) * N;
+    args.batch = batch;
+    // one workgroup per compute unit, equal row shares
+    const int64_t steps_total = (batch + kR - 1) / kR;
+    const int64_t per_cu = std::max<int64_t>(1, (160 * 1024) / (int64_t(S::STAGES) * S::STAGE_BYTES));
+    const int64_t wgs = std::max<int64_t>(1, int64_t(std::max(num_cus, 1)) * per_cu);
+    const int64_t steps = std::max<int64_t>(1, (steps_total + wgs - 1) / wgs);
+    args.rows_per_split = static_cast<int>(steps * kR);
+    const int64_t blocks = (batch + args.rows_per_split - 1) / args.rows_per_split;
+    if (blocks > 0x7fffffff) return KS_ERR_UNSUPPORTED;
+    return launch_kernel(monarch_pair_kernel<M, N, TX, TW>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
+                         size_t(S::STAGES) * S::STAGE_BYTES, stream, static_cast<const TX*>(X),
+                         static_cast<const TW*>(W0), static_cast<const TW*>(W1), Y, args);
+}
+
+template <typename TX, typename TW>
+ks_status_t launch_typed(int M, int N, const void* W0, const void* W1, const void* X, float* Y, int64_t batch,
+                         hipStream_t stream, int num_cus) {
+    if (M == 16 && N == 16) return launch_mn<16, 16, TX, TW>(W0, W1, X, Y, batch, stream, num_cus);
+    if (M == 16 && N == 32) return launch_mn<16, 32, TX, TW>(W0, W1, X, Y, batch, stream, num_cus);
+    if (M == 32 && N == 16) return launch_mn<32, 16, TX, TW>(W0, W1, X, Y, batch, stream, num_cus);
+    if (M == 32 && N == 32) return launch_mn<32, 32, TX, TW>(W0, W1, X, Y, batch, stream, num_cus);
+    return KS_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+
+bool monarch_pair_supports(const Shape& s0, const Shape& s1, int xt, int wt0, int wt1) {
+    // fp32 X with fp32 or bf16 weights, or bf16 X with bf16 weights
+    if (wt0 != wt1 || !(wt0 == kF32 || wt0 == kBF16) || !(xt == kF32 || xt == wt0)) return false;
+    const int M = s0.a, N = s0.b;
+    if (!((M == 16 || M == 32) && (N == 16 || N == 32))) return false;
+    return s0.c == N && s0.d == 1 && s1.a == 1 && s1.b == M && s1.c == M && s1.d == N;
+}
+
+bool monarch_pair_aligned(const void* X, const void* Y) { return aligned16(X) && aligned16(Y); }
+
+ks_status_t launch_monarch_pair(const Shape& s0, const Shape& s1, int xt, int wt0, int wt1, const void* W0,
+                                const void* W1, const void* X, float* Y, int64_t batch, hipStream_t stream,
+                                int num_cus) {
+    if (!monarch_pair_supports(s0, s1, xt, wt0, wt1) || !monarch_pair_aligned(X, Y)) return KS_ERR_UNSUPPORTED;
+    if (wt0 == kF32) return launch_typed<float, float>(s0.a, s0.b, W0, W1, X, Y, batch, stream, num_cus);
+    if (xt == kF32) return launch_typed<float, bf16_t>(s0.a, s0.b, W0, W1, X, Y, batch, stream, num_cus);
+    return launch_typed<bf16_t, bf16_t>(s0.a, s0.b, W0, W1, X, Y, batch, stream, num_cus);
+}
+
+}  // namespace ks

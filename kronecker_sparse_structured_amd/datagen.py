@@ -128,6 +128,12 @@ def workloads() -> dict:
     # then (1024, 16, 16, 4) at n = 65,536 (not a configuration of the pages)
     w["strided_pair_e4"] = Workload("strided_pair_e4", [(64, 16, 16, 64), (1024, 16, 16, 4)], 4096, [0.25] * 2, 9,
                                     note="two radix-16 factors four elements apart, n = 65,536")
+    # a Monarch-shaped pair: 32 blocks of 32 x 32, then the mixing factor
+    # across blocks, at n = 1024 (Monarch matrices as KS chains; the pages
+    # give no sizes, so these are synthetic)
+    w["monarch_n1024"] = Workload("monarch_n1024", [(32, 32, 32, 1), (1, 32, 32, 32)], 65536,
+                                  [1.0 / np.sqrt(32.0)] * 2, 10,
+                                  note="Monarch pair, 32 blocks of 32 x 32 then their mixing, n = 1024")
     for p_idx, p in enumerate(square_sweep_patterns()):
         name = "square_%d_%d_%d_%d" % p
         w[name] = Workload(name, [p], 16384, [1.0 / np.sqrt(p[2])], 3000 + p_idx,

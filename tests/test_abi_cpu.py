@@ -187,8 +187,9 @@ def test_chain_plan_row_resident_runs():
 def test_chain_plan_fuses_known_pairs():
     """The planner fuses the GPT-2 pair (rows shared by groups of beta0), the
     butterfly's last two factors (the second works inside the first's output
-    slabs) and, for fp32 rows, a factor with the next one of the strided
-    family (a, 16, 16, 16 e) -> (16 a, 16, 16, e); nothing with NO_FUSE."""
+    slabs), for fp32 rows a factor with the next one of the strided family
+    (a, 16, 16, 16 e) -> (16 a, 16, 16, e), and Monarch pairs
+    (M, N, N, 1) -> (1, M, M, N); nothing with NO_FUSE."""
     gpt2 = [(1, 64, 16, 64), (64, 8, 8, 8)]
     bfly = [(16 ** k, 16, 16, 16 ** (3 - k)) for k in range(4)]
     for dt in (libks.DTYPE_F32, libks.DTYPE_BF16):
@@ -214,6 +215,18 @@ def test_chain_plan_fuses_known_pairs():
     assert libks.ks_chain_groups([(4, 16, 16, 16), (64, 16, 8, 2)], 7, libks.DTYPE_F32) == [[0], [1]]
     assert libks.ks_chain_groups([(4, 8, 16, 16), (32, 16, 16, 1)], 7, libks.DTYPE_F32) == [[0], [1]]
 
+    # Monarch family: (M, N, N, 1) -> (1, M, M, N) with M, N in {16, 32}, every
+    # dtype; the spare buffer for unaligned X or Y; other shapes stay apart
+    for M in (16, 32):
+        for N in (16, 32):
+            pair = [(M, N, N, 1), (1, M, M, N)]
+            for dt in (libks.DTYPE_F32, libks.DTYPE_BF16, libks.DTYPE_BF16W):
+                assert libks.ks_chain_groups(pair, 7, dt) == [[0, 1]]
+                assert libks.ks_chain_groups(pair, 7, dt, libks.CHAIN_NO_FUSE) == [[0], [1]]
+            assert libks.ks_chain_workspace_size(pair, 7, libks.DTYPE_F32) == (7 * M * N * 4 + 255) // 256 * 256
+    assert libks.ks_chain_groups([(64, 64, 64, 1), (1, 64, 64, 64)], 7, libks.DTYPE_F32) == [[0], [1]]
+    assert libks.ks_chain_groups([(32, 32, 32, 1), (1, 32, 16, 64)], 7, libks.DTYPE_F32) == [[0], [1]]
+    assert libks.ks_chain_groups([(32, 32, 32, 2), (2, 32, 32, 32)], 7, libks.DTYPE_F32) == [[0], [1]]
 
 def test_one_hip_runtime_whatever_the_import_order():
     """Loading libks before torch must still leave a single HIP runtime in

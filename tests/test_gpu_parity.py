@@ -390,6 +390,77 @@ def test_strided_pair_shapes(ae, lead, bf16w):
     assert np.sqrt(se / sr) <= FP32_REL_TOL, (np.sqrt(se / sr), ma)
 
 
+MONARCH_DTYPES = {"f32": libks.DTYPE_F32, "bf16": libks.DTYPE_BF16, "bf16w": libks.DTYPE_BF16W}
+
+
+@pytest.mark.parametrize("dt", sorted(MONARCH_DTYPES))
+@pytest.mark.parametrize("lead", [False, True])
+@pytest.mark.parametrize("mn", [(16, 16), (16, 32), (32, 16), (32, 32)], ids=lambda v: "m%d_n%d" % v)
+def test_monarch_pair_shapes(mn, lead, dt):
+    """The one-launch Monarch pair (M, N, N, 1) -> (1, M, M, N): whole rows
+    in LDS, both products on the matrix cores. A ragged row count (203 rows,
+    13 stages of 16) and one large enough that every workgroup runs several
+    stages around its LDS ring (9001 rows); bf16 X with bf16 weights, and
+    fp32 X with fp32 or bf16 weights; behind a leading factor the pair reads
+    the workspace."""
+    M, N = mn
+    pats = [(M, N, N, 1), (1, M, M, N)]
+    if lead:
+        pats = [(M * N // 4, 4, 4, 1)] + pats
+    code = MONARCH_DTYPES[dt]
+    bf16 = dt == "bf16"
+    w_bf16 = dt != "f32"
+    for batch in (203, 9001):
+        wl = datagen.Workload("monarch", pats, batch, [1.0 / np.sqrt(p[2]) for p in pats], 80 + M + N)
+        groups = libks.ks_chain_groups(wl.patterns, wl.batch, code)
+        assert [len(g) for g in groups] == ([1, 2] if lead else [2]), groups
+        X, Ws = datagen.draw(wl)
+        Y = libks.chain_matmul(to_dev(X, bf16), [to_dev(W, w_bf16) for W in Ws], wl.patterns)
+        torch.cuda.synchronize()
+        Xd = host_values(X, bf16)
+        Wd = [host_values(W, w_bf16) for W in Ws]
+        se, sr, ma = oracle.ks_chain_err(wl.patterns, Wd, Xd, Y.cpu().numpy())
+        # the oracle takes the same bf16-rounded inputs, so only fp32
+        # accumulation separates the two
+        assert np.sqrt(se / sr) <= FP32_REL_TOL, (batch, np.sqrt(se / sr), ma)
+
+
+@pytest.mark.parametrize("dt", sorted(MONARCH_DTYPES))
+@pytest.mark.parametrize("mn", [(16, 32), (32, 32)], ids=lambda v: "m%d_n%d" % v)
+def test_monarch_pair_weights_at_element_offsets(mn, dt):
+    """The Monarch pair with both weight tensors one element past a 16-byte
+    boundary (the API asks only for element alignment of weights): still one
+    launch, and the same bits as with aligned weights."""
+    M, N = mn
+    pats = [(M, N, N, 1), (1, M, M, N)]
+    code = MONARCH_DTYPES[dt]
+    bf16 = dt == "bf16"
+    w_bf16 = dt != "f32"
+    wl = datagen.Workload("monarch", pats, 1001, [1.0 / np.sqrt(p[2]) for p in pats], 90 + M + N)
+    X, Ws = datagen.draw(wl)
+    Xd = to_dev(X, bf16)
+    Wa = [to_dev(W, w_bf16) for W in Ws]
+    Wo = [_offset_copy(w, 1) for w in Wa]
+    assert all(w.data_ptr() % 16 != 0 for w in Wo)
+    Ya = libks.chain_matmul(Xd, Wa, pats)
+    Yo = libks.chain_matmul(Xd, Wo, pats)
+    torch.cuda.synchronize()
+    assert libks.ks_chain_groups(pats, wl.batch, code) == [[0, 1]]
+    assert np.array_equal(Ya.cpu().numpy(), Yo.cpu().numpy())
+    se, sr, ma = oracle.ks_chain_err(pats, [host_values(W, w_bf16) for W in Ws], host_values(X, bf16),
+                                     Yo.cpu().numpy())
+    assert np.sqrt(se / sr) <= FP32_REL_TOL, (np.sqrt(se / sr), ma)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("fuse", [True, False])
+def test_monarch_chain_full_size(bf16, fuse):
+    """65,536 rows of 1,024 through the Monarch pair (32 blocks of 32 x 32,
+    then their mixing), in one launch and one launch per factor: every
+    output."""
+    _chain_workload("monarch_n1024", bf16, fuse)
+
+
 def _radix(r, L):
     """Factors (r^k, r, r, r^(L-1-k)), k = 0..L-1: a radix-r butterfly on n = r^L."""
     return [(r ** k, r, r, r ** (L - 1 - k)) for k in range(L)]
@@ -464,6 +535,7 @@ FUSED_CHAINS = {
     "slab_pair_a3": ([(3, 16, 16, 16), (48, 16, 16, 1)], 45, 43),
     "butterfly65536": (datagen.get("butterfly65536").patterns, 5, 44),
     "strided_pair_a2_e8": ([(2, 16, 16, 128), (32, 16, 16, 8)], 45, 45),
+    "monarch_m32_n16": ([(32, 16, 16, 1), (1, 32, 32, 16)], 45, 46),
 }
 
 
@@ -473,8 +545,11 @@ def test_fused_chain_unaligned_pointers(name, bf16):
     """The fused pair kernels with X and Y aligned only to their element
     size: X at every element offset from a 16-byte boundary that a 4-byte
     (fp32) or 2-byte (bf16) alignment allows, Y at 4 and 8 bytes past one.
-    The plan keeps its fused groups (16-byte alignment only selects vector
-    loads) and every offset matches the oracle."""
+    The plan keeps its fused groups and every offset matches the oracle. For
+    most pairs 16-byte alignment only selects vector loads, so every offset
+    gives the same bits; the strided and Monarch pairs run their two factors
+    one at a time when X or Y is not 16-byte aligned, so the same bits hold
+    within each of the two cases."""
     pats, batch, seed = FUSED_CHAINS[name]
     if bf16 and name.startswith("strided"):
         pytest.skip("the strided pair reads fp32 X; a bf16 chain runs these factors one at a time")
@@ -486,8 +561,9 @@ def test_fused_chain_unaligned_pointers(name, bf16):
     Xd = to_dev(X, bf16)
     Wts = [to_dev(W, bf16) for W in Ws]
     n_out = datagen.n_out(pats[-1])
-    ref = None
+    refs = {}
     per16 = 8 if bf16 else 4
+    split_when_unaligned = name.startswith("strided") or name.startswith("monarch")
     for xo in range(per16):
         for yo in ([1, 2] if xo % 2 else [0, 3]):
             Xo = _offset_copy(Xd, xo)
@@ -496,11 +572,12 @@ def test_fused_chain_unaligned_pointers(name, bf16):
             torch.cuda.synchronize()
             Yh = Yo.cpu().numpy()
             chain_check(pats, X, Ws, Yh, bf16)
-            if ref is None:
-                ref = Yh
+            key = (xo == 0 and yo == 0) if split_when_unaligned else None
+            if key not in refs:
+                refs[key] = Yh
             else:
-                # the same kernels and summation order at every offset
-                assert np.array_equal(Yh, ref), (xo, yo)
+                # the same kernels and summation order at every such offset
+                assert np.array_equal(Yh, refs[key]), (xo, yo)
 
 
 def test_dw_unaligned_pointers():
