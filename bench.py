@@ -119,6 +119,10 @@ def parse():
     ap.add_argument("--ingest-comparator", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="HBM bytes per call of the comparator from two --comparator-only counter runs "
                          "(same --steps / --warmup)")
+    ap.add_argument("--sweep-text", metavar="PATH",
+                    help="with --sweep: also write the per-pattern table as text to PATH; with --from-log: "
+                         "write it from a saved --sweep output instead (no GPU)")
+    ap.add_argument("--from-log", metavar="LOG", help="a saved --sweep output (see --sweep-text)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of a "
                          "`--calib-copy` run into profiles/traffic_counters.json and exit")
@@ -227,6 +231,14 @@ def main():
         return ingest_counters(args)
     if args.ingest_comparator:
         return ingest_comparator_counters(args)
+    if args.from_log:
+        if not args.sweep_text:
+            print("--from-log needs --sweep-text PATH", file=sys.stderr)
+            return 2
+        with open(args.from_log) as f:
+            summary = [json.loads(l) for l in f if l.startswith("{") and '"sweep"' in l][-1]
+        write_sweep_text(summary, args.sweep_text)
+        return 0
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(rows would shard across GPUs with no exchange); run with --gpus 1.",
@@ -756,7 +768,8 @@ def sweep(args) -> int:
         if args.families:
             row["families"] = time_families(p, batch, Wt, Xt, Yt, nset, dt, lib, sp, stream, torch, libks)
             best = min(row["families"], key=lambda f: f["ms"])
-            row["best"] = {"kernel": best["kernel"], "store_waves": best["store_waves"]}
+            row["best"] = {"kernel": best["kernel"], "store_waves": best["store_waves"],
+                           "mfma_tile": best["mfma_tile"]}
         rows.append(row)
         print("%-18s %9.1f us %8.1f GB/s %7.2f TFLOP/s  %s  roofline %.3f   %s" % (
             str(tuple(p)), ms * 1e3, row["GB/s"], row["TFLOP/s"], bound, row["roofline_frac"],
@@ -770,16 +783,63 @@ def sweep(args) -> int:
         extra = {"speedup_vs_permute_bmm_median": round(float(np.median(sp_all)), 3),
                  "speedup_min": round(float(np.min(sp_all)), 3), "speedup_max": round(float(np.max(sp_all)), 3),
                  "faster_than_permute_bmm": int(sum(s > 1.0 for s in sp_all))}
-    print(json.dumps({"sweep": "square n=4096, 16384 rows", "dtype": args.dtype, "patterns": len(rows), **extra,
-                      "roofline_frac_median": round(float(np.median(fr)), 4),
-                      "roofline_frac_min": round(float(np.min(fr)), 4),
-                      "roofline_frac_max": round(float(np.max(fr)), 4), "rows": rows}), flush=True)
+    summary = {"sweep": "square n=4096, 16384 rows", "dtype": args.dtype, "patterns": len(rows), **extra,
+               "roofline_frac_median": round(float(np.median(fr)), 4),
+               "roofline_frac_min": round(float(np.min(fr)), 4),
+               "roofline_frac_max": round(float(np.max(fr)), 4), "rows": rows}
+    print(json.dumps(summary), flush=True)
+    if args.sweep_text:
+        write_sweep_text(summary, args.sweep_text)
     return 0
 
 
-# Kernel families (and store schedules of the matrix-core family) timed per
-# pattern by --sweep --families: (name, ks_kernel_t, ks_store_waves_t).
-FAMILY_VARIANTS = [("mfma/compute", 3, 1), ("mfma/dedicated", 3, 2), ("valu", 2, 0), ("col", 5, 0)]
+def write_sweep_text(summary, path):
+    """The sweep as a text table (one line per pattern, then the fractions by
+    block size): the form kept under profiles/."""
+    import numpy as np
+    rows = summary["rows"]
+    dt = summary["dtype"]
+    peak = BF16_PEAK_TFLOPS if dt == "bf16" else FP32_PEAK_TFLOPS
+    out = ["# Square pattern sweep: every (a, b, b, d) with b in {4, 8, 16, 32, 64, 128}, a * b * d = 4096, "
+           "16,384 rows, %s" % ("bf16 X and weights" if dt == "bf16" else "fp32"),
+           "",
+           "command ($REPO = repository root):  python3 $REPO/bench.py --sweep%s --sweep-text <this file>"
+           % (" --dtype bf16" if dt == "bf16" else ""),
+           "(each pattern on its own seeded inputs; two rotated input/output sets of ~537 MB each, so every "
+           "launch reads",
+           " from HBM; 0.2 s of warm-up launches, then 30 back-to-back launches timed with HIP events on the "
+           "launch stream)",
+           "",
+           "roofline = max(bytes / 8 TB/s, flops / %.1f TFLOP/s) / measured time; bound = the larger term" % peak,
+           "",
+           "pattern               time us       GB/s    TFLOP/s  bound  roofline  plan"]
+    for r in rows:
+        out.append("%-20s %9.1f %10.1f %10.2f %7s %9.3f  %s" % (
+            str(tuple(r["pattern"])), r["ms"] * 1e3, r["GB/s"], r["TFLOP/s"], r["bound"], r["roofline_frac"],
+            r["plan"]))
+    fr = [r["roofline_frac"] for r in rows]
+    small = [r["roofline_frac"] for r in rows if r["pattern"][1] <= 32]
+    b128 = [r["roofline_frac"] for r in rows if r["pattern"][1] == 128]
+    out += ["",
+            "roofline fraction over the %d patterns: median %.3f, min %.3f, max %.3f"
+            % (len(fr), np.median(fr), min(fr), max(fr))]
+    if small:
+        out.append("b = c <= 32 (%d patterns, HBM-bound): median %.3f, min %.3f, max %.3f of 8 TB/s"
+                   % (len(small), np.median(small), min(small), max(small)))
+    if b128:
+        out.append("b = c = 128 (%d patterns, MFMA-bound): %s of %.1f TFLOP/s"
+                   % (len(b128), ", ".join("%.2f" % v for v in b128), peak))
+    with open(path, "w") as f:
+        f.write("\n".join(out) + "\n")
+
+
+# Kernel families (and the matrix-core family's store schedules and tile
+# candidates) timed per pattern by --sweep --families:
+# (name, ks_kernel_t, ks_store_waves_t, mfma tile; 0 = the kernel's own choice).
+FAMILY_VARIANTS = ([("mfma/compute", 3, 1, 0), ("mfma/dedicated", 3, 2, 0)] +
+                   [("mfma/t%d/%s" % (t, sn), 3, sw, t) for t in range(1, 8)
+                    for sn, sw in (("compute", 1), ("dedicated", 2))] +
+                   [("valu", 2, 0, 0), ("col", 5, 0, 0)])
 
 
 def time_families(p, batch, Wt, Xt, Yt, nset, dt, lib, sp, stream, torch, libks):
@@ -788,10 +848,11 @@ def time_families(p, batch, Wt, Xt, Yt, nset, dt, lib, sp, stream, torch, libks)
     warm-up, HIP events); families that refuse the pattern are skipped."""
     out = []
     pat = libks.ks_pattern_t(*p)
-    for name, kernel, store in FAMILY_VARIANTS:
+    for name, kernel, store, tile in FAMILY_VARIANTS:
         opt = libks.ks_options_t()
         opt.kernel = kernel
         opt.store_waves = store
+        opt.mfma_tile = tile
         calls = [(pat, ctypes.c_void_p(Wt.data_ptr()), ctypes.c_void_p(Xt[k].data_ptr()),
                   ctypes.c_void_p(Yt[k].data_ptr()), batch, dt, sp, ctypes.byref(opt)) for k in range(nset)]
         st = lib.ks_matmul_ex(*calls[0])
@@ -807,7 +868,8 @@ def time_families(p, batch, Wt, Xt, Yt, nset, dt, lib, sp, stream, torch, libks)
             lib.ks_matmul_ex(*calls[i % nset])
         e1.record(stream)
         torch.cuda.synchronize()
-        out.append({"name": name, "kernel": kernel, "store_waves": store, "ms": round(e0.elapsed_time(e1) / 30, 5)})
+        out.append({"name": name, "kernel": kernel, "store_waves": store, "mfma_tile": tile,
+                    "ms": round(e0.elapsed_time(e1) / 30, 5)})
     return out
 
 

@@ -102,12 +102,20 @@ typedef enum ks_store_waves_t {
                                MFMAs (needs LDS for two Y tiles)                 */
 } ks_store_waves_t;
 
+/* Tile candidates of the matrix-core kernel: k = 1..KS_MFMA_TILES selects
+   (B-operand register budget, b split) = (32, 1), (64, 1), (128, 1),
+   (128, 2), (64, 2), (128, 4), (64, 4) for the k-th entry. */
+#define KS_MFMA_TILES 7
+
 typedef struct ks_options_t {
     int32_t kernel;         /* a ks_kernel_t value                               */
     int32_t rows_per_block; /* 0 = planner default; else rows per workgroup step */
     int32_t store_waves;    /* a ks_store_waves_t value; MFMA family only;
                                KS_ERR_UNSUPPORTED if the tile cannot use it      */
-    int32_t reserved[5];    /* must be zero                                      */
+    int32_t mfma_tile;      /* 0 = planner choice; 1..KS_MFMA_TILES forces that
+                               tile candidate (MFMA family only);
+                               KS_ERR_UNSUPPORTED if it does not fit the pattern */
+    int32_t reserved[4];    /* must be zero                                      */
 } ks_options_t;
 
 /* Chain flags. */

@@ -569,8 +569,14 @@ bool geom_for(const Shape& s, int xt, int vb, int bsplit, int store_waves, MfmaG
 // part of a row that one tile reads) are at least 32 bytes, else the first
 // that runs at all. Candidates go from the cheapest (32 or 64 B registers
 // per wave, whole blocks) to wider register budgets and split blocks.
-bool choose_geom(const Shape& s, int xt, int store_waves, MfmaGeom* g) {
+// tile: 0 = the first candidate that reads X in runs of >= 32 bytes (or a
+// contiguous tile), else the first that fits; 1..KS_MFMA_TILES = that
+// candidate only.
+bool choose_geom(const Shape& s, int xt, int store_waves, int tile, MfmaGeom* g) {
     static const int kCand[][2] = {{32, 1}, {64, 1}, {128, 1}, {128, 2}, {64, 2}, {128, 4}, {64, 4}};
+    static_assert(sizeof(kCand) / sizeof(kCand[0]) == KS_MFMA_TILES, "tile candidates");
+    if (tile < 0 || tile > KS_MFMA_TILES) return false;
+    if (tile > 0) return geom_for(s, xt, kCand[tile - 1][0], kCand[tile - 1][1], store_waves, g);
     const int eb = elem_bytes(xt);
     bool found = false;
     for (const auto& cand : kCand) {
@@ -664,16 +670,16 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool mfma_supports(const Shape& s, int xt, int wt) {
     (void)wt;
     MfmaGeom g;
-    return choose_geom(s, xt, KS_STORE_AUTO, &g);
+    return choose_geom(s, xt, KS_STORE_AUTO, 0, &g);
 }
 
 bool mfma_lds_supports(const Shape& s, int xt, int wt) { return mfma_supports(s, xt, wt); }
 
 int mfma_describe(const Shape& s, int xt, int wt, int64_t batch, int num_cus, char* buf, size_t len,
-                  int store_waves) {
+                  int store_waves, int mfma_tile) {
     (void)wt;
     MfmaGeom g;
-    if (!choose_geom(s, xt, store_waves, &g) && !choose_geom(s, xt, KS_STORE_AUTO, &g))
+    if (!choose_geom(s, xt, store_waves, mfma_tile, &g) && !choose_geom(s, xt, KS_STORE_AUTO, 0, &g))
         return std::snprintf(buf, len, "mfma: unsupported");
     const int64_t rps = rows_per_split(g, batch, num_cus, 0);
     return std::snprintf(buf, len,
@@ -689,7 +695,7 @@ ks_status_t launch_mfma(const FactorCall& f) { return launch_mfma_lds(f); }
 
 ks_status_t launch_mfma_lds(const FactorCall& f) {
     MfmaGeom g;
-    if (!choose_geom(f.s, f.xt, f.store_waves, &g)) return KS_ERR_UNSUPPORTED;
+    if (!choose_geom(f.s, f.xt, f.store_waves, f.mfma_tile, &g)) return KS_ERR_UNSUPPORTED;
     if (!aligned16(f.X) || !aligned16(f.Y)) return KS_ERR_UNSUPPORTED;
     if ((f.s.n_in * elem_bytes(f.xt)) % 16 != 0 || (f.s.n_out * 4) % 16 != 0) return KS_ERR_UNSUPPORTED;
     const int64_t rps = rows_per_split(g, f.batch, f.num_cus, f.rows_per_block);
