@@ -123,6 +123,15 @@ ks_status_t launch_monarch_pair(const Shape& s0, const Shape& s1, int xt, int wt
 // A run of factors with whole rows resident in LDS (ks_rowchain.hip): n >= 2
 // factors of small blocks whose widest row fits on chip. s, W: n entries.
 bool row_chain_supports(const Shape* s, int n, int xt, int wt);
+
+// The same runs when every factor is square with b in {2, 4} and all sizes
+// are powers of two (butterflies, Walsh-Hadamard): several factors per LDS
+// round trip, in registers (ks_digitchain.hip). launch_row_chain takes it
+// when it applies.
+bool digit_chain_supports(const Shape* s, int n, int xt, int wt);
+ks_status_t launch_digit_chain(const Shape* s, int n, int xt, int wt, const void* const* W, const void* X, float* Y,
+                               int64_t batch, hipStream_t stream);
+int digit_chain_describe(const Shape* s, int n, char* buf, size_t len);
 ks_status_t launch_row_chain(const Shape* s, int n, int xt, int wt, const void* const* W, const void* X, float* Y,
                              int64_t batch, hipStream_t stream);
 int row_chain_describe(const Shape* s, int n, char* buf, size_t len);

@@ -474,6 +474,16 @@ ROW_CHAINS = {
     "radix4_n64": (_radix(4, 3), 1000),
     "uneven_blocks": ([(4, 2, 8, 16), (8, 8, 2, 8), (32, 1, 16, 1)], 77),
     "odd_c3": ([(1, 6, 2, 3), (3, 2, 3, 2), (2, 2, 3, 2)], 203),
+    # square power-of-two blocks (several factors per LDS round trip): the
+    # reversed butterfly, mixed radix, a digit mixed twice in a row, digits
+    # out of order, the 16-point Hadamard shape at a ragged row count
+    "radix2_reversed_n1024": (_radix(2, 10)[::-1], 333),
+    "radix4_reversed_n256": (_radix(4, 4)[::-1], 1001),
+    "mixed_radix_n64": ([(1, 4, 4, 16), (4, 2, 2, 8), (8, 2, 2, 4), (16, 2, 2, 2), (32, 2, 2, 1)], 257),
+    "repeated_digit_n32": ([(4, 2, 2, 4), (4, 2, 2, 4), (2, 2, 2, 8), (8, 4, 4, 1), (16, 2, 2, 1)], 1025),
+    "digits_out_of_order_n64": ([(4, 2, 2, 8), (4, 4, 4, 4), (32, 2, 2, 1), (1, 4, 4, 16), (2, 2, 2, 16),
+                                 (8, 2, 2, 4)], 515),
+    "radix2_n16": (_radix(2, 4), 3001),
 }
 
 
@@ -481,8 +491,9 @@ ROW_CHAINS = {
 @pytest.mark.parametrize("name", sorted(ROW_CHAINS))
 def test_row_chain(name, bf16):
     """A whole chain of small blocks in one launch, rows resident in LDS
-    (widths up to 4096, ragged row counts, c = 3 on the general path); the
-    same chain one launch per factor agrees with it and with the oracle."""
+    (widths up to 4096, ragged row counts, c = 3 on the general path, square
+    power-of-two blocks on the several-factors-per-pass path); the same
+    chain one launch per factor agrees with it and with the oracle."""
     pats, batch = ROW_CHAINS[name]
     wl = datagen.Workload("rowchain", pats, batch, [1.0 / np.sqrt(p[2]) for p in pats], 90 + len(pats))
     dt = libks.DTYPE_BF16 if bf16 else libks.DTYPE_F32
