@@ -303,12 +303,14 @@ bool geom_for(const Shape& s, int xt, ValuGeom* gm) {
         if (d % vw != 0) return false;
         gm->lane = true;
         gm->dv = (d % 4 == 0) ? 4 : 1;
-        // d = 8: an alpha's outputs for one beta are only two 16-byte runs,
-        // so with beta-major lanes each store would touch a quarter or less
-        // of its cache lines; one beta per thread with lanes ordered
-        // (alpha, beta, run) stores whole lines (measured 2.8 -> 4.4 TB/s on
-        // (128, 4, 4, 8) and 3.1 -> 3.9 on (64, 8, 8, 8); slower from d = 16)
-        gm->ilv = gm->dv == 4 && d / gm->dv <= 2;
+        // d <= 32: an alpha's outputs for one beta are at most 128 bytes, so
+        // with beta-major lanes a store instruction writes pieces of lines
+        // (the other betas' stores fill them later); one beta per thread with
+        // lanes ordered (alpha, beta, run) stores whole lines. Measured
+        // (16,384 rows): (128, 4, 4, 8) 2.8 -> 4.4 TB/s, (64, 8, 8, 8)
+        // 3.1 -> 3.9; (64, 4, 4, 16) 119 -> 107 us, (32, 8, 8, 16) 125 -> 108,
+        // (16, 8, 8, 32) 122 -> 108; (32, 4, 4, 32) unchanged
+        gm->ilv = gm->dv == 4 && d / gm->dv <= 8;
         gm->nb = gm->ilv ? 1 : nb_rule(b, c, gm->dv);
         gm->g = b / gm->nb;
         gm->p = kConsumerThreads / gm->g;
