@@ -119,6 +119,8 @@ def parse():
     ap.add_argument("--ingest-comparator", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="HBM bytes per call of the comparator from two --comparator-only counter runs "
                          "(same --steps / --warmup)")
+    ap.add_argument("--copy-ceiling", action="store_true",
+                    help="time a plain device copy at 64 MiB .. 4 GiB and print one JSON line")
     ap.add_argument("--sweep-text", metavar="PATH",
                     help="with --sweep: also write the per-pattern table as text to PATH; with --from-log: "
                          "write it from a saved --sweep output instead (no GPU)")
@@ -246,6 +248,8 @@ def main():
         return 2
     if args.sweep:
         return sweep(args)
+    if args.copy_ceiling:
+        return copy_ceilings(args)
     if args.comparator_only:
         return comparator_only(args)
     if args.backward:
@@ -587,12 +591,13 @@ def time_factors(wl, Wt, X0, bf16, lib, sp, stream, torch, np, datagen, libks):
 COPY_BYTES = 2 ** 30     # the device copy of copy_ceiling reads and writes this many bytes
 
 
-def copy_ceiling(dev, stream, torch) -> float:
-    """A plain 1 GiB device-to-device copy (torch's copy kernel), timed with
-    HIP events over back-to-back calls after warm-up: GB/s counting the bytes
-    read plus the bytes written. A practical streaming ceiling of this GPU,
-    reported beside the published 8 TB/s peak."""
-    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+def copy_ceiling(dev, stream, torch, nbytes=COPY_BYTES) -> float:
+    """A plain device-to-device copy of nbytes (torch's copy kernel; 1 GiB
+    by default), timed with HIP events over back-to-back calls after
+    warm-up: GB/s counting the bytes read plus the bytes written. A practical
+    streaming ceiling of this GPU, reported beside the published 8 TB/s
+    peak."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
     warm_up(lambda i: dst.copy_(src), 3, torch)
     e0 = torch.cuda.Event(enable_timing=True)
@@ -605,7 +610,23 @@ def copy_ceiling(dev, stream, torch) -> float:
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
     del src, dst
-    return round(2 * COPY_BYTES / (ms * 1e-3) / 1e9, 1)
+    return round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
+
+
+def copy_ceilings(args) -> int:
+    """The copy ceiling at several sizes (the sweep's per-launch traffic is
+    about 256 MiB each way; the butterfly factors move 1 GiB each way); one
+    JSON line."""
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    rows = []
+    for mib in (64, 256, 1024, 4096):
+        gbs = copy_ceiling(dev, stream, torch, mib * 2 ** 20)
+        rows.append({"bytes_each_way": mib * 2 ** 20, "GB/s": gbs, "frac_of_8TBs": round(gbs / HBM_PEAK_GBS, 4)})
+    print(json.dumps({"copy_ceiling": "torch device copy, read + write bytes", "rows": rows}), flush=True)
+    return 0
 
 
 def backward(args) -> int:
