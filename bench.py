@@ -57,7 +57,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 # and the headers: its traffic counters stay valid while these are unchanged.
 # Workloads not listed are keyed on every source.
 WORKLOAD_SOURCES = {
-    "butterfly65536": ("ks_mfma.hip", "ks_slab.hip"),
+    "butterfly65536": ("ks_mfma.hip", "ks_slab.hip", "ks_valu.hip"),
     "vit_mlp": ("ks_mfma.hip",),
     "gpt2_mlp": ("ks_fused.hip",),
     "gpt2_mlp:nofuse": ("ks_mfma.hip", "ks_valu.hip"),
@@ -119,6 +119,9 @@ def parse():
     ap.add_argument("--ingest-comparator", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="HBM bytes per call of the comparator from two --comparator-only counter runs "
                          "(same --steps / --warmup)")
+    ap.add_argument("--workload-factors", action="store_true",
+                    help="with --sweep: also time each factor of the butterfly, ViT and GPT-2 workloads alone, "
+                         "at the workload's batch (table rows for the launches those chains make)")
     ap.add_argument("--copy-ceiling", action="store_true",
                     help="time a plain device copy at 64 MiB .. 4 GiB and print one JSON line")
     ap.add_argument("--sweep-text", metavar="PATH",
@@ -744,8 +747,20 @@ def sweep(args) -> int:
     sp = ctypes.c_void_p(int(stream.cuda_stream))
     peak_flops = BF16_PEAK_TFLOPS if bf16 else FP32_PEAK_TFLOPS
     rows = []
-    for p in datagen.square_sweep_patterns():
-        wl = datagen.get("square_%d_%d_%d_%d" % p)
+    items = [(p, datagen.get("square_%d_%d_%d_%d" % p), "square") for p in datagen.square_sweep_patterns()]
+    if args.workload_factors:
+        # each factor of these workloads alone, at the workload's batch (the
+        # launches a chain makes for factors it does not fuse)
+        seen = set(tuple(p) for p, _, _ in items)
+        for name in WORKLOAD_FACTOR_SETS:
+            src = datagen.get(name)
+            for k, p in enumerate(src.patterns):
+                if tuple(p) in seen:
+                    continue
+                seen.add(tuple(p))
+                items.append((tuple(p), datagen.Workload(name, [tuple(p)], src.batch, [src.sigmas[k]],
+                                                         src.seed + 100 + k), name))
+    for p, wl, set_name in items:
         X, Ws = datagen.draw(wl)
         put = ((lambda a: torch.from_numpy(datagen.bf16_bits(a).view(np.int16)).to(dev).view(torch.bfloat16))
                if bf16 else (lambda a: torch.from_numpy(a).to(dev)))
@@ -776,7 +791,7 @@ def sweep(args) -> int:
         ms = e0.elapsed_time(e1) / steps
         t_roof = max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (peak_flops * 1e12))
         bound = "hbm" if nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (peak_flops * 1e12) else "mfma"
-        row = {"pattern": list(p), "ms": round(ms, 5),
+        row = {"pattern": list(p), "set": set_name, "batch": batch, "ms": round(ms, 5),
                "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
                "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
                "bound": bound,
@@ -797,7 +812,7 @@ def sweep(args) -> int:
             ("permute-bmm %.1f us, x%.2f  " % (row["comparator_ms"] * 1e3, row["speedup"])
              if "speedup" in row else "") + row["plan"][:60]), flush=True)
         del Xt, Yt, Wt, X, Ws
-    fr = [r["roofline_frac"] for r in rows]
+    fr = [r["roofline_frac"] for r in rows if r["set"] == "square"]
     extra = {}
     sp_all = [r["speedup"] for r in rows if "speedup" in r]
     if sp_all:
@@ -812,6 +827,10 @@ def sweep(args) -> int:
     if args.sweep_text:
         write_sweep_text(summary, args.sweep_text)
     return 0
+
+
+# workloads whose factors --workload-factors adds to the sweep
+WORKLOAD_FACTOR_SETS = ("butterfly65536", "vit_mlp", "gpt2_mlp")
 
 
 def write_sweep_text(summary, path):
@@ -835,14 +854,15 @@ def write_sweep_text(summary, path):
            "",
            "pattern               time us       GB/s    TFLOP/s  bound  roofline  plan"]
     for r in rows:
-        out.append("%-20s %9.1f %10.1f %10.2f %7s %9.3f  %s" % (
+        out.append("%-20s %9.1f %10.1f %10.2f %7s %9.3f  %s%s" % (
             str(tuple(r["pattern"])), r["ms"] * 1e3, r["GB/s"], r["TFLOP/s"], r["bound"], r["roofline_frac"],
-            r["plan"]))
-    fr = [r["roofline_frac"] for r in rows]
-    small = [r["roofline_frac"] for r in rows if r["pattern"][1] <= 32]
-    b128 = [r["roofline_frac"] for r in rows if r["pattern"][1] == 128]
+            "" if r.get("set", "square") == "square" else "[%s, %d rows] " % (r["set"], r["batch"]), r["plan"]))
+    square = [r for r in rows if r.get("set", "square") == "square"]
+    fr = [r["roofline_frac"] for r in square]
+    small = [r["roofline_frac"] for r in square if r["pattern"][1] <= 32]
+    b128 = [r["roofline_frac"] for r in square if r["pattern"][1] == 128]
     out += ["",
-            "roofline fraction over the %d patterns: median %.3f, min %.3f, max %.3f"
+            "roofline fraction over the %d square patterns: median %.3f, min %.3f, max %.3f"
             % (len(fr), np.median(fr), min(fr), max(fr))]
     if small:
         out.append("b = c <= 32 (%d patterns, HBM-bound): median %.3f, min %.3f, max %.3f of 8 TB/s"
