@@ -805,7 +805,7 @@ def sweep(args) -> int:
             row["families"] = time_families(p, batch, Wt, Xt, Yt, nset, dt, lib, sp, stream, torch, libks)
             best = min(row["families"], key=lambda f: f["ms"])
             row["best"] = {"kernel": best["kernel"], "store_waves": best["store_waves"],
-                           "mfma_tile": best["mfma_tile"]}
+                           "mfma_tile": best["mfma_tile"], "mfma_loaders": best["mfma_loaders"]}
         rows.append(row)
         print("%-18s %9.1f us %8.1f GB/s %7.2f TFLOP/s  %s  roofline %.3f   %s" % (
             str(tuple(p)), ms * 1e3, row["GB/s"], row["TFLOP/s"], bound, row["roofline_frac"],
@@ -874,13 +874,15 @@ def write_sweep_text(summary, path):
         f.write("\n".join(out) + "\n")
 
 
-# Kernel families (and the matrix-core family's store schedules and tile
-# candidates) timed per pattern by --sweep --families:
-# (name, ks_kernel_t, ks_store_waves_t, mfma tile; 0 = the kernel's own choice).
-FAMILY_VARIANTS = ([("mfma/compute", 3, 1, 0), ("mfma/dedicated", 3, 2, 0)] +
-                   [("mfma/t%d/%s" % (t, sn), 3, sw, t) for t in range(1, 8)
+# Kernel families (and the matrix-core family's store schedules, tile
+# candidates and loader waves) timed per pattern by --sweep --families:
+# (name, ks_kernel_t, ks_store_waves_t, mfma tile, mfma loaders; 0 = the
+# kernel's own choice).
+FAMILY_VARIANTS = ([("mfma/compute", 3, 1, 0, 0), ("mfma/dedicated", 3, 2, 0, 0)] +
+                   [("mfma/t%d/%s" % (t, sn), 3, sw, t, 0) for t in range(1, 8)
                     for sn, sw in (("compute", 1), ("dedicated", 2))] +
-                   [("valu", 2, 0, 0), ("col", 5, 0, 0)])
+                   [("mfma/2l/compute", 3, 1, 0, 2), ("mfma/2l/dedicated", 3, 2, 0, 2)] +
+                   [("valu", 2, 0, 0, 0), ("col", 5, 0, 0, 0)])
 
 
 def time_families(p, batch, Wt, Xt, Yt, nset, dt, lib, sp, stream, torch, libks):
@@ -889,11 +891,12 @@ def time_families(p, batch, Wt, Xt, Yt, nset, dt, lib, sp, stream, torch, libks)
     warm-up, HIP events); families that refuse the pattern are skipped."""
     out = []
     pat = libks.ks_pattern_t(*p)
-    for name, kernel, store, tile in FAMILY_VARIANTS:
+    for name, kernel, store, tile, loaders in FAMILY_VARIANTS:
         opt = libks.ks_options_t()
         opt.kernel = kernel
         opt.store_waves = store
         opt.mfma_tile = tile
+        opt.mfma_loaders = loaders
         calls = [(pat, ctypes.c_void_p(Wt.data_ptr()), ctypes.c_void_p(Xt[k].data_ptr()),
                   ctypes.c_void_p(Yt[k].data_ptr()), batch, dt, sp, ctypes.byref(opt)) for k in range(nset)]
         st = lib.ks_matmul_ex(*calls[0])
@@ -910,7 +913,7 @@ def time_families(p, batch, Wt, Xt, Yt, nset, dt, lib, sp, stream, torch, libks)
         e1.record(stream)
         torch.cuda.synchronize()
         out.append({"name": name, "kernel": kernel, "store_waves": store, "mfma_tile": tile,
-                    "ms": round(e0.elapsed_time(e1) / 30, 5)})
+                    "mfma_loaders": loaders, "ms": round(e0.elapsed_time(e1) / 30, 5)})
     return out
 
 

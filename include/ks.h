@@ -115,7 +115,10 @@ typedef struct ks_options_t {
     int32_t mfma_tile;      /* 0 = planner choice; 1..KS_MFMA_TILES forces that
                                tile candidate (MFMA family only);
                                KS_ERR_UNSUPPORTED if it does not fit the pattern */
-    int32_t reserved[4];    /* must be zero                                      */
+    int32_t mfma_loaders;   /* 0 = planner choice; 1 or 2 waves streaming X into
+                               LDS (MFMA family only; 2 needs c >= 64, else
+                               KS_ERR_UNSUPPORTED)                               */
+    int32_t reserved[3];    /* must be zero                                      */
 } ks_options_t;
 
 /* Chain flags. */

@@ -72,7 +72,8 @@ ks_status_t check_options(const ks_options_t* opt) {
     if (opt->rows_per_block < 0 || opt->rows_per_block > 4096) return KS_ERR_INVALID;
     if (opt->store_waves < KS_STORE_AUTO || opt->store_waves > KS_STORE_DEDICATED) return KS_ERR_INVALID;
     if (opt->mfma_tile < 0 || opt->mfma_tile > KS_MFMA_TILES) return KS_ERR_INVALID;
-    for (int i = 0; i < 4; ++i)
+    if (opt->mfma_loaders < 0 || opt->mfma_loaders > 2) return KS_ERR_INVALID;
+    for (int i = 0; i < 3; ++i)
         if (opt->reserved[i] != 0) return KS_ERR_INVALID;
     return KS_OK;
 }
@@ -102,11 +103,11 @@ ks_status_t current_cus(int* cus) {
 // plan_table.py; the pages' "simple heuristic" on the pattern parameters has
 // no published form, so it is fitted here).
 struct PlanEntry {
-    int a, b, c, d, xt, wt, kernel, store_waves, mfma_tile;
+    int a, b, c, d, xt, wt, kernel, store_waves, mfma_tile, mfma_loaders;
 };
 const PlanEntry kPlanTable[] = {
 #include "ks_plan_table.inc"
-    {0, 0, 0, 0, 0, 0, 0, 0, 0}  // end
+    {0, 0, 0, 0, 0, 0, 0, 0, 0, 0}  // end
 };
 
 bool family_supports(int kernel, const Shape& s, int xt, int wt) {
@@ -126,18 +127,18 @@ bool family_supports(int kernel, const Shape& s, int xt, int wt) {
 // tiles (measured faster than the VALU kernel from b = c = 16 up), else the
 // VALU kernel, else the generic one.
 struct Choice {
-    int kernel, store_waves, mfma_tile;
+    int kernel, store_waves, mfma_tile, mfma_loaders;
 };
 
 Choice choose_kernel(const Shape& s, int xt, int wt) {
     for (const PlanEntry* e = kPlanTable; e->a != 0; ++e)
         if (e->a == s.a && e->b == s.b && e->c == s.c && e->d == s.d && e->xt == xt && e->wt == wt &&
             family_supports(e->kernel, s, xt, wt))
-            return {e->kernel, e->store_waves, e->mfma_tile};
-    if (ks::col_preferred(s, xt, wt)) return {KS_KERNEL_COLUMN, KS_STORE_AUTO, 0};
-    if (ks::mfma_supports(s, xt, wt)) return {KS_KERNEL_MFMA, KS_STORE_AUTO, 0};
-    if (ks::valu_supports(s, xt, wt)) return {KS_KERNEL_VALU, KS_STORE_AUTO, 0};
-    return {KS_KERNEL_GENERIC, KS_STORE_AUTO, 0};
+            return {e->kernel, e->store_waves, e->mfma_tile, e->mfma_loaders};
+    if (ks::col_preferred(s, xt, wt)) return {KS_KERNEL_COLUMN, KS_STORE_AUTO, 0, 0};
+    if (ks::mfma_supports(s, xt, wt)) return {KS_KERNEL_MFMA, KS_STORE_AUTO, 0, 0};
+    if (ks::valu_supports(s, xt, wt)) return {KS_KERNEL_VALU, KS_STORE_AUTO, 0, 0};
+    return {KS_KERNEL_GENERIC, KS_STORE_AUTO, 0, 0};
 }
 
 ks_status_t launch_family(int kernel, const ks::FactorCall& f) {
@@ -160,8 +161,10 @@ ks_status_t run_factor(int kernel, const ks::FactorCall& f) {
     ks::FactorCall g = f;
     if (g.store_waves == KS_STORE_AUTO) g.store_waves = chosen.store_waves;
     if (g.mfma_tile == 0) g.mfma_tile = chosen.mfma_tile;
+    if (g.mfma_loaders == 0) g.mfma_loaders = chosen.mfma_loaders;
     ks_status_t st = launch_family(chosen.kernel, g);
-    if (st == KS_ERR_UNSUPPORTED && (g.store_waves != f.store_waves || g.mfma_tile != f.mfma_tile))
+    if (st == KS_ERR_UNSUPPORTED &&
+        (g.store_waves != f.store_waves || g.mfma_tile != f.mfma_tile || g.mfma_loaders != f.mfma_loaders))
         st = launch_family(chosen.kernel, f);
     if (st == KS_ERR_UNSUPPORTED && chosen.kernel != KS_KERNEL_GENERIC) st = ks::launch_generic(f);
     return st;
@@ -287,6 +290,7 @@ ks_status_t matmul_impl(ks_pattern_t p, const void* W, const void* X, void* Y, i
     f.rows_per_block = opt ? opt->rows_per_block : 0;
     f.store_waves = opt ? opt->store_waves : KS_STORE_AUTO;
     f.mfma_tile = opt ? opt->mfma_tile : 0;
+    f.mfma_loaders = opt ? opt->mfma_loaders : 0;
     st = current_cus(&f.num_cus);
     if (st != KS_OK) return st;
     return run_factor(kernel, f);
@@ -570,7 +574,8 @@ ks_status_t ks_plan_describe(ks_pattern_t p, int64_t batch, ks_dtype_t dt, char*
     if (kernel == KS_KERNEL_COLUMN) ks::col_describe(s, xt, wt, batch, cus, buf, len);
     else if (kernel == KS_KERNEL_VALU) ks::valu_describe(s, xt, wt, batch, cus, buf, len);
     else if (kernel == KS_KERNEL_MFMA)
-        ks::mfma_describe(s, xt, wt, batch, cus, buf, len, choice.store_waves, choice.mfma_tile);
+        ks::mfma_describe(s, xt, wt, batch, cus, buf, len, choice.store_waves, choice.mfma_tile,
+                          choice.mfma_loaders);
     else std::snprintf(buf, len, "generic: one thread per output");
     return KS_OK;
 }

@@ -59,6 +59,7 @@ struct FactorCall {
     int rows_per_block;    // 0 = default
     int store_waves;       // ks_store_waves_t (MFMA family)
     int mfma_tile = 0;     // 0 = planner choice, else a tile candidate 1..KS_MFMA_TILES (MFMA family)
+    int mfma_loaders = 0;  // 0 = planner choice (one), 1 or 2 loader waves (MFMA family)
 };
 
 // Kernel launchers. Each returns KS_OK, KS_ERR_UNSUPPORTED when the family
@@ -82,7 +83,7 @@ bool mfma_lds_supports(const Shape& s, int xt, int wt);
 // Planner description of the VALU / MFMA tiles (pure host).
 int valu_describe(const Shape& s, int xt, int wt, int64_t batch, int num_cus, char* buf, size_t len);
 int mfma_describe(const Shape& s, int xt, int wt, int64_t batch, int num_cus, char* buf, size_t len,
-                  int store_waves = KS_STORE_AUTO, int mfma_tile = 0);
+                  int store_waves = KS_STORE_AUTO, int mfma_tile = 0, int mfma_loaders = 0);
 
 // Fused pair of factors (intermediate kept in LDS). Returns KS_ERR_UNSUPPORTED
 // when the pair does not fit the fused kernel.

@@ -190,8 +190,15 @@ __device__ __forceinline__ void store_tile_rows(const A& args, const StoreTeam& 
 // barrier. NS > 0: NS storer waves store tile s-1 from one of two Y buffers
 // while the compute waves run the MFMAs of step s into the other, so the
 // stores drain during the contraction instead of after it.
-template <typename TX, typename TW, int BT, int C, int NS, int VB>
-__global__ __launch_bounds__(kStreamThreads + 64 * NS) void mfma_kernel(const TX* __restrict__ X,
+// NL loader waves: with two, each issues every other instruction of every
+// stage and waits for its own (more LDS-DMA issue per step; measured faster
+// on the b = c = 128 patterns with d >= 4, slower on others, so the fitted
+// planner table chooses it per pattern).
+template <int NL>
+constexpr int mfma_load_end() { return kConsumerThreads + 64 * NL; }
+
+template <typename TX, typename TW, int BT, int C, int NS, int VB, int NL>
+__global__ __launch_bounds__(mfma_load_end<NL>() + 64 * NS) void mfma_kernel(const TX* __restrict__ X,
                                                                         const TW* __restrict__ K,
                                                                         float* __restrict__ Y, MfmaArgs args) {
     constexpr int EB = int(sizeof(TX));
@@ -232,14 +239,14 @@ __global__ __launch_bounds__(kStreamThreads + 64 * NS) void mfma_kernel(const TX
     const int xblk_bytes = args.xmap.blk_vec * 16;   // no per-block padding in X stages
 
     if constexpr (NS > 0) {
-        if (t >= kStreamThreads) {
+        if (t >= mfma_load_end<NL>()) {
             // ---------------------------------------------------- storer waves
             // Issue priority over the compute waves on the same SIMD: their
             // MFMA bursts otherwise delay the stores (measured 4-9 % on the
             // ViT and b = c = 128 shapes).
             __builtin_amdgcn_s_setprio(3);
             StoreTeam team;
-            make_store_team(args, t - kStreamThreads, 64 * NS, at_eff, dt_eff, &team);
+            make_store_team(args, t - mfma_load_end<NL>(), 64 * NS, at_eff, dt_eff, &team);
             auto store_tile = [&](int s) {
                 const int64_t n0 = row_begin + int64_t(s) * R;
                 store_tile_rows<8>(args, team, ys0 + (s & 1) * args.ytile_bytes, Y + n0 * args.n_out + yg0,
@@ -261,16 +268,24 @@ __global__ __launch_bounds__(kStreamThreads + 64 * NS) void mfma_kernel(const TX
         const int valid_blocks = contig ? at_eff : args.xmap.blocks;
         const int valid_vec = contig ? args.xmap.blk_vec : dt_eff / VWX;
         make_loader_plan<kMaxInsts>(args.xmap, args.insts, VWX, EB, args.n_in, valid_blocks, valid_vec,
-                                    t - kConsumerThreads, &lp);
+                                    (t - kConsumerThreads) & 63, &lp);
+        const int L = (t - kConsumerThreads) >> 6;                // loader wave
+        const int own = (args.insts - L + NL - 1) / NL;          // its instructions per stage
         auto issue = [&](int s) {
             const int64_t n0 = row_begin + int64_t(s) * R;
-            issue_stage<kMaxInsts>(lp, args.insts, X + n0 * args.n_in + xg0,
-                                   stage_limit(n0, row_end, args.n_in, EB), lds + (s % kStages) * kStageBytes);
+            if constexpr (NL == 1) {
+                issue_stage<kMaxInsts>(lp, args.insts, X + n0 * args.n_in + xg0,
+                                       stage_limit(n0, row_end, args.n_in, EB), lds + (s % kStages) * kStageBytes);
+            } else {
+                issue_stage_part<kMaxInsts>(lp, args.insts, X + n0 * args.n_in + xg0,
+                                            stage_limit(n0, row_end, args.n_in, EB),
+                                            lds + (s % kStages) * kStageBytes, L, NL);
+            }
         };
         for (int s = 0; s < kStages - 1 && s < nsteps; ++s) issue(s);
         for (int s = 0; s < nsteps; ++s) {
             // stage s has landed once only the stages issued after it remain
-            wait_vmcnt_upto(min(kStages - 2, nsteps - 1 - s) * args.insts);
+            wait_vmcnt_upto(min(63, min(kStages - 2, nsteps - 1 - s) * own));
             lds_barrier();                                   // stage s ready
             if (s + kStages - 1 < nsteps) issue(s + kStages - 1);
             lds_barrier();                                   // Y tile written
@@ -616,14 +631,25 @@ int64_t rows_per_split(const MfmaGeom& g, int64_t batch, int num_cus, int rows_p
     return steps * g.r;
 }
 
+template <typename TX, typename TW, int BT, int C, int VB, int NL>
+ks_status_t launch_nl(const FactorCall& f, const MfmaGeom& g, const MfmaArgs& args, dim3 grid) {
+    constexpr int end = mfma_load_end<NL>();
+    if (g.ns == 1)
+        return launch_kernel(mfma_kernel<TX, TW, BT, C, 1, VB, NL>, grid, dim3(end + 64), g.lds, f.stream,
+                             static_cast<const TX*>(f.X), static_cast<const TW*>(f.W), f.Y, args);
+    return launch_kernel(mfma_kernel<TX, TW, BT, C, 0, VB, NL>, grid, dim3(end), g.lds, f.stream,
+                         static_cast<const TX*>(f.X), static_cast<const TW*>(f.W), f.Y, args);
+}
+
 template <typename TX, typename TW, int BT, int C, int VB>
 ks_status_t launch_vb(const FactorCall& f, const MfmaGeom& g, const MfmaArgs& args, dim3 grid) {
     if constexpr (mfma_stage_insts(BT, C, int(sizeof(TX)), VB) <= 63) {
-        if (g.ns == 1)
-            return launch_kernel(mfma_kernel<TX, TW, BT, C, 1, VB>, grid, dim3(kStreamThreads + 64), g.lds,
-                                 f.stream, static_cast<const TX*>(f.X), static_cast<const TW*>(f.W), f.Y, args);
-        return launch_kernel(mfma_kernel<TX, TW, BT, C, 0, VB>, grid, dim3(kStreamThreads), g.lds, f.stream,
-                             static_cast<const TX*>(f.X), static_cast<const TW*>(f.W), f.Y, args);
+        // two loader waves only for the large blocks, where they can pay
+        if constexpr (C >= 64) {
+            if (f.mfma_loaders == 2) return launch_nl<TX, TW, BT, C, VB, 2>(f, g, args, grid);
+        }
+        if (f.mfma_loaders > 1) return KS_ERR_UNSUPPORTED;
+        return launch_nl<TX, TW, BT, C, VB, 1>(f, g, args, grid);
     } else {
         return KS_ERR_UNSUPPORTED;
     }
@@ -676,7 +702,7 @@ bool mfma_supports(const Shape& s, int xt, int wt) {
 bool mfma_lds_supports(const Shape& s, int xt, int wt) { return mfma_supports(s, xt, wt); }
 
 int mfma_describe(const Shape& s, int xt, int wt, int64_t batch, int num_cus, char* buf, size_t len,
-                  int store_waves, int mfma_tile) {
+                  int store_waves, int mfma_tile, int mfma_loaders) {
     (void)wt;
     MfmaGeom g;
     if (!choose_geom(s, xt, store_waves, mfma_tile, &g) && !choose_geom(s, xt, KS_STORE_AUTO, 0, &g))
@@ -684,11 +710,11 @@ int mfma_describe(const Shape& s, int xt, int wt, int64_t batch, int num_cus, ch
     const int64_t rps = rows_per_split(g, batch, num_cus, 0);
     return std::snprintf(buf, len,
                          "mfma 16x16x4f32: pairs/tile=%d (alphas=%d deltas=%d %s) outputs/tile=%d of %d "
-                         "B regs=%d rows/wg=%lld wgs=%lld stages=%d x %d KB storers=%d lds=%zu",
+                         "B regs=%d rows/wg=%lld wgs=%lld stages=%d x %d KB storers=%d loaders=%d lds=%zu",
                          g.tp, g.at, g.dt, g.contiguous ? "contiguous" : "segmented", g.bt, s.b, g.vb,
                          static_cast<long long>(rps),
                          static_cast<long long>(g.n_tiles * ((batch + rps - 1) / std::max<int64_t>(rps, 1))),
-                         g.stages, g.insts, g.ns, g.lds);
+                         g.stages, g.insts, g.ns, (mfma_loaders == 2 && s.c >= 64) ? 2 : 1, g.lds);
 }
 
 ks_status_t launch_mfma(const FactorCall& f) { return launch_mfma_lds(f); }

@@ -115,6 +115,22 @@ __device__ __forceinline__ void issue_stage(const LoaderPlan<kMaxInsts>& lp, int
     }
 }
 
+// The part of a stage that loader wave `part` of `parts` issues: every
+// instruction i with i % parts == part (the same addresses as issue_stage).
+template <int kMaxInsts, typename T>
+__device__ __forceinline__ void issue_stage_part(const LoaderPlan<kMaxInsts>& lp, int insts, const T* first,
+                                                 uint32_t limit, unsigned char* stage, int part, int parts) {
+    const char* base = reinterpret_cast<const char*>(first);
+#pragma unroll
+    for (int i = 0; i < kMaxInsts; ++i) {
+        if (i < insts && i % parts == part) {
+            const uint32_t o = lp.off[i];
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + (o < limit ? o : 0u)),
+                                             stage + 1024 * i, 16, 0, 0);
+        }
+    }
+}
+
 // The byte limit of issue_stage for a stage whose first row is n0.
 __device__ __forceinline__ uint32_t stage_limit(int64_t n0, int64_t row_end, int64_t n_in, int eb) {
     const int64_t bytes = (row_end - n0) * n_in * eb;

@@ -55,7 +55,8 @@ MFMA_TILES = 7   # KS_MFMA_TILES: tile candidates of the matrix-core kernel
 
 class ks_options_t(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("rows_per_block", ctypes.c_int32),
-                ("store_waves", ctypes.c_int32), ("mfma_tile", ctypes.c_int32), ("reserved", ctypes.c_int32 * 4)]
+                ("store_waves", ctypes.c_int32), ("mfma_tile", ctypes.c_int32), ("mfma_loaders", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 3)]
 
 
 _lib = None
@@ -177,11 +178,12 @@ def ks_matmul(p, W, X, Y, batch: int, dtype: int, stream=None, check: bool = Tru
 
 def ks_matmul_ex(p, W, X, Y, batch: int, dtype: int, stream=None, kernel: int = KERNEL_AUTO,
                  rows_per_block: int = 0, check: bool = True, reserved=None, store_waves=STORE_AUTO,
-                 mfma_tile: int = 0) -> int:
+                 mfma_tile: int = 0, mfma_loaders: int = 0) -> int:
     opt = ks_options_t()
     opt.kernel = KERNELS.get(kernel, kernel) if isinstance(kernel, str) else int(kernel)
     opt.rows_per_block = int(rows_per_block)
     opt.mfma_tile = int(mfma_tile)
+    opt.mfma_loaders = int(mfma_loaders)
     opt.store_waves = STORE_WAVES.get(store_waves, store_waves) if isinstance(store_waves, str) else int(store_waves)
     if reserved is not None:
         for i, v in enumerate(reserved):

@@ -97,7 +97,9 @@ def test_options():
     assert st((2, 2, 2, 2), kernel=99) == libks.KS_ERR_INVALID
     assert st((2, 2, 2, 2), rows_per_block=-1) == libks.KS_ERR_INVALID
     assert st((2, 2, 2, 2), reserved=[1]) == libks.KS_ERR_INVALID
-    assert st((2, 2, 2, 2), reserved=[0, 0, 0, 1]) == libks.KS_ERR_INVALID
+    assert st((2, 2, 2, 2), reserved=[0, 0, 1]) == libks.KS_ERR_INVALID
+    assert st((2, 2, 2, 2), mfma_loaders=3) == libks.KS_ERR_INVALID
+    assert st((2, 2, 2, 2), mfma_loaders=-1) == libks.KS_ERR_INVALID
     assert st((2, 2, 2, 2), mfma_tile=-1) == libks.KS_ERR_INVALID
     assert st((2, 2, 2, 2), mfma_tile=libks.MFMA_TILES + 1) == libks.KS_ERR_INVALID
     assert st((2, 2, 2, 2), store_waves=3) == libks.KS_ERR_INVALID
@@ -328,11 +330,12 @@ def test_planner_follows_fitted_table():
               libks.KERNEL_GENERIC: "generic"}
     n = 0
     for line in open(inc):
-        m = re.match(r"\{(\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)(?:, (\d+))?\},", line)
+        m = re.match(r"\{(\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)(?:, (\d+))?(?:, (\d+))?\},", line)
         if not m:
             continue
         a, b, c, d, xt, wt, kernel, store = (int(v) for v in m.groups()[:8])
         tile = int(m.group(9) or 0)
+        loaders = int(m.group(10) or 0)
         dt = {(0, 0): libks.DTYPE_F32, (1, 1): libks.DTYPE_BF16, (0, 1): libks.DTYPE_BF16W}[(xt, wt)]
         desc = libks.ks_plan_describe((a, b, c, d), 16384, dt)
         assert desc.startswith(prefix[kernel]), ((a, b, c, d), kernel, desc)
@@ -342,5 +345,7 @@ def test_planner_follows_fitted_table():
             # candidate K: (B-register budget, b split) as listed in ks.h
             vb, split = [(32, 1), (64, 1), (128, 1), (128, 2), (64, 2), (128, 4), (64, 4)][tile - 1]
             assert "B regs=%d " % vb in desc and "outputs/tile=%d of %d " % (b // split, b) in desc, (tile, desc)
+        if kernel == libks.KERNEL_MFMA:
+            assert ("loaders=2" in desc) == (loaders == 2), (loaders, desc)
         n += 1
     assert n >= 51

@@ -461,6 +461,38 @@ def test_monarch_chain_full_size(bf16, fuse):
     _chain_workload("monarch_n1024", bf16, fuse)
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("store", [libks.STORE_COMPUTE, libks.STORE_DEDICATED])
+@pytest.mark.parametrize("p", [(1, 128, 128, 32), (4, 128, 128, 8), (8, 128, 128, 4), (2, 64, 64, 32), (8, 64, 64, 8)],
+                         ids=lambda v: "%d_%d_%d_%d" % v)
+def test_mfma_two_loader_waves(p, store, bf16):
+    """The matrix-core kernel with two loader waves (each issuing every other
+    LDS-DMA instruction of a stage) on segmented and contiguous tiles, with
+    either store schedule and a ragged row count: the same result as one
+    loader wave, and the oracle's. Blocks narrower than 64 refuse it."""
+    a, b, c, d = p
+    batch = 1001
+    X, W = datagen.random_pattern_inputs(p, batch, 120 + a)
+    Xt, Wt = to_dev(X, bf16), to_dev(W, bf16)
+    dt = libks.DTYPE_BF16 if bf16 else libks.DTYPE_F32
+    outs = []
+    for loaders in (1, 2):
+        Y = torch.full((batch, a * b * d), float("nan"), device=DEV)
+        st = libks.ks_matmul_ex(p, Wt, Xt, Y, batch, dt, kernel="mfma", store_waves=store, mfma_loaders=loaders,
+                                check=False)
+        if st == libks.KS_ERR_UNSUPPORTED and store == libks.STORE_DEDICATED:
+            pytest.skip("this tile has no room for a storer wave")
+        assert st == 0, st
+        torch.cuda.synchronize()
+        outs.append(Y.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+    check_factor(p, X, W, outs[1], bf16=bf16)
+    Y = torch.empty((10, 4 * 64 * 6), device=DEV)
+    Xs, Ws = datagen.random_pattern_inputs((4, 64, 16, 6), 10, 3)
+    assert libks.ks_matmul_ex((4, 64, 16, 6), to_dev(Ws), to_dev(Xs), Y, 10, libks.DTYPE_F32, kernel="mfma",
+                              mfma_loaders=2, check=False) == libks.KS_ERR_UNSUPPORTED
+
+
 def _radix(r, L):
     """Factors (r^k, r, r, r^(L-1-k)), k = 0..L-1: a radix-r butterfly on n = r^L."""
     return [(r ** k, r, r, r ** (L - 1 - k)) for k in range(L)]
