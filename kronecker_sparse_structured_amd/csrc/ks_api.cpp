@@ -520,7 +520,7 @@ ks_status_t ks_chain_matmul(const ks_pattern_t* p, int n, const void* const* W,
                                       W[k], W[k + 1], cur, out, batch, stream, cus);
         } else if (plan.group_kind[g] == 3) {
             st = ks::launch_row_chain(&plan.shapes[k], plan.group_len[g], cur_t, plan.wt, W + k, cur, out, batch,
-                                      stream);
+                                      stream, cus);
         } else if (plan.group_kind[g] == 4 && ks::strided_pair_aligned(cur, out)) {
             st = ks::launch_strided_pair(plan.shapes[k], plan.shapes[k + 1], cur_t, plan.wt, plan.wt, W[k], W[k + 1],
                                          cur, out, batch, stream, cus);

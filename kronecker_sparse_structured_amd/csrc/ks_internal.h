@@ -133,8 +133,17 @@ bool digit_chain_supports(const Shape* s, int n, int xt, int wt);
 ks_status_t launch_digit_chain(const Shape* s, int n, int xt, int wt, const void* const* W, const void* X, float* Y,
                                int64_t batch, hipStream_t stream);
 int digit_chain_describe(const Shape* s, int n, char* buf, size_t len);
+// Whole radix-2 or radix-4 butterflies on 1024- or 4096-wide rows, every
+// weight held in registers by one persistent workgroup a compute unit
+// (ks_resident.hip); needs X and Y 16-byte aligned. launch_row_chain takes
+// it first.
+bool resident_chain_supports(const Shape* s, int n, int xt, int wt);
+bool resident_chain_aligned(const void* X, const float* Y);
+ks_status_t launch_resident_chain(const Shape* s, int n, int xt, int wt, const void* const* W, const void* X,
+                                  float* Y, int64_t batch, hipStream_t stream, int num_cus);
+int resident_chain_describe(const Shape* s, int n, char* buf, size_t len);
 ks_status_t launch_row_chain(const Shape* s, int n, int xt, int wt, const void* const* W, const void* X, float* Y,
-                             int64_t batch, hipStream_t stream);
+                             int64_t batch, hipStream_t stream, int num_cus);
 int row_chain_describe(const Shape* s, int n, char* buf, size_t len);
 // Gradients (ks_backward.hip). Blocks of W transposed into Wt (same element
 // type); dK partial sums over row ranges in the workspace, then added in

@@ -261,8 +261,10 @@ ks_status_t launch_rc(int maxbc, dim3 grid, size_t lds, hipStream_t stream, cons
 }
 
 ks_status_t launch_row_chain(const Shape* s, int n, int xt, int wt, const void* const* W, const void* X, float* Y,
-                             int64_t batch, hipStream_t stream) {
+                             int64_t batch, hipStream_t stream, int num_cus) {
     if (!row_chain_supports(s, n, xt, wt)) return KS_ERR_UNSUPPORTED;
+    if (resident_chain_supports(s, n, xt, wt) && resident_chain_aligned(X, Y))
+        return launch_resident_chain(s, n, xt, wt, W, X, Y, batch, stream, num_cus);
     if (digit_chain_supports(s, n, xt, wt)) return launch_digit_chain(s, n, xt, wt, W, X, Y, batch, stream);
     RowChainArgs args{};
     args.nf = n;
@@ -295,6 +297,7 @@ ks_status_t launch_row_chain(const Shape* s, int n, int xt, int wt, const void* 
 }
 
 int row_chain_describe(const Shape* s, int n, char* buf, size_t len) {
+    if (resident_chain_supports(s, n, kF32, kF32)) return resident_chain_describe(s, n, buf, len);
     if (digit_chain_supports(s, n, kF32, kF32)) return digit_chain_describe(s, n, buf, len);
     const int pitch = row_pitch(s, n);
     const int rows = chain_rows(pitch);

@@ -539,6 +539,63 @@ def test_row_chain(name, bf16):
     chain_check(pats, X, Ws, Yu.cpu().numpy(), bf16)
 
 
+# Whole butterflies that run on the register-resident kernel: (radix, digits,
+# rows); the row counts leave a ragged last block and give every workgroup
+# several blocks (the DMA of block i + 1 overlaps block i).
+RESIDENT = {
+    "radix4_n4096": (4, 6, 4093),
+    "radix2_n4096": (2, 12, 4093),
+    "radix4_n1024": (4, 5, 16381),
+    "radix2_n1024": (2, 10, 16381),
+}
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "bf16w"])
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("name", sorted(RESIDENT))
+def test_resident_butterfly(name, reverse, dt):
+    """Radix-2 and radix-4 butterflies in both digit orders on the persistent
+    kernel that keeps every weight in registers: all of Y against the oracle,
+    fp32, bf16 and fp32 X with bf16 weights."""
+    r, L, batch = RESIDENT[name]
+    pats = _radix(r, L)[::-1] if reverse else _radix(r, L)
+    wl = datagen.Workload("resident", pats, batch, [1.0 / np.sqrt(r)] * len(pats), 300 + 3 * L + r)
+    X, Ws = datagen.draw(wl)
+    bx, bw = dt == "bf16", dt != "f32"
+    Xt, Wts = to_dev(X, bx), [to_dev(W, bw) for W in Ws]
+    assert libks.ks_chain_groups(pats, batch, libks.dtype_code(Xt.dtype, Wts[0].dtype)) == [list(range(len(pats)))]
+    Y = libks.chain_matmul(Xt, Wts, pats)
+    torch.cuda.synchronize()
+    se, sr, ma = oracle.ks_chain_err(pats, [host_values(W, bw) for W in Ws], host_values(X, bx), Y.cpu().numpy())
+    assert np.sqrt(se / sr) <= FP32_REL_TOL, "relative Frobenius error %g (max abs %g)" % (np.sqrt(se / sr), ma)
+
+
+@pytest.mark.parametrize("batch", [1, 3, 255, 16384])
+def test_resident_butterfly_batches(batch):
+    """The radix-4 4096-point butterfly at row counts below one block, below
+    one block per workgroup, and at full size (16,384 rows), fp32; plus the
+    Hadamard version bit-exact on integer rows."""
+    pats = _radix(4, 6)
+    wl = datagen.Workload("resident", pats, batch, [0.5] * len(pats), 400 + batch % 97)
+    X, Ws = datagen.draw(wl)
+    Y = libks.chain_matmul(to_dev(X), [to_dev(W) for W in Ws], pats)
+    torch.cuda.synchronize()
+    chain_check(pats, X, Ws, Y.cpu().numpy(), False)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_resident_hadamard_exact(bf16):
+    """The 4096-point Hadamard transform as twelve radix-2 factors of
+    [[1, 1], [1, -1]] blocks on small integers: exact in fp32, so the kernel
+    must match the oracle bit for bit."""
+    pats = datagen.hadamard_patterns(12)
+    wl = datagen.Workload("hadamard4096", pats, 77, [1.0] * len(pats), 12, x_kind="int8range", w_kind="hadamard")
+    X, Ws = datagen.draw(wl)
+    Y = libks.chain_matmul(to_dev(X, bf16), [to_dev(W, bf16) for W in Ws], pats).cpu().numpy()
+    ref = oracle.ks_chain_matmul(pats, [host_values(W, bf16) for W in Ws], host_values(X, bf16))
+    assert np.array_equal(Y.astype(np.float64), ref)
+
+
 @pytest.mark.parametrize("bf16", [False, True])
 def test_row_chain_unaligned_rows(bf16):
     """X and Y at 4-byte (not 16-byte) offsets: the element-wise load and
