@@ -711,21 +711,12 @@ def backward(args) -> int:
 
 
 def chain_plan_text(patterns, batch, dt, flags, bf16) -> str:
-    """One entry per launch of the chain: the kernel plan of a single factor,
-    or the pair that runs as one launch."""
+    """One entry per launch of the chain (the library's own description of
+    each launch group), "; "-separated, without the factor ranges."""
     from kronecker_sparse_structured_amd import libks
-    parts = []
-    for grp in libks.ks_chain_groups(patterns, batch, dt, flags):
-        if len(grp) == 2:
-            parts.append("fused pair %s -> %s (one launch, intermediate in LDS)"
-                         % (tuple(patterns[grp[0]]), tuple(patterns[grp[1]])))
-        elif len(grp) > 2:
-            parts.append("fused run of factors %d..%d (one launch, rows resident in LDS)" % (grp[0], grp[-1]))
-        else:
-            k = grp[0]
-            fdt = libks.DTYPE_F32 if not bf16 else (libks.DTYPE_BF16 if k == 0 else libks.DTYPE_BF16W)
-            parts.append(libks.ks_plan_describe(patterns[k], batch, fdt))
-    return "; ".join(parts)
+    del bf16  # the dtype code already says which factors read bf16
+    parts = libks.ks_chain_describe(patterns, batch, dt, flags).split("; ")
+    return "; ".join(p.split("] ", 1)[1] if p.startswith("[") else p for p in parts)
 
 
 def sweep(args) -> int:

@@ -290,6 +290,17 @@ ks_status_t ks_chain_plan(const ks_pattern_t* p, int n, int64_t batch, ks_dtype_
 ks_status_t ks_plan_describe(ks_pattern_t p, int64_t batch, ks_dtype_t dt,
                              char* buf, size_t len);
 
+/*
+ * ks_chain_describe: one description per launch group of the chain
+ * ks_chain_matmul would run for these arguments, "[first..last] kernel",
+ * separated by "; ", into buf (NUL-terminated, truncated to len). Same
+ * validation as ks_chain_plan; pure host code, no HIP call. Describes the
+ * path for 16-byte-aligned X and Y (a group that needs them runs another
+ * kernel otherwise). For tests and benchmark labels.
+ */
+ks_status_t ks_chain_describe(const ks_pattern_t* p, int n, int64_t batch, ks_dtype_t dt,
+                              unsigned flags, char* buf, size_t len);
+
 #ifdef __cplusplus
 }  /* extern "C" */
 #endif

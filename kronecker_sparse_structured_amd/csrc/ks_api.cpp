@@ -580,4 +580,48 @@ ks_status_t ks_plan_describe(ks_pattern_t p, int64_t batch, ks_dtype_t dt, char*
     return KS_OK;
 }
 
+ks_status_t ks_chain_describe(const ks_pattern_t* p, int n, int64_t batch, ks_dtype_t dt, unsigned flags, char* buf,
+                              size_t len) {
+    if (!buf || len == 0) return KS_ERR_NULL;
+    ChainPlan plan;
+    ks_status_t st = plan_chain(p, n, batch, enum_value(&dt), flags, &plan);
+    if (st != KS_OK) return st;
+    buf[0] = '\0';
+    size_t used = 0;
+    const int groups = static_cast<int>(plan.group_start.size());
+    for (int g = 0; g < groups && used + 1 < len; ++g) {
+        const int k = plan.group_start[g];
+        const Shape& s0 = plan.shapes[k];
+        const int xt = g == 0 ? plan.xt0 : ks::kF32;
+        char part[512];
+        part[0] = '\0';
+        switch (plan.group_kind[g]) {
+            case 1:
+            case 2:
+            case 4:
+            case 5: {
+                static const char* const names[] = {"", "fused pair (shared rows)", "slab pair", "", "strided pair",
+                                                    "Monarch pair"};
+                const Shape& s1 = plan.shapes[k + 1];
+                std::snprintf(part, sizeof part, "%s (%d, %d, %d, %d) -> (%d, %d, %d, %d), one launch",
+                              names[plan.group_kind[g]], s0.a, s0.b, s0.c, s0.d, s1.a, s1.b, s1.c, s1.d);
+                break;
+            }
+            case 3:
+                ks::row_chain_describe(&plan.shapes[k], plan.group_len[g], part, sizeof part);
+                break;
+            default: {
+                const ks_pattern_t pk = p[k];
+                const int fdt = xt == ks::kBF16 ? KS_DTYPE_BF16 : (plan.wt == ks::kBF16 ? KS_DTYPE_BF16W : KS_DTYPE_F32);
+                ks_plan_describe(pk, batch, static_cast<ks_dtype_t>(fdt), part, sizeof part);
+            }
+        }
+        const int w = std::snprintf(buf + used, len - used, "%s[%d..%d] %s", g ? "; " : "", k,
+                                    k + plan.group_len[g] - 1, part);
+        if (w < 0) break;
+        used = std::min(len - 1, used + static_cast<size_t>(w));
+    }
+    return KS_OK;
+}
+
 }  // extern "C"

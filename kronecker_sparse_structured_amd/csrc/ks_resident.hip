@@ -63,7 +63,7 @@ constexpr int kRowStride = 16 * 1024;    // LDS bytes between a thread's rows
 constexpr int kLdsBytes = 2 * kBlockBytes;
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef uint32_t uint32x2 __attribute__((ext_vector_type(2)));
 
 // Pass kinds: one radix-4 factor; two radix-2 factors, bit p first; two
 // radix-2 factors, bit p + 1 first.
@@ -282,18 +282,20 @@ __global__ __launch_bounds__(kThreads) void resident_chain_kernel(const TX* __re
             const int p = C::p(ps);
             const bool last = ps == C::NP - 1;
             if (ps > 0) lds_barrier();
-#pragma unroll 1
+            // rows interleaved for LDS latency: all four (fp32 X), two at a
+            // time where widening bf16 X needs the registers
+            constexpr int kInterleave = kWiden ? 2 : kRowsPerThread;
+#pragma unroll kInterleave
             for (int j = 0; j < kRowsPerThread; ++j) {
                 float v[4];
                 if (kWiden && ps == 0) {
                     const uint32_t sa = stage + (addr[ps] >> 1) + j * (kRowStride / 2);
                     if (p == 0) {
-                        const uint32_t u0 = *reinterpret_cast<const uint32_t*>(lds + sa);
-                        const uint32_t u1 = *reinterpret_cast<const uint32_t*>(lds + sa + 4);
-                        v[0] = bf16_lo(u0);
-                        v[1] = bf16_hi(u0);
-                        v[2] = bf16_lo(u1);
-                        v[3] = bf16_hi(u1);
+                        const uint32x2 u = *static_cast<const uint32x2*>(__builtin_assume_aligned(lds + sa, 8));
+                        v[0] = bf16_lo(u[0]);
+                        v[1] = bf16_hi(u[0]);
+                        v[2] = bf16_lo(u[1]);
+                        v[3] = bf16_hi(u[1]);
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
@@ -302,7 +304,7 @@ __global__ __launch_bounds__(kThreads) void resident_chain_kernel(const TX* __re
                 } else {
                     const uint32_t wa = work + addr[ps] + j * kRowStride;
                     if (p == 0) {
-                        const floatx4 x = *reinterpret_cast<const floatx4*>(lds + wa);
+                        const floatx4 x = *static_cast<const floatx4*>(__builtin_assume_aligned(lds + wa, 16));
                         v[0] = x[0];
                         v[1] = x[1];
                         v[2] = x[2];
@@ -316,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void resident_chain_kernel(const TX* __re
                 if (!last) {
                     const uint32_t wa = work + addr[ps] + j * kRowStride;
                     if (p == 0) {
-                        *reinterpret_cast<floatx4*>(lds + wa) = floatx4{v[0], v[1], v[2], v[3]};
+                        *static_cast<floatx4*>(__builtin_assume_aligned(lds + wa, 16)) = floatx4{v[0], v[1], v[2], v[3]};
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) *reinterpret_cast<float*>(lds + (wa ^ (e << (p + 2)))) = v[e];

@@ -1,8 +1,9 @@
 """Thin Python binding of libks (include/ks.h) through ctypes.
 
 The functions named like the C entry points (``ks_matmul``, ``ks_matmul_ex``,
-``ks_chain_workspace_size``, ``ks_chain_matmul``, ``ks_plan_describe``,
-``ks_status_string``, ``ks_version``) only marshal arguments: tensors become
+``ks_chain_workspace_size``, ``ks_chain_matmul``, ``ks_chain_plan``,
+``ks_chain_describe``, ``ks_plan_describe``, ``ks_status_string``,
+``ks_version``, the gradient calls) only marshal arguments: tensors become
 device pointers, the stream defaults to torch's current stream, and a
 non-OK status raises ``KSError``. Every step of the computation runs in the
 HIP kernels of libks.so; there is no fallback. If the library is not built,
@@ -110,6 +111,9 @@ def load(path: str = LIB_PATH):
     lib.ks_chain_plan.restype = i32
     lib.ks_plan_describe.argtypes = [ks_pattern_t, i64, i32, ctypes.c_char_p, ctypes.c_size_t]
     lib.ks_plan_describe.restype = i32
+    lib.ks_chain_describe.argtypes = [ctypes.POINTER(ks_pattern_t), i32, i64, i32, ctypes.c_uint,
+                                      ctypes.c_char_p, ctypes.c_size_t]
+    lib.ks_chain_describe.restype = i32
     lib.ks_matmul_dx_workspace_size.argtypes = [ks_pattern_t, i32, ctypes.POINTER(ctypes.c_size_t)]
     lib.ks_matmul_dx_workspace_size.restype = i32
     lib.ks_matmul_dx.argtypes = [ks_pattern_t, vp, vp, vp, i64, i32, vp, ctypes.c_size_t, vp]
@@ -272,6 +276,14 @@ def ks_chain_groups(ps: Sequence, batch: int, dtype: int, flags: int = CHAIN_AUT
         out.append(list(range(k, k + ln)))
         k += ln
     return out
+
+
+def ks_chain_describe(ps: Sequence, batch: int, dtype: int, flags: int = CHAIN_AUTO) -> str:
+    """The kernel of each launch group, "[first..last] description; ..."."""
+    buf = ctypes.create_string_buffer(4096)
+    _raise(load().ks_chain_describe(_patterns(ps), len(ps), int(batch), int(dtype), int(flags), buf, 4096),
+           "ks_chain_describe", True)
+    return buf.value.decode()
 
 
 def ks_plan_describe(p, batch: int, dtype: int) -> str:

@@ -167,6 +167,30 @@ def test_plan_describe():
     assert libks.ks_plan_describe((2, 3, 5, 7), 10, libks.DTYPE_F32).startswith("generic")
 
 
+def test_chain_describe():
+    """The library's own label of each launch group: whole radix-2/4
+    butterflies on 1024- or 4096-wide rows name the register-resident kernel
+    (with their digit order), other runs the digit-pass kernel, pairs their
+    family, single factors their tile plan."""
+    r4 = [(4 ** k, 4, 4, 4 ** (5 - k)) for k in range(6)]
+    d = libks.ks_chain_describe(r4, 16384, libks.DTYPE_F32)
+    assert d.startswith("[0..5] register-resident butterfly: 6 radix-4 factors in 6 passes (descending)")
+    assert "(ascending)" in libks.ks_chain_describe(r4[::-1], 7, libks.DTYPE_BF16)
+    r2 = [(2 ** k, 2, 2, 2 ** (9 - k)) for k in range(10)]
+    assert "10 radix-2 factors in 5 passes" in libks.ks_chain_describe(r2, 5, libks.DTYPE_BF16W)
+    # n = 256 and a chain that is not a whole butterfly keep the digit-pass kernel
+    r4s = [(4 ** k, 4, 4, 4 ** (3 - k)) for k in range(4)]
+    assert libks.ks_chain_describe(r4s, 100, libks.DTYPE_F32).startswith("[0..3] digit-pass chain")
+    assert libks.ks_chain_describe(r4[:5], 100, libks.DTYPE_F32).startswith("[0..4] digit-pass chain")
+    bf = [(1, 16, 16, 4096), (16, 16, 16, 256), (256, 16, 16, 16), (4096, 16, 16, 1)]
+    parts = libks.ks_chain_describe(bf, 4096, libks.DTYPE_F32).split("; ")
+    assert [p.split("]")[0] + "]" for p in parts] == ["[0..0]", "[1..1]", "[2..3]"]
+    assert parts[2].startswith("[2..3] slab pair")
+    assert libks.ks_chain_describe(bf, 4096, libks.DTYPE_F32, libks.CHAIN_NO_FUSE).count(";") == 3
+    with pytest.raises(libks.KSError):
+        libks.ks_chain_describe([(1, 4, 4, 16), (1, 4, 4, 8)], 10, libks.DTYPE_F32)
+
+
 def test_chain_plan():
     three = [(1, 6, 2, 3), (3, 2, 3, 2), (2, 2, 3, 2)]
     assert libks.ks_chain_plan(three, 10, libks.DTYPE_F32, libks.CHAIN_NO_FUSE) == [1, 1, 1]
