@@ -167,9 +167,13 @@ struct DwArgs {
     int64_t out_stride;          // elements between the partial sums of consecutive splits (0: one split)
 };
 
-template <typename TX>
-__global__ __launch_bounds__(kStreamThreads) void dw_mfma_kernel(const float* __restrict__ dY, const TX* __restrict__ X,
-                                                                  float* __restrict__ out, DwArgs args) {
+// NL loader waves: with two, each issues every other instruction of X's and
+// of dY's part of a stage and waits on its own vector-memory counter, which
+// doubles the loads a workgroup keeps in flight (a wave's counter allows 63).
+template <typename TX, int NL>
+__global__ __launch_bounds__(kConsumerThreads + 64 * NL) void dw_mfma_kernel(const float* __restrict__ dY,
+                                                                              const TX* __restrict__ X,
+                                                                              float* __restrict__ out, DwArgs args) {
     constexpr int EB = int(sizeof(TX));
     constexpr int VWX = 16 / EB;
     extern __shared__ __align__(16) unsigned char lds[];
@@ -199,22 +203,33 @@ __global__ __launch_bounds__(kStreamThreads) void dw_mfma_kernel(const float* __
     if (t >= kConsumerThreads) {
         // ------------------------------------------------------ loader wave
         LoaderPlan<kDwMaxInsts> lx, ly;
-        const int lane = t - kConsumerThreads;
+        const int lane = t & 63;
+        const int L = (t - kConsumerThreads) >> 6;             // loader wave
         make_loader_plan<kDwMaxInsts>(args.xmap, args.insts_x, VWX, EB, args.n_in, args.xmap.blocks,
                                       args.xmap.blk_vec, lane, &lx);
         make_loader_plan<kDwMaxInsts>(args.ymap, args.insts_y, 4, 4, args.n_out, args.ymap.blocks,
                                       args.ymap.blk_vec, lane, &ly);
+        // this wave's instructions per stage
+        const int own = (args.insts_x - L + NL - 1) / NL + (args.insts_y - L + NL - 1) / NL;
         auto issue = [&](int s) {
             const int64_t n0 = row_begin + int64_t(s) * kDwRows;
             unsigned char* st = lds + (s % S) * stage_bytes;
-            issue_stage<kDwMaxInsts>(lx, args.insts_x, X + n0 * args.n_in + xg0,
-                                     stage_limit(n0, row_end, args.n_in, EB), st);
-            issue_stage<kDwMaxInsts>(ly, args.insts_y, dY + n0 * args.n_out + yg0,
-                                     stage_limit(n0, row_end, args.n_out, 4), st + args.insts_x * 1024);
+            if constexpr (NL == 1) {
+                issue_stage<kDwMaxInsts>(lx, args.insts_x, X + n0 * args.n_in + xg0,
+                                         stage_limit(n0, row_end, args.n_in, EB), st);
+                issue_stage<kDwMaxInsts>(ly, args.insts_y, dY + n0 * args.n_out + yg0,
+                                         stage_limit(n0, row_end, args.n_out, 4), st + args.insts_x * 1024);
+            } else {
+                issue_stage_part<kDwMaxInsts>(lx, args.insts_x, X + n0 * args.n_in + xg0,
+                                              stage_limit(n0, row_end, args.n_in, EB), st, L, NL);
+                issue_stage_part<kDwMaxInsts>(ly, args.insts_y, dY + n0 * args.n_out + yg0,
+                                              stage_limit(n0, row_end, args.n_out, 4), st + args.insts_x * 1024, L,
+                                              NL);
+            }
         };
         for (int s = 0; s < S - 1 && s < nsteps; ++s) issue(s);
         for (int s = 0; s < nsteps; ++s) {
-            wait_vmcnt_upto(min(S - 2, nsteps - 1 - s) * (args.insts_x + args.insts_y));
+            wait_vmcnt_upto(min(63, min(S - 2, nsteps - 1 - s) * own));
             lds_barrier();                                   // stage s ready
             if (s + S - 1 < nsteps) issue(s + S - 1);
             lds_barrier();                                   // stage s consumed
@@ -235,11 +250,11 @@ __global__ __launch_bounds__(kStreamThreads) void dw_mfma_kernel(const float* __
     const int ys = contig ? d : args.dt;                     // element stride of beta in a dY stage row
     const int xrow = args.xmap.row_vec * 16, yrow = args.ymap.row_vec * 16;
     int aoff[kDwTilesPerWave], boff[kDwTilesPerWave];       // byte offsets within a stage row
-    bool tv[kDwTilesPerWave];
+    // this wave's tiles w, w + 4, ..: the first `ntv` of its slots
+    const int ntv = __builtin_amdgcn_readfirstlane((args.ntiles_acc - w + 3) / 4);
 #pragma unroll
     for (int j = 0; j < kDwTilesPerWave; ++j) {
         const int ti = w + 4 * j;
-        tv[j] = ti < args.ntiles_acc;
         const int dl = ti / (MT * NT);
         const int mt = (ti / NT) % MT;
         const int nt = ti % NT;
@@ -263,7 +278,7 @@ __global__ __launch_bounds__(kStreamThreads) void dw_mfma_kernel(const float* __
             const unsigned char* xr = xst + r * xrow;
 #pragma unroll
             for (int j = 0; j < kDwTilesPerWave; ++j) {
-                if (!tv[j]) continue;
+                if (j >= ntv) continue;
                 const float av = rv ? *reinterpret_cast<const float*>(yr + aoff[j]) : 0.0f;
                 const float bv = rv ? to_f32(*reinterpret_cast<const TX*>(xr + boff[j])) : 0.0f;
                 acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[j], 0, 0, 0);
@@ -275,7 +290,7 @@ __global__ __launch_bounds__(kStreamThreads) void dw_mfma_kernel(const float* __
     float* o = out + int64_t(split) * args.out_stride;
 #pragma unroll
     for (int j = 0; j < kDwTilesPerWave; ++j) {
-        if (!tv[j]) continue;
+        if (j >= ntv) continue;
         const int ti = w + 4 * j;
         const int dl = ti / (MT * NT);
         const int mt = (ti / NT) % MT;
@@ -292,7 +307,7 @@ __global__ __launch_bounds__(kStreamThreads) void dw_mfma_kernel(const float* __
 
 // Tile of the matrix-core dK kernel for pattern s and X element size eb.
 struct DwGeom {
-    int bt, dt, contiguous, tiles_beta, tiles_delta, n_tiles, ntiles_acc, insts_x, insts_y, stages;
+    int bt, dt, contiguous, tiles_beta, tiles_delta, n_tiles, ntiles_acc, insts_x, insts_y, stages, loaders;
     StageMap xmap, ymap;
     size_t lds;
 };
@@ -334,8 +349,15 @@ bool dw_geom(const Shape& s, int xt, DwGeom* g) {
         if (g->insts_x > kDwMaxInsts || g->insts_y > kDwMaxInsts || insts > 63) return false;
         // the loader addresses a stage with 32-bit byte offsets
         if (int64_t(kDwRows) * std::max(s.n_in * eb, s.n_out * 4) >= (int64_t(1) << 31)) return false;
-        int st = std::max(3, std::min(8, (150 * 1024) / (insts * 1024)));
-        while (st > 3 && (st - 2) * insts > 63) --st;
+        // A wave keeps at most 63 loads in flight. Where X arrives in short
+        // runs (segments of under 64 bytes: many pieces a stage), a second
+        // loader wave takes every other instruction and the ring deepens
+        // (measured: (1,128,128,32) 711 -> 559 us on 16,384 rows); with
+        // longer runs a second loader measured slower (ViT factor 83 -> 99 us).
+        g->loaders = (!contig && dt * eb < 64 && insts > 21) ? 2 : 1;
+        const int own = (g->insts_x + g->loaders - 1) / g->loaders + (g->insts_y + g->loaders - 1) / g->loaders;
+        int st = std::max(3, std::min(8, (g->loaders == 2 ? 160 : 150) * 1024 / (insts * 1024)));
+        while (st > 3 && (st - 2) * own > 63) --st;
         g->stages = st;
         g->lds = size_t(st) * insts * 1024;
         return g->lds <= 160 * 1024;
@@ -523,12 +545,18 @@ ks_status_t launch_dw(const Shape& s, int xt, const float* dY, const void* X, fl
         args.out_stride = pl.ranges > 1 ? s.nnz : 0;
         const int64_t blocks = int64_t(pl.g.n_tiles) * pl.ranges;
         if (blocks > 0x7fffffff) return KS_ERR_UNSUPPORTED;
-        if (xt == kF32)
-            st = launch_kernel(dw_mfma_kernel<float>, dim3(static_cast<unsigned>(blocks)), dim3(kStreamThreads),
-                               pl.g.lds, stream, dY, static_cast<const float*>(X), out, args);
+        const dim3 grid(static_cast<unsigned>(blocks));
+        const dim3 blk1(kConsumerThreads + 64), blk2(kConsumerThreads + 128);
+        const float* xf = static_cast<const float*>(X);
+        const bf16_t* xb = static_cast<const bf16_t*>(X);
+        if (xt == kF32 && pl.g.loaders == 2)
+            st = launch_kernel(dw_mfma_kernel<float, 2>, grid, blk2, pl.g.lds, stream, dY, xf, out, args);
+        else if (xt == kF32)
+            st = launch_kernel(dw_mfma_kernel<float, 1>, grid, blk1, pl.g.lds, stream, dY, xf, out, args);
+        else if (pl.g.loaders == 2)
+            st = launch_kernel(dw_mfma_kernel<bf16_t, 2>, grid, blk2, pl.g.lds, stream, dY, xb, out, args);
         else
-            st = launch_kernel(dw_mfma_kernel<bf16_t>, dim3(static_cast<unsigned>(blocks)), dim3(kStreamThreads),
-                               pl.g.lds, stream, dY, static_cast<const bf16_t*>(X), out, args);
+            st = launch_kernel(dw_mfma_kernel<bf16_t, 1>, grid, blk1, pl.g.lds, stream, dY, xb, out, args);
     } else if (pl.small) {
         st = launch_small(s, xt, dY, X, out, batch, pl.rows_per_range, pl.ranges, stream);
     } else {
@@ -554,11 +582,11 @@ int dw_describe(const Shape& s, int xt, int64_t batch, char* buf, size_t len) {
         return std::snprintf(buf, len, "dw generic: one K entry per thread, ranges=%d", pl.ranges);
     return std::snprintf(buf, len,
                          "dw mfma 16x16x4f32: deltas/tile=%d (%s) outputs/tile=%d of %d acc tiles=%d ranges=%d "
-                         "rows/range=%lld wgs=%lld stages=%d x %d KB",
+                         "rows/range=%lld wgs=%lld stages=%d x %d KB loaders=%d",
                          pl.g.dt, pl.g.contiguous ? "contiguous" : "segmented", pl.g.bt, s.b, pl.g.ntiles_acc,
                          pl.ranges, static_cast<long long>(pl.rows_per_range),
                          static_cast<long long>(int64_t(pl.g.n_tiles) * pl.ranges), pl.g.stages,
-                         pl.g.insts_x + pl.g.insts_y);
+                         pl.g.insts_x + pl.g.insts_y, pl.g.loaders);
 }
 
 }  // namespace ks

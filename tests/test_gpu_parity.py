@@ -814,8 +814,9 @@ def test_mfma_store_modes(p, bf16):
 
 # ---------------------------------------------------------------- gradients
 
+# (1, 128, 128, 32): dK X segments of 16 bytes, the two-loader-wave stage
 BACKWARD_PATTERNS = [(2, 16, 16, 8), (4, 64, 16, 6), (64, 8, 8, 8), (3, 5, 7, 2), (2, 128, 128, 4),
-                     (1, 4, 4, 64), (5, 1, 3, 2)]
+                     (1, 4, 4, 64), (5, 1, 3, 2), (1, 128, 128, 32)]
 
 
 def _rel(a, b):
