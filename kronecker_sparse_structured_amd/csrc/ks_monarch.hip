@@ -48,6 +48,7 @@
 // merges element loads into the same instructions by itself).
 
 #include <algorithm>
+#include <type_traits>
 #include <cstdio>
 
 #include "ks_device.h"
@@ -58,14 +59,17 @@ namespace ks {
 namespace {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
 
 constexpr int kR = 16;                               // rows per stage: one MFMA M tile
 
-// NW compute waves (4, or 8 for 32 x 32 blocks: two a SIMD) plus one loader
-// wave.
+// NW compute waves plus one loader wave (NW = 4), or sixteen compute waves
+// that copy their own shares of the next stage (SELF: 32 x 32 blocks, whose
+// weights the sixteen waves keep in registers between them).
 template <int M, int N, int NW>
 struct MonShape {
-    static constexpr int THREADS = NW * 64 + 64;
+    static constexpr bool SELF = NW == 16;
+    static constexpr int THREADS = NW * 64 + (SELF ? 0 : 64);
     static constexpr int CONSUMERS = NW * 64;
     static constexpr int XP = N + 4;                 // floats per index x in LDS
     static constexpr int RP = M * XP + 4;            // floats per row in LDS
@@ -77,9 +81,11 @@ struct MonShape {
     static constexpr int KSF = N / 4, NTF = N / 16;  // F: k steps (gamma), N tiles (beta)
     static constexpr int KSG = M / 4, NTG = M / 16;  // G: k steps (alpha), N tiles (beta')
     static constexpr int GA = M / NW;                // F blocks per wave
-    static constexpr int GB = N / NW;                // G positions per wave (batches of 4)
-    static_assert(GA >= 1 && GB % 4 == 0, "a wave takes whole batches of four G positions");
+    static constexpr int GB = N / NW;                // G positions per wave
+    static constexpr int BB = GB < 4 ? GB : 4;       // G positions a batch (one LDS read of Z)
+    static_assert(GA >= 1 && GB % BB == 0 && (BB == 2 || BB == 4), "a wave takes whole batches of G positions");
     static_assert(STAGES >= 2 && (N == 16 || N == 32) && (M == 16 || M == 32), "shapes");
+    static_assert(!SELF || STAGES == 2, "the self-copy waits assume two stages");
     static_assert(RP % 4 == 0 && (RP / 4) % 2 == 1 && XP % 4 == 0, "16-byte rows; odd row pitch in vectors");
 };
 
@@ -123,7 +129,7 @@ __device__ __forceinline__ floatx4 lds_x4(const unsigned char* p, bf16_t) {
 }
 
 template <int M, int N, int NW, typename TX, typename TW>
-__global__ __launch_bounds__(NW * 64 + 64) void monarch_pair_kernel(const TX* __restrict__ X,
+__global__ __launch_bounds__(NW * 64 + (NW == 16 ? 0 : 64)) void monarch_pair_kernel(const TX* __restrict__ X,
                                                                 const TW* KF,
                                                                 const TW* KG,
                                                                 float* __restrict__ Y, MonArgs args) {
@@ -137,23 +143,24 @@ __global__ __launch_bounds__(NW * 64 + 64) void monarch_pair_kernel(const TX* __
     const int nsteps = static_cast<int>((row_end - row_begin + kR - 1) / kR);
     auto stage = [&](int s) { return reinterpret_cast<float*>(lds + (s % S::STAGES) * S::STAGE_BYTES); };
 
-    if (t >= kConsumerThreads) {
-        // ------------------------------------------------------ loader wave
-        // instruction i fills LDS vectors [64 i, 64 i + 64) of a stage: row
-        // r, index x, vector v of the row's x-th run of N values (N / 4 fp32
-        // or N / 8 bf16 vectors); padding vectors (and any past the stage)
-        // load the stage's first vector
-        constexpr int EB = sizeof(TX);
+    // instruction i of a stage's copy fills LDS vectors [64 i, 64 i + 64):
+    // row r, index x, vector v of the row's x-th run of N values (N / 4 fp32
+    // or N / 8 bf16 vectors); padding vectors (and any past the stage) load
+    // the stage's first vector
+    constexpr int EB = sizeof(TX);
+    auto x_offset = [&](int i, int lane) -> uint32_t {
         constexpr int XIN = N * EB / 16;
+        const int q = 64 * i + lane;
+        const int r = q / (S::RP / 4), u = q - r * (S::RP / 4);
+        const int x = u / (S::XP / 4), v = u - x * (S::XP / 4);
+        return (r < kR && x < M && v < XIN) ? static_cast<uint32_t>((r * args.n + x * N) * EB + 16 * v) : 0u;
+    };
+    if (!S::SELF && t >= kConsumerThreads) {
+        // ------------------------------------------------------ loader wave
         const int lane = t - kConsumerThreads;
         uint32_t off[S::INSTS];
 #pragma unroll
-        for (int i = 0; i < S::INSTS; ++i) {
-            const int q = 64 * i + lane;
-            const int r = q / (S::RP / 4), u = q - r * (S::RP / 4);
-            const int x = u / (S::XP / 4), v = u - x * (S::XP / 4);
-            off[i] = (r < kR && x < M && v < XIN) ? static_cast<uint32_t>((r * args.n + x * N) * EB + 16 * v) : 0u;
-        }
+        for (int i = 0; i < S::INSTS; ++i) off[i] = x_offset(i, lane);
         auto issue = [&](int s) {
             const int64_t n0 = row_begin + int64_t(s) * kR;
             const uint32_t limit = stage_limit(n0, row_end, args.n, EB);
@@ -200,7 +207,7 @@ __global__ __launch_bounds__(NW * 64 + 64) void monarch_pair_kernel(const TX* __
     constexpr int CF = S::NTF * (S::KSF / 4);
     constexpr int CG = S::NTG * (S::KSG / 4);
     constexpr int kChunks = S::GA + S::GB;
-    constexpr bool kStream = (M * N * N + N * M * M) > 24576;
+    constexpr bool kStream = !S::SELF && (M * N * N + N * M * M) > 24576;
     constexpr int kSlots = S::GA;
     static_assert(!kStream || (CF == CG && S::GB == kSlots), "ring layout");
     constexpr int kRegs = kStream ? kSlots * CF : S::GA * CF + S::GB * CG;
@@ -265,6 +272,42 @@ __global__ __launch_bounds__(NW * 64 + 64) void monarch_pair_kernel(const TX* __
         if (kStream) order_point();
     }
 
+    // SELF: every wave copies instructions w, w + NW, .. of each stage with
+    // LDS DMA issued from inline assembly (the compiler would wait for any
+    // LDS DMA in flight before each LDS read, serialising the next stage's
+    // copy with this stage's products). The weights are waited for here,
+    // once: the compiler, unaware of the copies, would otherwise wait for
+    // every request in flight at their first use inside the stage loop.
+    constexpr int kOwnMax = (S::INSTS + NW - 1) / NW;
+    const int own = (S::INSTS - w + NW - 1) / NW;            // this wave's instructions a stage
+    uint32_t soff[kOwnMax];
+    auto self_issue = [&](int s) {
+        const int64_t n0 = row_begin + int64_t(s) * kR;
+        const uint32_t limit = stage_limit(n0, row_end, args.n, EB);
+        const char* base = reinterpret_cast<const char*>(X + n0 * args.n);
+        const uint32_t st0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)) +
+                             static_cast<uint32_t>((s % S::STAGES) * S::STAGE_BYTES);
+#pragma unroll
+        for (int m = 0; m < kOwnMax; ++m) {
+            const int i = wu + NW * m;
+            if (i < S::INSTS) {
+                const void* g = base + (soff[m] < limit ? soff[m] : 0u);
+                asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g),
+                             "s"(st0 + 1024u * i)
+                             : "memory");
+            }
+        }
+    };
+    if constexpr (S::SELF) {
+#pragma unroll
+        for (int m = 0; m < kOwnMax; ++m) soff[m] = x_offset(w + NW * m, lane);
+        wait_vmcnt<0>();
+        self_issue(0);
+        if (nsteps > 1) self_issue(1);
+    }
+    (void)own;
+    (void)soff;
+
     // this lane's X values of F block alpha: X[col][alpha][KSF g ..]
     auto read_x = [&](const float* st, int alpha, floatx4 (&xv)[S::KSF / 4]) {
         const unsigned char* xr =
@@ -272,13 +315,20 @@ __global__ __launch_bounds__(NW * 64 + 64) void monarch_pair_kernel(const TX* __
 #pragma unroll
         for (int q = 0; q < S::KSF / 4; ++q) xv[q] = lds_x4(xr + 4 * q * sizeof(TX), TX());
     };
-    // Z[col][alpha = KSG g + ks][beta0 .. beta0 + 3]
+    // Z[col][alpha = KSG g + ks][beta0 .. beta0 + BB - 1]
+    using ZV = typename std::conditional<S::BB == 4, floatx4, floatx2>::type;
     auto read_z = [&](const float* st, int ks, int beta0) {
-        return *reinterpret_cast<const floatx4*>(st + col * S::RP + (S::KSG * g + ks) * S::XP + beta0);
+        return *reinterpret_cast<const ZV*>(st + col * S::RP + (S::KSG * g + ks) * S::XP + beta0);
     };
 
     for (int s = 0; s < nsteps; ++s) {
         float* st = stage(s);
+        if constexpr (S::SELF) {
+            // this wave's part of stage s has landed once only what it issued
+            // after it remains: stage s - 1's stores and stage s + 1's copy
+            constexpr int kStores = kR * M * S::XVEC / kConsumerThreads;
+            wait_vmcnt_upto((s >= 1 ? kStores : 0) + (s + 1 < nsteps ? own : 0));
+        }
         lds_barrier();                                                   // stage s ready
         // (A) Z[r][alpha][beta] = sum_gamma K_F[alpha][0][beta][gamma] X[r][alpha][gamma].
         // Block j + 1's inputs are read before block j's results are
@@ -309,20 +359,20 @@ __global__ __launch_bounds__(NW * 64 + 64) void monarch_pair_kernel(const TX* __
                 for (int i = 0; i < 4; ++i) st[(4 * g + i) * S::RP + alpha * S::XP + 16 * nt + col] = acc[nt][i];
         }
         lds_barrier();                                                   // Z written
-        // (B) Y[r][beta'][beta] = sum_alpha K_G[0][beta][beta'][alpha] Z[r][alpha][beta], four beta at a time
+        // (B) Y[r][beta'][beta] = sum_alpha K_G[0][beta][beta'][alpha] Z[r][alpha][beta], BB beta at a time
 #pragma unroll
-        for (int j = 0; j < S::GB; j += 4) {
+        for (int j = 0; j < S::GB; j += S::BB) {
             const int beta0 = w * S::GB + j;
-            floatx4 acc[4][S::NTG];
+            floatx4 acc[S::BB][S::NTG];
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < S::BB; ++u)
 #pragma unroll
                 for (int nt = 0; nt < S::NTG; ++nt) acc[u][nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int ks = 0; ks < S::KSG; ++ks) {
-                const floatx4 zv = read_z(st, ks, beta0);
+                const ZV zv = read_z(st, ks, beta0);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
+                for (int u = 0; u < S::BB; ++u) {
                     const int base = chunk_base(S::GA + j + u);
 #pragma unroll
                     for (int nt = 0; nt < S::NTG; ++nt)
@@ -331,13 +381,17 @@ __global__ __launch_bounds__(NW * 64 + 64) void monarch_pair_kernel(const TX* __
                 }
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) refill(S::GA + j + u);
+            for (int u = 0; u < S::BB; ++u) refill(S::GA + j + u);
 #pragma unroll
             for (int nt = 0; nt < S::NTG; ++nt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    *reinterpret_cast<floatx4*>(st + (4 * g + i) * S::RP + (16 * nt + col) * S::XP + beta0) =
-                        floatx4{acc[0][nt][i], acc[1][nt][i], acc[2][nt][i], acc[3][nt][i]};
+                for (int i = 0; i < 4; ++i) {
+                    float* zp = st + (4 * g + i) * S::RP + (16 * nt + col) * S::XP + beta0;
+                    if constexpr (S::BB == 4)
+                        *reinterpret_cast<floatx4*>(zp) = floatx4{acc[0][nt][i], acc[1][nt][i], acc[2][nt][i], acc[3][nt][i]};
+                    else
+                        *reinterpret_cast<floatx2*>(zp) = floatx2{acc[0][nt][i], acc[1][nt][i]};
+                }
         }
         lds_barrier();                                                   // Y written
         // (C) the rows out: thread t takes 16-byte vectors t, t + 256, .. of
@@ -366,6 +420,9 @@ __global__ __launch_bounds__(NW * 64 + 64) void monarch_pair_kernel(const TX* __
                 }
             }
             lds_barrier();                                               // stage s read out
+        }
+        if constexpr (S::SELF) {
+            if (s + S::STAGES < nsteps) self_issue(s + S::STAGES);
         }
     }
     // the ring's last prefetches (of a stage that does not come) land
@@ -404,7 +461,7 @@ ks_status_t launch_typed(int M, int N, const void* W0, const void* W1, const voi
     if (M == 16 && N == 16) return launch_mn<16, 16, 4, TX, TW>(W0, W1, X, Y, batch, stream, num_cus);
     if (M == 16 && N == 32) return launch_mn<16, 32, 4, TX, TW>(W0, W1, X, Y, batch, stream, num_cus);
     if (M == 32 && N == 16) return launch_mn<32, 16, 4, TX, TW>(W0, W1, X, Y, batch, stream, num_cus);
-    if (M == 32 && N == 32) return launch_mn<32, 32, 8, TX, TW>(W0, W1, X, Y, batch, stream, num_cus);
+    if (M == 32 && N == 32) return launch_mn<32, 32, 16, TX, TW>(W0, W1, X, Y, batch, stream, num_cus);
     return KS_ERR_UNSUPPORTED;
 }
 
