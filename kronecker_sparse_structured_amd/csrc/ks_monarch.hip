@@ -13,28 +13,29 @@
 // |X| + |Y| + weights through HBM instead of |X| + 2 |Z| + |Y|.
 //
 // Every row needs all of the two factors' weights (M N N + N M M values),
-// and each compute wave needs those of its own groups at every stage: up to
-// 96 registers a lane, which stay resident for the whole launch, or for
-// M = N = 32 (256 KB of fp32, 128 registers a lane over eight waves) a
-// stream from L2 through a ring of registers, several groups ahead of their
-// use. In both products
+// and each compute wave needs those of its own groups at every stage; they
+// stay in registers for the whole launch: up to 96 a lane with four compute
+// waves, and for M = N = 32 (256 KB of fp32, half a compute unit's register
+// file) 64 a lane spread over sixteen waves. In both products
 // the k index is assigned so that a lane's k values are consecutive (lane
 // group g takes k = (K / 4) g + ks in step ks; any order of the k sum is the
 // same sum up to rounding), which makes a lane's B operands of one group
 // consecutive weights (16-byte loads) and its A operands consecutive values
 // of the row.
 //
-// Per 16-row stage, in place in LDS (NW compute waves: four, or eight for
+// Per 16-row stage, in place in LDS (NW compute waves: four, or sixteen for
 // 32 x 32 blocks):
 //  (A) wave w takes the blocks alpha = w M / NW ..: Z[rows][alpha][beta] =
 //      X[rows][alpha][.] (16 x N) times the block's transpose, written over
 //      X[rows][alpha][.] (a wave reads and writes only its own blocks);
 //  (B) after an LDS barrier, wave w takes positions beta = w N / NW .., four
-//      at a time (one 16-byte LDS read gives the A operands of four
-//      positions): Y[rows][beta'][beta] = Z[rows][.][beta] (16 x M) times
-//      K_G[beta]'s transpose, written over Z[rows][.][beta];
+//      (two with sixteen waves) at a time (one LDS read gives the A operands
+//      of those positions): Y[rows][beta'][beta] = Z[rows][.][beta] (16 x M)
+//      times K_G[beta]'s transpose, written over Z[rows][.][beta];
 //  (C) after another barrier the compute waves store the rows.
-// A loader wave streams the next stages from HBM meanwhile.
+// A loader wave streams the next stages from HBM meanwhile; sixteen compute
+// waves fill a workgroup's 1024 threads, so there each copies its own share
+// of the next stage.
 //
 // LDS row layout (floats): value (x, y) at x * (N + 4) + y, rows
 // M (N + 4) + 4 apart: the 16 rows, the 16 consecutive y or the 16
@@ -190,27 +191,18 @@ __global__ __launch_bounds__(NW * 64 + (NW == 16 ? 0 : 64)) void monarch_pair_ke
     // B[l / 16][l % 16] and receives D[4 (l / 16) + i][l % 16] in register i.
     // Lane group g = l / 16 takes k = (K / 4) g + ks in step ks.
     //
-    // The weights of a wave's groups are the same for every stage. A chunk
-    // is one group's B operands for this lane: F block j (CF 4-value
-    // registers) or G position p (CG). When all of them fit (M N N + N M M
-    // <= 24,576 values, at most 96 registers a lane) they are loaded once and
-    // stay resident. For M = N = 32 (eight waves, 128 registers a lane)
-    // each stage streams a wave's 8 chunks (its F blocks 0..3, then its G
-    // positions 0..3) through a ring of 4 slots: a slot is refilled as soon
-    // as its chunk has been used, with the chunk 4 places later (F block j
-    // is followed by G position j, G position j by the next stage's F block
-    // j). All of a stage's F blocks are thus requested before the previous
-    // stage's rows are stored: the vector-memory counter completes in order, so a wait
-    // for a chunk requested after those stores would also wait for them.
-    // bf16 weights stay packed and widen at use.
+    // The weights of a wave's groups are the same for every stage, so they
+    // are loaded once and stay in registers. A chunk is one group's B
+    // operands for this lane: F block j (CF 4-value registers) or G position
+    // p (CG): (M N N + N M M) / (64 NW) registers a lane, at most 96 with
+    // four waves, 64 with sixteen for M = N = 32. bf16 weights stay packed
+    // and widen at use.
     using WR = typename WReg<TW>::type;
     constexpr int CF = S::NTF * (S::KSF / 4);
     constexpr int CG = S::NTG * (S::KSG / 4);
     constexpr int kChunks = S::GA + S::GB;
-    constexpr bool kStream = !S::SELF && (M * N * N + N * M * M) > 24576;
-    constexpr int kSlots = S::GA;
-    static_assert(!kStream || (CF == CG && S::GB == kSlots), "ring layout");
-    constexpr int kRegs = kStream ? kSlots * CF : S::GA * CF + S::GB * CG;
+    constexpr int kRegs = S::GA * CF + S::GB * CG;
+    static_assert(kRegs * sizeof(WR) / 4 <= 96, "weights a lane");
 
     const int w = t >> 6;
     const int lane = t & 63;
@@ -218,21 +210,17 @@ __global__ __launch_bounds__(NW * 64 + (NW == 16 ? 0 : 64)) void monarch_pair_ke
     const int g = lane >> 4;
 
     WR wr[kRegs];
-    // where chunk c (0 <= c < kChunks of a stage) lives in wr
-    auto chunk_base = [&](int c) constexpr {
-        if (kStream) return (c % kSlots) * CF;
-        return c < S::GA ? c * CF : S::GA * CF + (c - S::GA) * CG;
-    };
-    // load chunk c (of any stage: the same weights) into its registers.
-    // Addresses are a wave-uniform base (scalar registers) plus this lane's
-    // 32-bit byte offset, which keeps per-chunk addresses out of VGPRs.
+    // where chunk c (0 <= c < kChunks) lives in wr
+    auto chunk_base = [&](int c) constexpr { return c < S::GA ? c * CF : S::GA * CF + (c - S::GA) * CG; };
+    // load chunk c into its registers. Addresses are a wave-uniform base
+    // (scalar registers) plus this lane's 32-bit byte offset, which keeps
+    // per-chunk addresses out of VGPRs.
     const int wu = __builtin_amdgcn_readfirstlane(w);
     const char* kf = reinterpret_cast<const char*>(KF + int64_t(wu) * S::GA * N * N);
     const char* kg = reinterpret_cast<const char*>(KG + int64_t(wu) * S::GB * M * M);
     const uint32_t lf = static_cast<uint32_t>((col * N + S::KSF * g) * sizeof(TW));
     const uint32_t lg = static_cast<uint32_t>((col * M + S::KSG * g) * sizeof(TW));
     auto load_chunk = [&](int c) {
-        c %= kChunks;
         const int base = chunk_base(c);
         if (c < S::GA) {
             // K_F[alpha = w GA + c][0][beta = 16 nt + col][gamma = KSF g ..]
@@ -249,28 +237,8 @@ __global__ __launch_bounds__(NW * 64 + (NW == 16 ? 0 : 64)) void monarch_pair_ke
                         reinterpret_cast<const TW*>(kg + (p * M + 16 * nt) * M * sizeof(TW) + lg), S::KSG / 4);
         }
     };
-    // the requests keep their place in the program: no compiler pass may
-    // move memory operations across this point (the scheduler would sink a
-    // prefetch next to its use; earlier passes could merge or reorder loads)
-    auto order_point = [] {
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    // refill the slot of chunk c, just used, with chunk c + kSlots
-    auto refill = [&](int c) {
-        if (kStream) {
-            order_point();
-            load_chunk(c + kSlots);
-            order_point();
-        }
-    };
-    // the first chunks, in the order the refills keep afterwards (waits are
-    // counted against the order of requests, the first stage's included)
 #pragma unroll
-    for (int c = 0; c < (kStream ? kSlots : kChunks); ++c) {
-        load_chunk(c);
-        if (kStream) order_point();
-    }
+    for (int c = 0; c < kChunks; ++c) load_chunk(c);
 
     // SELF: every wave copies instructions w, w + NW, .. of each stage with
     // LDS DMA issued from inline assembly (the compiler would wait for any
@@ -352,7 +320,6 @@ __global__ __launch_bounds__(NW * 64 + (NW == 16 ? 0 : 64)) void monarch_pair_ke
                 for (int nt = 0; nt < S::NTF; ++nt)
                     acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(
                         xv[ks / 4][ks % 4], w_at(wr[base + nt * (S::KSF / 4) + ks / 4], ks % 4), acc[nt], 0, 0, 0);
-            refill(j);
 #pragma unroll
             for (int nt = 0; nt < S::NTF; ++nt)
 #pragma unroll
@@ -380,8 +347,6 @@ __global__ __launch_bounds__(NW * 64 + (NW == 16 ? 0 : 64)) void monarch_pair_ke
                             zv[u], w_at(wr[base + nt * (S::KSG / 4) + ks / 4], ks % 4), acc[u][nt], 0, 0, 0);
                 }
             }
-#pragma unroll
-            for (int u = 0; u < S::BB; ++u) refill(S::GA + j + u);
 #pragma unroll
             for (int nt = 0; nt < S::NTG; ++nt)
 #pragma unroll
@@ -455,9 +420,9 @@ ks_status_t launch_mn(const void* W0, const void* W1, const void* X, float* Y, i
 template <typename TX, typename TW>
 ks_status_t launch_typed(int M, int N, const void* W0, const void* W1, const void* X, float* Y, int64_t batch,
                          hipStream_t stream, int num_cus) {
-    // 32 x 32 blocks take eight compute waves (two a SIMD, a ring of four
-    // weight chunks each): 157 -> 135 us with bf16 weights (65,536 rows),
-    // unchanged with fp32 weights, where streaming the blocks from L2 limits
+    // 32 x 32 blocks take sixteen compute waves, which hold all of the
+    // pair's weights in registers (65,536 rows, fp32: 115 us; streaming them
+    // from L2 for each stage through register rings of eight waves took 182)
     if (M == 16 && N == 16) return launch_mn<16, 16, 4, TX, TW>(W0, W1, X, Y, batch, stream, num_cus);
     if (M == 16 && N == 32) return launch_mn<16, 32, 4, TX, TW>(W0, W1, X, Y, batch, stream, num_cus);
     if (M == 32 && N == 16) return launch_mn<32, 16, 4, TX, TW>(W0, W1, X, Y, batch, stream, num_cus);
