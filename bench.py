@@ -62,6 +62,8 @@ WORKLOAD_SOURCES = {
     "gpt2_mlp": ("ks_fused.hip",),
     "gpt2_mlp:nofuse": ("ks_mfma.hip", "ks_valu.hip"),
     "monarch_n1024": ("ks_monarch.hip",),
+    "radix4_n4096": ("ks_resident.hip", "ks_rowchain.hip", "ks_digitchain.hip"),
+    "radix2_n1024": ("ks_resident.hip", "ks_rowchain.hip", "ks_digitchain.hip"),
 }
 
 
