@@ -291,6 +291,38 @@ ks_status_t ks_plan_describe(ks_pattern_t p, int64_t batch, ks_dtype_t dt,
                              char* buf, size_t len);
 
 /*
+ * ks_pair_closure: the closure rule for running factor f and then factor g
+ * in one pass, which the chain planner applies (KS abstract page, first
+ * paragraph, first sentence: Butterfly and Monarch matrices are chains of
+ * such factors). f's output groups (fixed alpha, delta of f; all beta) and
+ * g's input groups (fixed alpha, delta of g; all gamma) link the
+ * intermediate's n_out(f) values into closed components: a component's
+ * outputs depend only on its own inputs, f blocks and g blocks. Reports the
+ * component count, the largest component's sizes and the tile of components
+ * whose X reads come in runs of 16 bytes (4 fp32 values). A pair can run
+ * fused only if such a tile's intermediates fit in LDS and its weights near
+ * the compute units; the planner also needs a kernel family for the shape.
+ * Pure host code, no HIP call. KS_ERR_NULL (out), KS_ERR_PATTERN,
+ * KS_ERR_CHAIN_MISMATCH (n_out(f) != n_in(g)), KS_ERR_UNSUPPORTED (an
+ * intermediate of more than 2^22 values is not analysed).
+ */
+typedef struct ks_closure_t {
+    int64_t components;       /* closed components of the intermediate */
+    int64_t mid;              /* intermediate values of the largest component */
+    int64_t inputs;           /* values of X it reads */
+    int64_t outputs;          /* values of Y it writes */
+    int64_t weights;          /* weights it needs: its blocks of f and of g */
+    int64_t in_run;           /* shortest run of consecutive X indices it reads */
+    int64_t out_run;          /* shortest run of consecutive Y indices it writes */
+    int64_t tile_components;  /* components per tile with 16-byte X runs */
+    int64_t tile_weights;     /* weights of such a tile */
+    int32_t uniform;          /* 1: all components have the same size */
+    int32_t reserved;         /* 0 */
+} ks_closure_t;
+
+ks_status_t ks_pair_closure(ks_pattern_t f, ks_pattern_t g, ks_closure_t* out);
+
+/*
  * ks_chain_describe: one description per launch group of the chain
  * ks_chain_matmul would run for these arguments, "[first..last] kernel",
  * separated by "; ", into buf (NUL-terminated, truncated to len). Same

@@ -7,6 +7,8 @@
 // include/ks.h for the layouts.
 
 #include <algorithm>
+#include <array>
+#include <map>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -188,6 +190,30 @@ struct ChainPlan {
     size_t buf_bytes = 0;          // bytes per workspace buffer
 };
 
+// The closure rule (ks_closure.cpp) as a precondition of fusing a pair: a
+// tile of its closed components with 16-byte X runs must keep its weights
+// (at most 64 K values: half a compute unit's register file in fp32) and
+// 16 rows of its intermediates (at most 128 KB of LDS) on chip. A kernel
+// family for the shape is needed as well. Pairs too large to analyse
+// (intermediates over 2^22 values) are left to the families' own checks.
+// Results are cached: the analysis is a union-find over the intermediate.
+bool closure_fits(const Shape& f, const Shape& g) {
+    static std::mutex mu;
+    static std::map<std::array<int, 8>, bool> cache;
+    const std::array<int, 8> key{f.a, f.b, f.c, f.d, g.a, g.b, g.c, g.d};
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        const auto it = cache.find(key);
+        if (it != cache.end()) return it->second;
+    }
+    ks::Closure c;
+    const bool fits = !ks::closure_of(f, g, &c) ||
+                      (c.tile_weights <= 65536 && c.tile_components * c.mid * 16 * 4 <= 128 * 1024);
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache.size() < 4096) cache.emplace(key, fits);
+    return fits;
+}
+
 ks_status_t plan_chain(const ks_pattern_t* p, int n, int64_t batch, int dt,
                        unsigned flags, ChainPlan* plan) {
     if (!p) return KS_ERR_NULL;
@@ -206,17 +232,21 @@ ks_status_t plan_chain(const ks_pattern_t* p, int n, int64_t batch, int dt,
     for (int k = 0; k < n;) {
         const int xt = (k == 0) ? plan->xt0 : ks::kF32;
         int len = 1, kind = 0;
+        const bool pair_ok =
+            flags == KS_CHAIN_AUTO && k + 1 < n && closure_fits(plan->shapes[k], plan->shapes[k + 1]);
         if (flags == KS_CHAIN_AUTO && k + 1 < n) {
-            if (ks::fused_pair_supports(plan->shapes[k], plan->shapes[k + 1], xt, plan->wt, plan->wt)) {
+            if (pair_ok && ks::fused_pair_supports(plan->shapes[k], plan->shapes[k + 1], xt, plan->wt, plan->wt)) {
                 len = 2;
                 kind = 1;
-            } else if (ks::slab_pair_supports(plan->shapes[k], plan->shapes[k + 1], xt, plan->wt, plan->wt)) {
+            } else if (pair_ok && ks::slab_pair_supports(plan->shapes[k], plan->shapes[k + 1], xt, plan->wt, plan->wt)) {
                 len = 2;
                 kind = 2;
-            } else if (ks::strided_pair_supports(plan->shapes[k], plan->shapes[k + 1], xt, plan->wt, plan->wt)) {
+            } else if (pair_ok &&
+                       ks::strided_pair_supports(plan->shapes[k], plan->shapes[k + 1], xt, plan->wt, plan->wt)) {
                 len = 2;
                 kind = 4;
-            } else if (ks::monarch_pair_supports(plan->shapes[k], plan->shapes[k + 1], xt, plan->wt, plan->wt)) {
+            } else if (pair_ok &&
+                       ks::monarch_pair_supports(plan->shapes[k], plan->shapes[k + 1], xt, plan->wt, plan->wt)) {
                 len = 2;
                 kind = 5;
             } else {
@@ -580,6 +610,30 @@ ks_status_t ks_plan_describe(ks_pattern_t p, int64_t batch, ks_dtype_t dt, char*
     return KS_OK;
 }
 
+ks_status_t ks_pair_closure(ks_pattern_t f, ks_pattern_t g, ks_closure_t* out) {
+    if (!out) return KS_ERR_NULL;
+    Shape sf, sg;
+    ks_status_t st = shape_of(f, &sf);
+    if (st != KS_OK) return st;
+    st = shape_of(g, &sg);
+    if (st != KS_OK) return st;
+    if (sf.n_out != sg.n_in) return KS_ERR_CHAIN_MISMATCH;
+    ks::Closure c;
+    if (!ks::closure_of(sf, sg, &c)) return KS_ERR_UNSUPPORTED;
+    out->components = c.components;
+    out->mid = c.mid;
+    out->inputs = c.inputs;
+    out->outputs = c.outputs;
+    out->weights = c.weights;
+    out->in_run = c.in_run;
+    out->out_run = c.out_run;
+    out->tile_components = c.tile_components;
+    out->tile_weights = c.tile_weights;
+    out->uniform = c.uniform ? 1 : 0;
+    out->reserved = 0;
+    return KS_OK;
+}
+
 ks_status_t ks_chain_describe(const ks_pattern_t* p, int n, int64_t batch, ks_dtype_t dt, unsigned flags, char* buf,
                               size_t len) {
     if (!buf || len == 0) return KS_ERR_NULL;
@@ -616,8 +670,21 @@ ks_status_t ks_chain_describe(const ks_pattern_t* p, int n, int64_t batch, ks_dt
                 ks_plan_describe(pk, batch, static_cast<ks_dtype_t>(fdt), part, sizeof part);
             }
         }
-        const int w = std::snprintf(buf + used, len - used, "%s[%d..%d] %s", g ? "; " : "", k,
-                                    k + plan.group_len[g] - 1, part);
+        // the closure of the pair that this group's boundary splits
+        char note[224];
+        note[0] = '\0';
+        const int last = k + plan.group_len[g] - 1;
+        ks::Closure cl;
+        if (flags == KS_CHAIN_AUTO && g + 1 < groups && ks::closure_of(plan.shapes[last], plan.shapes[last + 1], &cl))
+            std::snprintf(note, sizeof note,
+                          " (pair %d-%d unfused: %lld closed components of %lld values, 16-byte-run tile of %lld: "
+                          "%lld weights, %s)",
+                          last, last + 1, static_cast<long long>(cl.components), static_cast<long long>(cl.mid),
+                          static_cast<long long>(cl.tile_components), static_cast<long long>(cl.tile_weights),
+                          closure_fits(plan.shapes[last], plan.shapes[last + 1])
+                              ? "fits on chip, no fused kernel for this shape"
+                              : "too large for on-chip fusion");
+        const int w = std::snprintf(buf + used, len - used, "%s[%d..%d] %s%s", g ? "; " : "", k, last, part, note);
         if (w < 0) break;
         used = std::min(len - 1, used + static_cast<size_t>(w));
     }

@@ -142,6 +142,22 @@ bool resident_chain_aligned(const void* X, const float* Y);
 ks_status_t launch_resident_chain(const Shape* s, int n, int xt, int wt, const void* const* W, const void* X,
                                   float* Y, int64_t batch, hipStream_t stream, int num_cus);
 int resident_chain_describe(const Shape* s, int n, char* buf, size_t len);
+// The closure rule for fusing factor f then g (ks_closure.cpp): closed
+// components of the intermediate, with the largest component's sizes (in
+// values) and the shortest runs of consecutive indices its X reads and Y
+// writes form; a tile of components whose X reads come in 16-byte runs.
+constexpr int64_t kMaxClosureMid = int64_t(1) << 22;
+struct Closure {
+    int64_t components;       // closed components
+    int64_t mid;              // intermediates of the largest component
+    int64_t inputs, outputs;  // its values of X read and of Y written
+    int64_t weights;          // its weights (F blocks and G blocks)
+    int64_t in_run, out_run;  // shortest runs of consecutive X and Y indices (component of index 0)
+    int64_t tile_components;  // components per 16-byte-run tile
+    int64_t tile_weights;     // weights of such a tile
+    bool uniform;             // every component the same size
+};
+bool closure_of(const Shape& f, const Shape& g, Closure* c);
 ks_status_t launch_row_chain(const Shape* s, int n, int xt, int wt, const void* const* W, const void* X, float* Y,
                              int64_t batch, hipStream_t stream, int num_cus);
 int row_chain_describe(const Shape* s, int n, char* buf, size_t len);

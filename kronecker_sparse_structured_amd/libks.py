@@ -60,6 +60,13 @@ class ks_options_t(ctypes.Structure):
                 ("reserved", ctypes.c_int32 * 3)]
 
 
+class ks_closure_t(ctypes.Structure):
+    _fields_ = [("components", ctypes.c_int64), ("mid", ctypes.c_int64), ("inputs", ctypes.c_int64),
+                ("outputs", ctypes.c_int64), ("weights", ctypes.c_int64), ("in_run", ctypes.c_int64),
+                ("out_run", ctypes.c_int64), ("tile_components", ctypes.c_int64), ("tile_weights", ctypes.c_int64),
+                ("uniform", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -114,6 +121,8 @@ def load(path: str = LIB_PATH):
     lib.ks_chain_describe.argtypes = [ctypes.POINTER(ks_pattern_t), i32, i64, i32, ctypes.c_uint,
                                       ctypes.c_char_p, ctypes.c_size_t]
     lib.ks_chain_describe.restype = i32
+    lib.ks_pair_closure.argtypes = [ks_pattern_t, ks_pattern_t, ctypes.POINTER(ks_closure_t)]
+    lib.ks_pair_closure.restype = i32
     lib.ks_matmul_dx_workspace_size.argtypes = [ks_pattern_t, i32, ctypes.POINTER(ctypes.c_size_t)]
     lib.ks_matmul_dx_workspace_size.restype = i32
     lib.ks_matmul_dx.argtypes = [ks_pattern_t, vp, vp, vp, i64, i32, vp, ctypes.c_size_t, vp]
@@ -276,6 +285,13 @@ def ks_chain_groups(ps: Sequence, batch: int, dtype: int, flags: int = CHAIN_AUT
         out.append(list(range(k, k + ln)))
         k += ln
     return out
+
+
+def ks_pair_closure(f, g) -> dict:
+    """The closure rule for running factor f then g in one pass (ks.h)."""
+    out = ks_closure_t()
+    _raise(load().ks_pair_closure(_pattern(f), _pattern(g), ctypes.byref(out)), "ks_pair_closure", True)
+    return {name: int(getattr(out, name)) for name, _ in ks_closure_t._fields_ if name != "reserved"}
 
 
 def ks_chain_describe(ps: Sequence, batch: int, dtype: int, flags: int = CHAIN_AUTO) -> str:

@@ -5,6 +5,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 from kronecker_sparse_structured_amd import libks
@@ -189,6 +190,101 @@ def test_chain_describe():
     assert libks.ks_chain_describe(bf, 4096, libks.DTYPE_F32, libks.CHAIN_NO_FUSE).count(";") == 3
     with pytest.raises(libks.KSError):
         libks.ks_chain_describe([(1, 4, 4, 16), (1, 4, 4, 8)], 10, libks.DTYPE_F32)
+
+
+def _closure_brute(f, g):
+    """Closed components of the intermediate of f then g, by search over the
+    intermediate indices (independent of the library's union-find)."""
+    a1, b1, c1, d1 = f
+    a2, b2, c2, d2 = g
+    n = a1 * b1 * d1
+    assert n == a2 * c2 * d2
+    comp = [-1] * n
+    comps = []
+    for s in range(n):
+        if comp[s] >= 0:
+            continue
+        stack, members = [s], []
+        comp[s] = len(comps)
+        while stack:
+            m = stack.pop()
+            members.append(m)
+            al1, rest = divmod(m, b1 * d1)
+            de1 = rest % d1
+            al2, rest2 = divmod(m, c2 * d2)
+            de2 = rest2 % d2
+            nbrs = [al1 * b1 * d1 + be * d1 + de1 for be in range(b1)]
+            nbrs += [al2 * c2 * d2 + ga * d2 + de2 for ga in range(c2)]
+            for q in nbrs:
+                if comp[q] < 0:
+                    comp[q] = comp[s]
+                    stack.append(q)
+        comps.append(members)
+    big = max(comps, key=len)
+    fgroups = {(m // (b1 * d1), m % d1) for m in big}
+    ggroups = {(m // (c2 * d2), m % d2) for m in big}
+
+    def shortest_run(idx):
+        idx = sorted(idx)
+        best, run = len(idx), 1
+        for i in range(1, len(idx) + 1):
+            if i < len(idx) and idx[i] == idx[i - 1] + 1:
+                run += 1
+            else:
+                best, run = min(best, run), 1
+        return best
+
+    c0 = comps[0]
+    f0 = {(m // (b1 * d1), m % d1) for m in c0}
+    g0 = {(m // (c2 * d2), m % d2) for m in c0}
+    xin = [al * c1 * d1 + ga * d1 + de for al, de in f0 for ga in range(c1)]
+    yout = [al * b2 * d2 + be * d2 + de for al, de in g0 for be in range(b2)]
+    in_run = shortest_run(xin)
+    tile = min(len(comps), max(1, -(-4 // in_run)))
+    weights = len(fgroups) * b1 * c1 + len(ggroups) * b2 * c2
+    return {"components": len(comps), "mid": len(big), "inputs": len(fgroups) * c1,
+            "outputs": len(ggroups) * b2, "weights": weights, "in_run": in_run,
+            "out_run": shortest_run(yout), "tile_components": tile, "tile_weights": tile * weights,
+            "uniform": int(len({len(c) for c in comps}) == 1)}
+
+
+def test_pair_closure():
+    """The closure rule on the chains the pages name (figures derived by hand:
+    the GPT-2 MLP pair splits each 4096-value intermediate into 8 closed
+    components of 512 with 32 KiB + 16 KiB of fp32 weights; each butterfly
+    pair of the 65,536-point chain into 256 of 256, whose X indices sit 256
+    apart; a Monarch pair is one component, the whole row)."""
+    c = libks.ks_pair_closure((1, 64, 16, 64), (64, 8, 8, 8))
+    assert (c["components"], c["mid"], c["weights"] * 4) == (8, 512, 48 * 1024)
+    c = libks.ks_pair_closure((1, 16, 16, 4096), (16, 16, 16, 256))
+    assert (c["components"], c["mid"], c["in_run"], c["tile_components"]) == (256, 256, 1, 4)
+    c = libks.ks_pair_closure((256, 16, 16, 16), (4096, 16, 16, 1))
+    assert (c["components"], c["in_run"], c["tile_components"], c["tile_weights"]) == (256, 256, 1, 8192)
+    c = libks.ks_pair_closure((32, 32, 32, 1), (1, 32, 32, 32))
+    assert (c["components"], c["mid"], c["weights"]) == (1, 1024, 65536)
+    with pytest.raises(libks.KSError):
+        libks.ks_pair_closure((1, 4, 4, 16), (1, 4, 4, 8))           # 64 -> 32: chain mismatch
+    with pytest.raises(libks.KSError):
+        libks.ks_pair_closure((1, 8192, 1, 1024), (1024, 8, 8192, 1))  # 8 M intermediates: not analysed
+
+
+def test_pair_closure_brute_force():
+    """Every field against an independent search on random small pairs,
+    uneven sizes included."""
+    rng = np.random.default_rng(7)
+    checked = 0
+    while checked < 60:
+        a1, b1, d1 = (int(v) for v in rng.integers(1, 7, size=3))
+        n = a1 * b1 * d1
+        divs = [v for v in range(1, n + 1) if n % v == 0]
+        c2 = int(rng.choice(divs))
+        rest = n // c2
+        d2 = int(rng.choice([v for v in range(1, rest + 1) if rest % v == 0]))
+        a2 = rest // d2
+        f = (a1, b1, int(rng.integers(1, 6)), d1)
+        g = (a2, int(rng.integers(1, 6)), c2, d2)
+        assert libks.ks_pair_closure(f, g) == _closure_brute(f, g), (f, g)
+        checked += 1
 
 
 def test_chain_plan():
