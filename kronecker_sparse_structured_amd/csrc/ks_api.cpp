@@ -190,13 +190,14 @@ struct ChainPlan {
     size_t buf_bytes = 0;          // bytes per workspace buffer
 };
 
-// The closure rule (ks_closure.cpp) as a precondition of fusing a pair: a
-// tile of its closed components with 16-byte X runs must keep its weights
-// (at most 64 K values: half a compute unit's register file in fp32) and
-// 16 rows of its intermediates (at most 128 KB of LDS) on chip. A kernel
-// family for the shape is needed as well. Pairs too large to analyse
-// (intermediates over 2^22 values) are left to the families' own checks.
-// Results are cached: the analysis is a union-find over the intermediate.
+// The closure rule (ks_closure.cpp) for a pair: whether a tile of its closed
+// components with 16-byte X runs keeps its weights (at most 64 K values:
+// half a compute unit's register file in fp32) and 16 rows of its
+// intermediates (at most 128 KB of LDS) on chip, i.e. whether the pair can
+// run as one pass that reads every X value once. Fused kernels may also
+// split components and re-read X from L2 instead (the GPT-2 pair kernel does,
+// for 8 beta0 a workgroup), so this reports rather than gates. Results are
+// cached: the analysis is a union-find over the intermediate.
 bool closure_fits(const Shape& f, const Shape& g) {
     static std::mutex mu;
     static std::map<std::array<int, 8>, bool> cache;
@@ -232,21 +233,17 @@ ks_status_t plan_chain(const ks_pattern_t* p, int n, int64_t batch, int dt,
     for (int k = 0; k < n;) {
         const int xt = (k == 0) ? plan->xt0 : ks::kF32;
         int len = 1, kind = 0;
-        const bool pair_ok =
-            flags == KS_CHAIN_AUTO && k + 1 < n && closure_fits(plan->shapes[k], plan->shapes[k + 1]);
         if (flags == KS_CHAIN_AUTO && k + 1 < n) {
-            if (pair_ok && ks::fused_pair_supports(plan->shapes[k], plan->shapes[k + 1], xt, plan->wt, plan->wt)) {
+            if (ks::fused_pair_supports(plan->shapes[k], plan->shapes[k + 1], xt, plan->wt, plan->wt)) {
                 len = 2;
                 kind = 1;
-            } else if (pair_ok && ks::slab_pair_supports(plan->shapes[k], plan->shapes[k + 1], xt, plan->wt, plan->wt)) {
+            } else if (ks::slab_pair_supports(plan->shapes[k], plan->shapes[k + 1], xt, plan->wt, plan->wt)) {
                 len = 2;
                 kind = 2;
-            } else if (pair_ok &&
-                       ks::strided_pair_supports(plan->shapes[k], plan->shapes[k + 1], xt, plan->wt, plan->wt)) {
+            } else if (ks::strided_pair_supports(plan->shapes[k], plan->shapes[k + 1], xt, plan->wt, plan->wt)) {
                 len = 2;
                 kind = 4;
-            } else if (pair_ok &&
-                       ks::monarch_pair_supports(plan->shapes[k], plan->shapes[k + 1], xt, plan->wt, plan->wt)) {
+            } else if (ks::monarch_pair_supports(plan->shapes[k], plan->shapes[k + 1], xt, plan->wt, plan->wt)) {
                 len = 2;
                 kind = 5;
             } else {
@@ -683,7 +680,7 @@ ks_status_t ks_chain_describe(const ks_pattern_t* p, int n, int64_t batch, ks_dt
                           static_cast<long long>(cl.tile_components), static_cast<long long>(cl.tile_weights),
                           closure_fits(plan.shapes[last], plan.shapes[last + 1])
                               ? "fits on chip, no fused kernel for this shape"
-                              : "too large for on-chip fusion");
+                              : "too large to fuse without re-reading X");
         const int w = std::snprintf(buf + used, len - used, "%s[%d..%d] %s%s", g ? "; " : "", k, last, part, note);
         if (w < 0) break;
         used = std::min(len - 1, used + static_cast<size_t>(w));
