@@ -30,7 +30,11 @@ Printed: one JSON line with
   per_group / per_factor   every launch group, and every factor as a single
              launch, timed the same way;
   cpu_baseline   the fp64 oracle timed on this host's cores on a bounded
-             sample of the same workload.
+             sample of the same workload;
+  other_configs  (default run only; --headline-only skips it) the other
+             configurations timed the same way and summarised: the ViT
+             factor, the GPT-2 chain fused and one launch per factor, the
+             butterfly with bf16 inputs, and the 51-pattern square sweep.
 """
 from __future__ import annotations
 
@@ -130,6 +134,9 @@ def parse():
                     help="with --sweep: also write the per-pattern table as text to PATH; with --from-log: "
                          "write it from a saved --sweep output instead (no GPU)")
     ap.add_argument("--from-log", metavar="LOG", help="a saved --sweep output (see --sweep-text)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the other configurations' summary (other_configs) of the default run; "
+                         "profiler runs use it so that only the headline workload's kernels are traced")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of a "
                          "`--calib-copy` run into profiles/traffic_counters.json and exit")
@@ -479,8 +486,141 @@ def main():
         out["per_group"] = per_group
     if per_factor is not None:
         out["per_factor"] = per_factor
+    if (args.workload == "butterfly65536" and args.dtype == "f32" and args.kernel == "auto" and not args.no_fuse
+            and not args.no_factors and not args.calib_copy and not args.headline_only):
+        del Xt, Yt, wst, Wt, calls
+        torch.cuda.empty_cache()
+        try:
+            out["other_configs"] = other_configs(lib, sp, stream, torch, np, datagen, libks)
+        except Exception as e:  # noqa: BLE001
+            # the headline line is printed whatever happens to this leg
+            out["other_configs"] = {"error": "%s: %s" % (type(e).__name__, e)}
     print(json.dumps(out), flush=True)
     return 0
+
+
+def time_launches(run, nset, stream, torch, reps=20) -> float:
+    """Mean milliseconds of run(i) over reps back-to-back calls on rotated
+    sets, after the time-based warm-up; HIP events on the launch stream."""
+    warm_up(lambda i: run(i % nset), 3, torch)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(reps):
+        run(i % nset)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def time_workload(wl, bf16, flags, lib, sp, stream, torch, np, datagen, libks, reps=20) -> dict:
+    """One workload as the contract run does it (ks_matmul for one factor,
+    ks_chain_matmul for a chain) on seeded N(0, 1) device inputs with the
+    workload's weight scales, rotated so each call reads from HBM. Returns
+    the mean call time and the algorithmic bytes as run and fused."""
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.seed)
+    dt = libks.DTYPE_BF16 if bf16 else libks.DTYPE_F32
+    el = torch.bfloat16 if bf16 else torch.float32
+    xb = 2 if bf16 else 4
+    batch = wl.batch
+    Wt = [(torch.randn(datagen.nnz(p), generator=gen, device=dev) * sg).to(el)
+          for p, sg in zip(wl.patterns, wl.sigmas)]
+    chain = len(wl.patterns) > 1
+    groups = libks.ks_chain_groups(wl.patterns, batch, dt, flags) if chain else [[0]]
+    bytes_run, x_sz = 0, xb
+    for grp in groups:
+        bytes_run += x_sz * batch * datagen.n_in(wl.patterns[grp[0]]) + 4 * batch * datagen.n_out(
+            wl.patterns[grp[-1]]) + sum(xb * datagen.nnz(wl.patterns[k]) for k in grp)
+        x_sz = 4
+    wsum = sum(xb * datagen.nnz(p) for p in wl.patterns)
+    bytes_min = xb * batch * wl.n_in + 4 * batch * wl.n_out + wsum
+    ws_bytes = libks.ks_chain_workspace_size(wl.patterns, batch, dt, flags) if chain else 0
+    nset = max(2, int(np.ceil(CACHE_BYTES / (bytes_min + 2 * ws_bytes))) + 1)
+    Xt = [torch.randn((batch, wl.n_in), generator=gen, device=dev).to(el)]
+    for _ in range(nset - 1):
+        Xt.append(Xt[0].clone())
+    Yt = [torch.empty((batch, wl.n_out), dtype=torch.float32, device=dev) for _ in range(nset)]
+    wst = [torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None for _ in range(nset)]
+    if chain:
+        pats = (libks.ks_pattern_t * len(wl.patterns))(*[libks.ks_pattern_t(*p) for p in wl.patterns])
+        wptrs = (ctypes.c_void_p * len(Wt))(*[w.data_ptr() for w in Wt])
+        calls = [(lib.ks_chain_matmul,
+                  (pats, len(wl.patterns), wptrs, ctypes.c_void_p(Xt[k].data_ptr()),
+                   ctypes.c_void_p(Yt[k].data_ptr()), batch, dt,
+                   ctypes.c_void_p(wst[k].data_ptr() if wst[k] is not None else None), ws_bytes, flags, sp))
+                 for k in range(nset)]
+    else:
+        pat = libks.ks_pattern_t(*wl.patterns[0])
+        calls = [(lib.ks_matmul, (pat, ctypes.c_void_p(Wt[0].data_ptr()), ctypes.c_void_p(Xt[k].data_ptr()),
+                                  ctypes.c_void_p(Yt[k].data_ptr()), batch, dt, sp)) for k in range(nset)]
+
+    def run(i):
+        fn, a = calls[i]
+        st = fn(*a)
+        if st != 0:
+            raise libks.KSError(st, "bench %s" % wl.name)
+
+    ms = time_launches(run, nset, stream, torch, reps)
+    flops = sum(2 * batch * datagen.nnz(p) for p in wl.patterns)
+    del Xt, Yt, wst, Wt, calls
+    return {"ms": ms, "bytes_run": bytes_run, "bytes_min": bytes_min, "flops": flops,
+            "launches": len(groups)}
+
+
+def other_configs(lib, sp, stream, torch, np, datagen, libks) -> dict:
+    """The other configurations of the KS workloads, each timed like the
+    headline (rotated inputs, back-to-back calls, HIP events), summarised:
+    the ViT factor, the GPT-2 chain fused and one launch per factor, the
+    65,536-point butterfly with bf16 inputs and weights, and the 51-pattern
+    square sweep (roofline fraction of each pattern: bytes over 8 TB/s or
+    flops over the fp32 matrix peak, whichever takes longer)."""
+    out = {}
+
+    def frac(b, ms):
+        return round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+
+    r = time_workload(datagen.get("vit_mlp"), False, libks.CHAIN_AUTO, lib, sp, stream, torch, np, datagen,
+                      libks)
+    out["vit_mlp"] = {"dtype": "f32", "ms": round(r["ms"], 5), "GB/s": round(r["bytes_run"] / r["ms"] / 1e6, 1),
+                      "TFLOP/s": round(r["flops"] / r["ms"] / 1e9, 2), "frac": frac(r["bytes_run"], r["ms"]),
+                      "plan": libks.ks_plan_describe((4, 64, 16, 6), 25216, libks.DTYPE_F32)}
+    g = {}
+    for name, flags in (("fused", libks.CHAIN_AUTO), ("one_launch_per_factor", libks.CHAIN_NO_FUSE)):
+        r = time_workload(datagen.get("gpt2_mlp"), False, flags, lib, sp, stream, torch, np, datagen, libks)
+        g[name] = {"ms": round(r["ms"], 5), "launches": r["launches"],
+                   "frac_as_run": frac(r["bytes_run"], r["ms"]),
+                   "frac_vs_fused_minimum": frac(r["bytes_min"], r["ms"])}
+    out["gpt2_mlp"] = {"dtype": "f32", **g}
+    r = time_workload(datagen.get("butterfly65536"), True, libks.CHAIN_AUTO, lib, sp, stream, torch, np, datagen,
+                      libks, reps=10)
+    out["butterfly65536_bf16"] = {"dtype": "bf16", "ms": round(r["ms"], 5), "launches": r["launches"],
+                                  "GB/s": round(r["bytes_run"] / r["ms"] / 1e6, 1),
+                                  "frac_as_run": frac(r["bytes_run"], r["ms"]),
+                                  "frac_vs_fused_minimum": frac(r["bytes_min"], r["ms"])}
+    fr, small, big = [], [], []
+    for p in datagen.square_sweep_patterns():
+        wl = datagen.get("square_%d_%d_%d_%d" % p)
+        r = time_workload(wl, False, libks.CHAIN_AUTO, lib, sp, stream, torch, np, datagen, libks, reps=30)
+        t_roof = max(r["bytes_run"] / (HBM_PEAK_GBS * 1e9), r["flops"] / (FP32_PEAK_TFLOPS * 1e12))
+        f = t_roof / (r["ms"] * 1e-3)
+        fr.append(f)
+        (small if p[1] <= 32 else big).append(f)
+        if p[1] == 128:
+            out.setdefault("_b128", []).append(round(f, 3))
+    out["square_sweep"] = {
+        "dtype": "f32", "patterns": len(fr), "rows": 16384,
+        "roofline_frac_median": round(float(np.median(fr)), 4),
+        "roofline_frac_min": round(float(np.min(fr)), 4),
+        "roofline_frac_max": round(float(np.max(fr)), 4),
+        "b_le_32_patterns": len(small),
+        "b_le_32_hbm_frac_median": round(float(np.median(small)), 4),
+        "b_le_32_at_or_above_0.70": int(sum(f >= 0.70 for f in small)),
+        "b_128_mfma_fracs": out.pop("_b128"),
+    }
+    torch.cuda.empty_cache()
+    return out
 
 
 def traffic_key(args) -> str:
