@@ -11,21 +11,23 @@
 // tensors. The GPT-2-medium MLP shape (1, 64, 16, 64) -> (64, 8, 8, 8) is of
 // this kind.
 //
-// Workgroup: 8 consecutive beta0 (= alpha1) values and a range of rows; one
-// loader wave streams whole rows of X into an LDS ring (ks_stream.h), each
-// row followed by 32 bytes of padding so that the four rows a matrix-core
-// instruction reads start in different banks; the 8 workgroups that share
-// rows run on the same XCD, so X is fetched from HBM once and served to the
-// others from L2. Per stage of 4 rows, four consumer waves
+// Workgroup: BT consecutive beta0 (= alpha1) values (32, 16 or 8, the
+// largest that divides b0) and a range of rows; one loader wave streams whole
+// rows of X into an LDS ring (ks_stream.h), each row followed by 32 bytes of
+// padding so that the four rows a matrix-core instruction reads start in
+// different banks; the b0 / BT workgroups that share rows run on the same
+// XCD, so X is fetched from HBM once and served to the others from L2. Per
+// stage of 4 rows, eight consumer waves
 //  (A) compute Z[r][beta0][delta0] into LDS on the matrix cores: for a fixed
 //      delta0 it is a (rows x c0) by (c0 x beta0) product, and the 16-block
 //      4x4x1 fp32 MFMA does 16 such delta0 at once (weights in registers),
 //  (B) compute Y[r][alpha1][beta1][delta1] of the previous stage from the
-//      other Z buffer: for fp32 rows on the VALU, runs of 4 delta1 per
-//      thread (c1 FMAs per value, weights in registers) stored as 16-byte
-//      vectors; for bf16 rows on the matrix cores again, block = (alpha1,
-//      delta1), a (rows x c1) by (c1 x beta1) product per block.
-// One LDS barrier per stage separates the two.
+//      other Z buffer on the VALU: runs of 4 delta1 per thread (c1 FMAs per
+//      value, weights in registers), stored as 16-byte vectors.
+// One LDS barrier per stage separates the two. A wide tile (BT = 32 for
+// GPT-2-medium's b0 = 64) cuts the L2 re-reads of X to b0 / BT per row and
+// keeps more X bytes in flight per byte of Y than two narrow workgroups
+// per compute unit would.
 // Z never leaves the chip: the pair moves |X| + |Y| + weights through HBM
 // instead of |X| + 2|Z| + |Y|.
 //
@@ -52,27 +54,29 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 // Shape family handled: F0 = (1, b0, 16, 64), F1 = (b0, 8, 8, 8), b0 % 8 == 0.
 constexpr int kC0 = 16, kD0 = 64;          // first factor: gamma0, delta0 extents
 constexpr int kB1 = 8, kC1 = 8, kD1 = 8;   // second factor: beta1, gamma1, delta1 extents
-constexpr int kBT = 8;                     // beta0 (= alpha1) values per workgroup
 constexpr int kRows = 4;                   // rows per stage
 constexpr int kXPadBytes = 32;             // LDS pad after each row of X: rows start 8 banks apart
 constexpr int kZPitch = kD0 + 8;           // Z pitch per beta0 (floats): beta0 neighbours 8 banks apart
-constexpr int kZRow = kBT * kZPitch + 8;   // Z pitch per row (floats): rows 8 banks apart
-constexpr int kZFloats = kRows * kZRow;    // one Z buffer
 constexpr int kZBufs = 2;                  // Z double buffer: phase B of stage s - 1 runs beside phase A of stage s
-constexpr int kFusedConsumers = 4;         // consumer waves per workgroup
+constexpr int kFusedConsumers = 8;         // consumer waves per workgroup
 constexpr int kFusedThreads = kFusedConsumers * 64 + 64;   // + one loader wave
-constexpr int kSetsPerWave = kBT / kFusedConsumers;        // phase A: groups of 4 beta0 per wave
-// Phase B runs on the VALU (16-byte stores) for fp32 rows and on the matrix
-// cores (4-byte stores) for bf16 rows: the faster of the two for each, by
-// measurement on the GPT-2-medium shape.
-constexpr bool phase_b_mfma(int eb) { return eb == 2; }
-constexpr int kRowsPerPass = kFusedConsumers * 64 / (kBT * kB1 * 2);   // VALU phase B: rows per pass
-static_assert(kRowsPerPass >= 1 && kRows % kRowsPerPass == 0 && (kZPitch * 4) % 16 == 0 && (kZRow * 4) % 16 == 0,
-              "phase B covers whole rows per pass, Z in 16-byte runs");
-static_assert(kRows % 4 == 0 && kBT % kFusedConsumers == 0 && kFusedConsumers % 4 == 0 && kD0 == 64,
-              "phase A: 4x4 MFMA blocks of rows x beta0, 16 delta0 per block group");
-static_assert(kRows == 4 && kBT * kD1 == 16 * kFusedConsumers && kB1 == 8,
-              "MFMA phase B: 4x4 blocks of rows x beta1, 16 (alpha1, delta1) blocks per wave");
+
+// Geometry of a tile of BT beta0 (= alpha1) values.
+template <int BT>
+struct FusedTile {
+    static constexpr int kZRow = BT * kZPitch + 8;       // Z pitch per row (floats): rows 8 banks apart
+    static constexpr int kZFloats = kRows * kZRow;       // one Z buffer
+    static constexpr int kSetsPerWave = BT / kFusedConsumers;   // phase A: groups of 4 beta0 per wave
+    static constexpr int kRowsPerPass = kFusedConsumers * 64 / (BT * kB1 * 2);   // phase B: rows per pass
+    static_assert(BT == 8 || BT == 16 || BT == 32, "tile widths");
+    static_assert(kRowsPerPass >= 1 && kRows % kRowsPerPass == 0 && (kZPitch * 4) % 16 == 0 &&
+                      (kZRow * 4) % 16 == 0,
+                  "phase B covers whole rows per pass, Z in 16-byte runs");
+    // phase A: wave w takes delta0 in [16 (w % 4), +16) and the beta0 groups
+    // [(w / 4) * kSetsPerWave * 4, +kSetsPerWave * 4)
+    static_assert(kRows == 4 && kD0 == 64 && kFusedConsumers == 8 && (kFusedConsumers / 4) * kSetsPerWave * 4 == BT,
+                  "phase A: 4x4 MFMA blocks of rows x beta0, 16 delta0 per block group");
+};
 
 // Loader instructions (1 KB each) for one stage of rows of elem_bytes-wide
 // elements with kXPadBytes after each row.
@@ -81,15 +85,15 @@ constexpr int stage_bytes(int eb) { return stage_insts(eb) * 1024; }
 constexpr int kStagesF32 = 3;              // LDS ring depth for fp32 rows
 constexpr int kStagesBF16 = 4;             // ... and for bf16 rows (half the bytes)
 constexpr int stages_for(int eb) { return eb == 4 ? kStagesF32 : kStagesBF16; }
-constexpr size_t fused_lds_bytes(int eb) {
-    return size_t(stages_for(eb)) * stage_bytes(eb) + size_t(kZBufs) * kZFloats * sizeof(float);
+constexpr size_t fused_lds_bytes(int eb, int bt) {
+    return size_t(stages_for(eb)) * stage_bytes(eb) + size_t(kZBufs) * kRows * (bt * kZPitch + 8) * sizeof(float);
 }
 
 struct FusedArgs {
     int b0;                 // beta0 extent (= alpha1 extent)
     int64_t n_in, n_mid, n_out;
     int64_t batch;
-    int n_tiles;            // b0 / kBT
+    int n_tiles;            // b0 / BT
     int rows_per_split;     // multiple of kRows
     int xshift;             // elements from the 16-byte boundary below X to X (the same in every row)
 };
@@ -101,8 +105,8 @@ __device__ __forceinline__ uint32_t shifted_limit(uint32_t limit, int xshift) {
     return (xshift == 0 || limit > kNoVector - 16u) ? limit : limit + 16u;
 }
 
-// kYVec: Y is 16-byte aligned (vector stores in the fp32 phase B).
-template <typename TX, typename TW, bool kYVec>
+// kYVec: Y is 16-byte aligned (vector stores in phase B); BT: beta0 per tile.
+template <typename TX, typename TW, bool kYVec, int BT>
 __global__ __launch_bounds__(kFusedThreads) void fused_pair_kernel(const TX* __restrict__ X,
                                                                    const TW* __restrict__ K0,
                                                                    const TW* __restrict__ K1,
@@ -113,14 +117,19 @@ __global__ __launch_bounds__(kFusedThreads) void fused_pair_kernel(const TX* __r
     constexpr int kStageBytes = stage_bytes(EB);
     constexpr int kStages = stages_for(EB);
     constexpr int kRowBytes = kC0 * kD0 * EB + kXPadBytes;   // LDS pitch of a row of X
+    using Tile = FusedTile<BT>;
+    constexpr int kZRow = Tile::kZRow;
+    constexpr int kZFloats = Tile::kZFloats;
+    constexpr int kSetsPerWave = Tile::kSetsPerWave;
+    constexpr int kRowsPerPass = Tile::kRowsPerPass;
     extern __shared__ __align__(16) unsigned char lds[];
-    float* const zs = reinterpret_cast<float*>(lds + kStages * kStageBytes);   // kZBufs x [kRows][kBT][kZPitch]
+    float* const zs = reinterpret_cast<float*>(lds + kStages * kStageBytes);   // kZBufs x [kRows][BT][kZPitch]
 
     const int t = threadIdx.x;
     const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
     const int tile = blk % args.n_tiles;
     const int split = blk / args.n_tiles;
-    const int beta0 = tile * kBT;                          // first beta0 (= alpha1) of the tile
+    const int beta0 = tile * BT;                           // first beta0 (= alpha1) of the tile
 
     const int64_t row_begin = int64_t(split) * args.rows_per_split;
     if (row_begin >= args.batch) return;
@@ -158,7 +167,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_pair_kernel(const TX* __r
     }
 
     // ---------------------------------------------------------- consumers
-    // Both phases are batched 4x4 outer products on the matrix cores: in
+    // Phase A is a batched 4x4 outer product on the matrix cores: in
     // v_mfma_f32_4x4x1f32 lane l belongs to block l / 4, supplies row l % 4
     // of that block's A column and column l % 4 of its B row, and receives
     // D[i][l % 4] of its block in accumulator register i. One instruction
@@ -213,107 +222,68 @@ __global__ __launch_bounds__(kFusedThreads) void fused_pair_kernel(const TX* __r
         }
     };
 
-    if constexpr (phase_b_mfma(EB)) {
-        // (B) block = (alpha1, delta1), A = Z[row][alpha1][gamma1 * 8 + delta1],
-        // B = K1[alpha1][delta1][beta1][gamma1]; wave w -> alpha1 in
-        // {2w, 2w + 1} (within the tile), all 8 delta1 and both groups of 4
-        // beta1. A wave's store of one accumulator register covers, for one
-        // row, Y[alpha1][beta1 of the group][all delta1]: two runs of 128 bytes.
-        const int b_e1 = (lane >> 2) & (kD1 - 1);
-        const int b_a1 = 2 * wave + (lane >> 5);
-        float k1m[2][kC1];
+    // (B) thread -> one row of a pass, (alpha1, beta1) and a run of 4 delta1:
+    // lanes in (alpha1, beta1, run) order store 16-byte vectors that tile
+    // the row's slab of Y contiguously
+    const int rsub = t / (BT * kB1 * 2);               // row within a pass
+    const int run = t & 1;
+    const int b1 = (t >> 1) & (kB1 - 1);
+    const int a1 = (t >> 4) & (BT - 1);                // alpha1 within the tile
+    const int e10 = run * 4;                           // first delta1 of the run
+    float k1r[4][kC1];
 #pragma unroll
-        for (int grp = 0; grp < 2; ++grp) {
-            const TW* kp = K1 + ((int64_t(beta0 + b_a1) * kD1 + b_e1) * kB1 + 4 * grp + q) * kC1;   // K1[a][e][b][:]
+    for (int k = 0; k < 4; ++k) {
+        const TW* kp = K1 + ((int64_t(beta0 + a1) * kD1 + e10 + k) * kB1 + b1) * kC1;   // K1[a][e][b][:]
 #pragma unroll
-            for (int g = 0; g < kC1; ++g) k1m[grp][g] = to_f32(kp[g]);
-        }
-        const int64_t yoff = int64_t(beta0 + b_a1) * (kB1 * kD1) + q * kD1 + b_e1;
-        auto phase_b = [&](int s, const float* zb) {
-            const int64_t n0 = row_begin + int64_t(s) * kRows;
-            const int rows = static_cast<int>(min(int64_t(kRows), row_end - n0));
-            const float* za = zb + q * kZRow + b_a1 * kZPitch + b_e1;
-            floatx4 y[2] = {floatx4{0.0f, 0.0f, 0.0f, 0.0f}, floatx4{0.0f, 0.0f, 0.0f, 0.0f}};
+        for (int g = 0; g < kC1; ++g) k1r[k][g] = to_f32(kp[g]);
+    }
+    const int64_t yoff = int64_t(beta0 + a1) * (kB1 * kD1) + b1 * kD1 + e10;
+    auto phase_b = [&](int s, const float* zb) {
+        const int64_t n0 = row_begin + int64_t(s) * kRows;
+        const int rows = static_cast<int>(min(int64_t(kRows), row_end - n0));
+#pragma unroll
+        for (int r0 = 0; r0 < kRows; r0 += kRowsPerPass) {
+            const int r = r0 + rsub;
+            const float* zr = zb + r * kZRow + a1 * kZPitch + e10;
+            floatx4 y = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int g = 0; g < kC1; ++g) {
-                const float z = za[g * kD1];
-                y[0] = __builtin_amdgcn_mfma_f32_4x4x1f32(z, k1m[0][g], y[0], 0, 0, 0);
-                y[1] = __builtin_amdgcn_mfma_f32_4x4x1f32(z, k1m[1][g], y[1], 0, 0, 0);
-            }
-            float* yr = Y + n0 * args.n_out + yoff;
+                const floatx4 z = *reinterpret_cast<const floatx4*>(zr + g * kD1);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (i < rows) {
-                    __builtin_nontemporal_store(y[0][i], yr + i * args.n_out);
-                    __builtin_nontemporal_store(y[1][i], yr + i * args.n_out + 4 * kD1);
+                for (int k = 0; k < 4; ++k) y[k] = fmaf(k1r[k][g], z[k], y[k]);
+            }
+            if (r < rows) {
+                float* yr = Y + (n0 + r) * args.n_out + yoff;
+                if constexpr (kYVec) {
+                    __builtin_nontemporal_store(y, reinterpret_cast<floatx4*>(yr));
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) __builtin_nontemporal_store(y[k], yr + k);
                 }
             }
-        };
-        pipeline(phase_b);
-    } else {
-        // (B) thread -> one row of a pass, (alpha1, beta1) and a run of 4 delta1:
-        // lanes in (alpha1, beta1, run) order store 16-byte vectors that tile
-        // the row's slab of Y contiguously
-        const int rsub = t / (kBT * kB1 * 2);              // row within a pass
-        const int run = t & 1;
-        const int b1 = (t >> 1) & (kB1 - 1);
-        const int a1 = (t >> 4) & (kBT - 1);               // alpha1 within the tile
-        const int e10 = run * 4;                           // first delta1 of the run
-        float k1r[4][kC1];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const TW* kp = K1 + ((int64_t(beta0 + a1) * kD1 + e10 + k) * kB1 + b1) * kC1;   // K1[a][e][b][:]
-#pragma unroll
-            for (int g = 0; g < kC1; ++g) k1r[k][g] = to_f32(kp[g]);
         }
-        const int64_t yoff = int64_t(beta0 + a1) * (kB1 * kD1) + b1 * kD1 + e10;
-        auto phase_b = [&](int s, const float* zb) {
-            const int64_t n0 = row_begin + int64_t(s) * kRows;
-            const int rows = static_cast<int>(min(int64_t(kRows), row_end - n0));
-#pragma unroll
-            for (int r0 = 0; r0 < kRows; r0 += kRowsPerPass) {
-                const int r = r0 + rsub;
-                const float* zr = zb + r * kZRow + a1 * kZPitch + e10;
-                floatx4 y = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                for (int g = 0; g < kC1; ++g) {
-                    const floatx4 z = *reinterpret_cast<const floatx4*>(zr + g * kD1);
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) y[k] = fmaf(k1r[k][g], z[k], y[k]);
-                }
-                if (r < rows) {
-                    float* yr = Y + (n0 + r) * args.n_out + yoff;
-                    if constexpr (kYVec) {
-                        __builtin_nontemporal_store(y, reinterpret_cast<floatx4*>(yr));
-                    } else {
-#pragma unroll
-                        for (int k = 0; k < 4; ++k) __builtin_nontemporal_store(y[k], yr + k);
-                    }
-                }
-            }
-        };
-        pipeline(phase_b);
-    }
+    };
+    pipeline(phase_b);
 }
 
 bool shape_ok(const Shape& s0, const Shape& s1) {
-    return s0.a == 1 && s0.c == kC0 && s0.d == kD0 && s0.b % kBT == 0 && s1.a == s0.b && s1.b == kB1 &&
+    return s0.a == 1 && s0.c == kC0 && s0.d == kD0 && s0.b % 8 == 0 && s1.a == s0.b && s1.b == kB1 &&
            s1.c == kC1 && s1.d == kD1;
 }
 
-template <typename TX, typename TW>
-ks_status_t launch_typed(const Shape& s0, const Shape& s1, const void* W0, const void* W1, const void* X,
-                         float* Y, int64_t batch, hipStream_t stream, int num_cus) {
+template <typename TX, typename TW, int BT>
+ks_status_t launch_tile(const Shape& s0, const Shape& s1, const void* W0, const void* W1, const void* X,
+                        float* Y, int64_t batch, hipStream_t stream, int num_cus) {
     FusedArgs args;
     args.b0 = s0.b;
     args.n_in = s0.n_in;
     args.n_mid = s0.n_out;
     args.n_out = s1.n_out;
     args.batch = batch;
-    args.n_tiles = s0.b / kBT;
+    args.n_tiles = s0.b / BT;
     args.xshift = static_cast<int>((reinterpret_cast<uintptr_t>(X) & 15u) / sizeof(TX));
     // about one resident wave of workgroups (as many per compute unit as fit its 160 KB of LDS)
-    const size_t lds = fused_lds_bytes(int(sizeof(TX)));
+    const size_t lds = fused_lds_bytes(int(sizeof(TX)), BT);
     const int per_cu = std::max(1, std::min(4, int((160 * 1024) / lds)));
     const int64_t steps_total = (batch + kRows - 1) / kRows;
     const int64_t splits = std::max<int64_t>(1, int64_t(std::max(num_cus, 1)) * per_cu / args.n_tiles);
@@ -323,9 +293,20 @@ ks_status_t launch_typed(const Shape& s0, const Shape& s1, const void* W0, const
     const int64_t blocks = nsplit * args.n_tiles;
     if (blocks > 0x7fffffff) return KS_ERR_UNSUPPORTED;
     const bool y_vec = (reinterpret_cast<uintptr_t>(Y) & 15u) == 0;
-    auto kernel = y_vec ? fused_pair_kernel<TX, TW, true> : fused_pair_kernel<TX, TW, false>;
+    auto kernel = y_vec ? fused_pair_kernel<TX, TW, true, BT> : fused_pair_kernel<TX, TW, false, BT>;
     return launch_kernel(kernel, dim3(static_cast<unsigned>(blocks)), dim3(kFusedThreads), lds, stream,
                          static_cast<const TX*>(X), static_cast<const TW*>(W0), static_cast<const TW*>(W1), Y, args);
+}
+
+// The widest tile that divides b0: 32 beta0 per workgroup on GPT-2-medium's
+// b0 = 64 (fp32 64 vs 72 us, bf16 61 vs 68 us against 8 beta0 and four
+// compute waves, measured A/B in one process).
+template <typename TX, typename TW>
+ks_status_t launch_typed(const Shape& s0, const Shape& s1, const void* W0, const void* W1, const void* X,
+                         float* Y, int64_t batch, hipStream_t stream, int num_cus) {
+    if (s0.b % 32 == 0) return launch_tile<TX, TW, 32>(s0, s1, W0, W1, X, Y, batch, stream, num_cus);
+    if (s0.b % 16 == 0) return launch_tile<TX, TW, 16>(s0, s1, W0, W1, X, Y, batch, stream, num_cus);
+    return launch_tile<TX, TW, 8>(s0, s1, W0, W1, X, Y, batch, stream, num_cus);
 }
 
 }  // namespace

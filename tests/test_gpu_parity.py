@@ -322,11 +322,11 @@ def test_gpt2_chain_full_size(fuse):
 
 @pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("lead", [False, True])
-@pytest.mark.parametrize("b0", [8, 64, 128])
+@pytest.mark.parametrize("b0", [8, 24, 48, 64, 128])
 def test_fused_pair_shapes(b0, lead, bf16):
-    """The one-launch pair (1, b0, 16, 64) -> (b0, 8, 8, 8) for several b0,
-    with a ragged row count; behind a leading factor in a bf16 chain the
-    pair reads fp32 rows with bf16 weights."""
+    """The one-launch pair (1, b0, 16, 64) -> (b0, 8, 8, 8) for several b0
+    (tiles of 8, 16 and 32 beta0), with a ragged row count; behind a leading
+    factor in a bf16 chain the pair reads fp32 rows with bf16 weights."""
     pats = [(1, b0, 16, 64), (b0, 8, 8, 8)]
     sig = [0.25, 1.0 / np.sqrt(8.0)]
     if lead:
