@@ -21,6 +21,22 @@
 // weights (at most 64 KB here) are read once per workgroup, from the L2
 // cache after the first. fp32 accumulation; intermediates are fp32 (bf16 X
 // and weights are widened exactly).
+//
+// Rows wider than the LDS allows are cut by the closure of the run. Factor
+// (a, b, c, d) maps the slab alpha of a row (c*d inputs) to the slab alpha of
+// the output (b*d values), and never changes an index modulo d. If P divides
+// every a of the run and Q every d, the run therefore acts on each of P
+// contiguous slabs of the row, and within a slab on each of Q classes of
+// indices that are equal modulo Q, independently: on slab p, class q the
+// factor is the KS factor (a/P, b, c, d/Q) with the blocks
+// K[p*(a/P) + alpha'][delta'*Q + q]. A workgroup takes one slab and T
+// consecutive classes (T divides Q) and keeps them with class fastest:
+// tile element e*T + t is slab element e*Q + q0 + t, so on the tile each
+// factor is again a KS factor, (a/P, b, c, (d/Q)*T), whose block
+// (alpha', delta'') is K[p*(a/P) + alpha'][(delta''/T)*Q + q0 + delta''%T].
+// X and Y move in runs of T elements. When whole slabs fit, a tile is the
+// fewest consecutive slabs that do (P taken as a smaller divisor, Q = T = 1):
+// one contiguous run, on which each factor is (a/P, b, c, d).
 
 #include <algorithm>
 #include <cstdio>
@@ -37,19 +53,48 @@ constexpr int kThreads = 256;
 constexpr int kMaxFactors = 16;              // factors per launch
 constexpr int kMaxWidth = 4096;              // widest row of the run (elements)
 constexpr int kLdsTarget = 32 * 1024;        // LDS of the two row buffers (rows of 4096: 2 rows)
+constexpr int kTiledLdsTarget = 64 * 1024;   // the same for tiles of rows too wide for LDS
+constexpr int kMaxRows = 32;                 // rows per workgroup of a tiled run (16 for whole rows)
+constexpr int64_t kSlabTarget = 256;         // slabs merged into tiles of at most this many values
+constexpr int64_t kClassWidth = 1024;        // widest tile made of index classes (16 rows in 64 KB)
 constexpr int64_t kMaxWeightBytes = 64 * 1024;
 constexpr int kMaxBlock = 16;                // b * c held in registers
 
+constexpr int kMinRun = 16;                  // elements per run of X / Y when tiles are class groups
+
 struct RowChainArgs {
     int nf;                  // factors in the run
-    int pitch;               // LDS floats per row (widest row, multiple of 4)
+    int pitch;               // LDS floats per row (widest tile row, multiple of 4)
     int rows;                // rows per workgroup
     int n_in, n_out;         // row widths of X and Y
     int64_t batch;
-    int vec_x, vec_y;        // 1: rows of X / Y move as 4-element vectors
+    int vec_x, vec_y;        // 1: tile rows of X / Y move as 4-element vectors
+    int inplace;             // 1: every factor square on the register path, one LDS buffer
+    int P, Q, T;             // slabs, classes per slab, classes per tile (T divides Q)
+    int ntiles;              // P * (Q / T) tiles per row
+    int tin, tout;           // tile widths of X and Y: (n_in / (P Q)) T, (n_out / (P Q)) T
     int pat[kMaxFactors][4]; // (a, b, c, d) of each factor
+    int sub[kMaxFactors][2]; // (a / P, (d / Q) T): the factor on a tile
     const void* w[kMaxFactors];
 };
+
+// Where a tile's factor finds its blocks: tile group (alpha', delta'') is
+// block (abase + alpha') * d + (delta'' / T) * Q + q0 + delta'' % T.
+struct BlockMap {
+    int abase, d, Q, T, q0;
+    __device__ __forceinline__ int64_t block(int alpha, int dext) const {
+        const int dq = dext / T;
+        return int64_t(abase + alpha) * d + dq * Q + q0 + (dext - dq * T);
+    }
+};
+
+// Offset within a row of the tile element l (slab p, classes q0 ..): the
+// slab's element (l / T) * Q + q0 + l % T; the slab itself when T = Q = 1.
+__device__ __forceinline__ int tile_offset(int l, int slab0, int Q, int T, int q0) {
+    if (T == Q) return slab0 + l;
+    const int e = l / T;
+    return slab0 + e * Q + q0 + (l - e * T);
+}
 
 // Threads of one factor: with at least kThreads groups a thread takes
 // groups t, t + kThreads, ... over all rows; with fewer, the rows of a group
@@ -75,30 +120,49 @@ __device__ __forceinline__ bool item_map(int groups, ItemMap* m) {
 // once, B outputs written).
 template <int B, int C, typename TW>
 __device__ __forceinline__ void apply_block(const float* src, float* dst, int pitch, int nr, int a, int d,
-                                            const TW* __restrict__ K) {
+                                            const TW* __restrict__ K, const BlockMap& bm) {
+    // the blocks of NB groups are loaded together (one wait on the cache for
+    // NB groups, not one per group), at most 16 weights and 8 groups a thread
+    constexpr int NB = B * C >= 16 ? 1 : (16 / (B * C) > 8 ? 8 : 16 / (B * C));
     ItemMap m;
     if (!item_map(a * d, &m)) return;
-    for (int g = m.g0; g < a * d; g += m.gstep) {
-        const int alpha = g / d;
-        const int delta = g - alpha * d;
-        const TW* kp = K + int64_t(g) * (B * C);   // (alpha * d + delta) * b * c
-        float w[B][C];
+    const int groups = a * d;
+    for (int g0 = m.g0; g0 < groups; g0 += NB * m.gstep) {
+        float w[NB][B][C];
 #pragma unroll
-        for (int be = 0; be < B; ++be)
+        for (int j = 0; j < NB; ++j) {
+            const int g = g0 + j * m.gstep;
+            if (g < groups) {
+                const int alpha = g / d;
+                const TW* kp = K + bm.block(alpha, g - alpha * d) * (B * C);
 #pragma unroll
-            for (int gm = 0; gm < C; ++gm) w[be][gm] = to_f32(kp[be * C + gm]);
-        const float* s = src + alpha * C * d + delta;
-        float* o = dst + alpha * B * d + delta;
-        for (int r = m.r0; r < nr; r += m.rstep) {
-            float x[C];
+                for (int be = 0; be < B; ++be)
 #pragma unroll
-            for (int gm = 0; gm < C; ++gm) x[gm] = s[r * pitch + gm * d];
+                    for (int gm = 0; gm < C; ++gm) w[j][be][gm] = to_f32(kp[be * C + gm]);
+            }
+        }
 #pragma unroll
-            for (int be = 0; be < B; ++be) {
-                float acc = 0.0f;
+        for (int j = 0; j < NB; ++j) {
+            const int g = g0 + j * m.gstep;
+            if (g >= groups) break;
+            const int alpha = g / d;
+            const int delta = g - alpha * d;
+            // with B == C the outputs land on the inputs' own places: each
+            // thread reads all C inputs of a row before it writes, so src may
+            // be dst
+            const float* s = src + alpha * C * d + delta;
+            float* o = dst + alpha * B * d + delta;
+            for (int r = m.r0; r < nr; r += m.rstep) {
+                float x[C];
 #pragma unroll
-                for (int gm = 0; gm < C; ++gm) acc = fmaf(w[be][gm], x[gm], acc);
-                o[r * pitch + be * d] = acc;
+                for (int gm = 0; gm < C; ++gm) x[gm] = s[r * pitch + gm * d];
+#pragma unroll
+                for (int be = 0; be < B; ++be) {
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int gm = 0; gm < C; ++gm) acc = fmaf(w[j][be][gm], x[gm], acc);
+                    o[r * pitch + be * d] = acc;
+                }
             }
         }
     }
@@ -107,13 +171,13 @@ __device__ __forceinline__ void apply_block(const float* src, float* dst, int pi
 // Any b, c (up to 16): weights read from global memory (cached) per row.
 template <typename TW>
 __device__ __forceinline__ void apply_any(const float* src, float* dst, int pitch, int nr, int a, int b, int c,
-                                          int d, const TW* __restrict__ K) {
+                                          int d, const TW* __restrict__ K, const BlockMap& bm) {
     ItemMap m;
     if (!item_map(a * d, &m)) return;
     for (int g = m.g0; g < a * d; g += m.gstep) {
         const int alpha = g / d;
         const int delta = g - alpha * d;
-        const TW* kp = K + int64_t(g) * b * c;
+        const TW* kp = K + bm.block(alpha, delta) * b * c;
         const float* s = src + alpha * c * d + delta;
         float* o = dst + alpha * b * d + delta;
         for (int r = m.r0; r < nr; r += m.rstep) {
@@ -131,9 +195,9 @@ __device__ __forceinline__ void apply_any(const float* src, float* dst, int pitc
 // waves per SIMD).
 template <int MAXBC, int B, int C, typename TW>
 __device__ __forceinline__ bool try_block(const float* src, float* dst, int pitch, int nr, int a, int d,
-                                          const TW* __restrict__ K) {
+                                          const TW* __restrict__ K, const BlockMap& bm) {
     if constexpr (B * C <= MAXBC) {
-        apply_block<B, C>(src, dst, pitch, nr, a, d, K);
+        apply_block<B, C>(src, dst, pitch, nr, a, d, K, bm);
         return true;
     } else {
         return false;
@@ -142,29 +206,31 @@ __device__ __forceinline__ bool try_block(const float* src, float* dst, int pitc
 
 template <int MAXBC, int B, typename TW>
 __device__ __forceinline__ void apply_b(const float* src, float* dst, int pitch, int nr, int a, int c, int d,
-                                        const TW* __restrict__ K) {
+                                        const TW* __restrict__ K, const BlockMap& bm) {
     bool done = false;
     switch (c) {
-        case 1: done = try_block<MAXBC, B, 1>(src, dst, pitch, nr, a, d, K); break;
-        case 2: done = try_block<MAXBC, B, 2>(src, dst, pitch, nr, a, d, K); break;
-        case 4: done = try_block<MAXBC, B, 4>(src, dst, pitch, nr, a, d, K); break;
-        case 8: done = try_block<MAXBC, B, 8>(src, dst, pitch, nr, a, d, K); break;
-        case 16: done = try_block<MAXBC, B, 16>(src, dst, pitch, nr, a, d, K); break;
+        case 1: done = try_block<MAXBC, B, 1>(src, dst, pitch, nr, a, d, K, bm); break;
+        case 2: done = try_block<MAXBC, B, 2>(src, dst, pitch, nr, a, d, K, bm); break;
+        case 4: done = try_block<MAXBC, B, 4>(src, dst, pitch, nr, a, d, K, bm); break;
+        case 8: done = try_block<MAXBC, B, 8>(src, dst, pitch, nr, a, d, K, bm); break;
+        case 16: done = try_block<MAXBC, B, 16>(src, dst, pitch, nr, a, d, K, bm); break;
     }
-    if (!done) apply_any(src, dst, pitch, nr, a, B, c, d, K);
+    if (!done) apply_any(src, dst, pitch, nr, a, B, c, d, K, bm);
 }
 
+// One factor on the tile: a and d are the tile's (a / P, (d / Q) T); bm
+// finds the blocks.
 template <int MAXBC, typename TW>
 __device__ __forceinline__ void apply_factor(const float* src, float* dst, int pitch, int nr, int a, int b, int c,
-                                             int d, const TW* __restrict__ K) {
+                                             int d, const TW* __restrict__ K, const BlockMap& bm) {
     switch (b) {
-        case 1: apply_b<MAXBC, 1>(src, dst, pitch, nr, a, c, d, K); return;
-        case 2: apply_b<MAXBC, 2>(src, dst, pitch, nr, a, c, d, K); return;
-        case 4: apply_b<MAXBC, 4>(src, dst, pitch, nr, a, c, d, K); return;
-        case 8: apply_b<MAXBC, 8>(src, dst, pitch, nr, a, c, d, K); return;
-        case 16: apply_b<MAXBC, 16>(src, dst, pitch, nr, a, c, d, K); return;
+        case 1: apply_b<MAXBC, 1>(src, dst, pitch, nr, a, c, d, K, bm); return;
+        case 2: apply_b<MAXBC, 2>(src, dst, pitch, nr, a, c, d, K, bm); return;
+        case 4: apply_b<MAXBC, 4>(src, dst, pitch, nr, a, c, d, K, bm); return;
+        case 8: apply_b<MAXBC, 8>(src, dst, pitch, nr, a, c, d, K, bm); return;
+        case 16: apply_b<MAXBC, 16>(src, dst, pitch, nr, a, c, d, K, bm); return;
     }
-    apply_any(src, dst, pitch, nr, a, b, c, d, K);
+    apply_any(src, dst, pitch, nr, a, b, c, d, K, bm);
 }
 
 template <typename TX, typename TW, int MAXBC>
@@ -174,82 +240,159 @@ __global__ __launch_bounds__(kThreads) void row_chain_kernel(const TX* __restric
     const int pitch = args.pitch;
     // buffers as offsets from the LDS array itself (a pointer picked from an
     // array of pointers would lose its address space: generic accesses)
-    const int bufsz = args.rows * pitch;
-    const int64_t n0 = int64_t(blockIdx.x) * args.rows;
+    const int bufsz = args.inplace ? 0 : args.rows * pitch;
+    // workgroup: row block, then tile (slab p, classes q0 .. q0 + T - 1)
+    const int tile = static_cast<int>(blockIdx.x % static_cast<unsigned>(args.ntiles));
+    const int64_t n0 = int64_t(blockIdx.x / static_cast<unsigned>(args.ntiles)) * args.rows;
+    const int groups_per_slab = args.Q / args.T;
+    const int p = tile / groups_per_slab;
+    const int q0 = (tile - p * groups_per_slab) * args.T;
     const int nr = static_cast<int>(min(int64_t(args.rows), args.batch - n0));
     const int t = threadIdx.x;
 
-    // X rows into buffer 0 (bf16 widened exactly)
+    // X tile rows into buffer 0 (bf16 widened exactly)
     const TX* xs = X + n0 * args.n_in;
+    const int slab_in = p * (args.n_in / args.P);
     if (args.vec_x) {
-        const int q = args.n_in / 4;
+        const int q = args.tin / 4;
         for (int i = t; i < nr * q; i += kThreads) {
             const int r = i / q, j = i - r * q;
             float v[4];
-            load4_f32(xs + int64_t(r) * args.n_in + 4 * j, v);
+            load4_f32(xs + int64_t(r) * args.n_in + tile_offset(4 * j, slab_in, args.Q, args.T, q0), v);
             *reinterpret_cast<floatx4_t*>(zbuf + r * pitch + 4 * j) = floatx4_t{v[0], v[1], v[2], v[3]};
         }
     } else {
-        for (int i = t; i < nr * args.n_in; i += kThreads) {
-            const int r = i / args.n_in, j = i - r * args.n_in;
-            zbuf[r * pitch + j] = to_f32(xs[int64_t(r) * args.n_in + j]);
+        for (int i = t; i < nr * args.tin; i += kThreads) {
+            const int r = i / args.tin, j = i - r * args.tin;
+            zbuf[r * pitch + j] = to_f32(xs[int64_t(r) * args.n_in + tile_offset(j, slab_in, args.Q, args.T, q0)]);
         }
     }
     __syncthreads();
 
     for (int f = 0; f < args.nf; ++f) {
-        const int a = args.pat[f][0], b = args.pat[f][1], c = args.pat[f][2], d = args.pat[f][3];
+        const int b = args.pat[f][1], c = args.pat[f][2];
+        const int a = args.sub[f][0], d = args.sub[f][1];
+        const BlockMap bm{p * a, args.pat[f][3], args.Q, args.T, q0};
         const TW* K = static_cast<const TW*>(args.w[f]);
         const float* src = zbuf + (f & 1) * bufsz;
         float* dst = zbuf + ((f + 1) & 1) * bufsz;
-        apply_factor<MAXBC>(src, dst, pitch, nr, a, b, c, d, K);
+        apply_factor<MAXBC>(src, dst, pitch, nr, a, b, c, d, K, bm);
         __syncthreads();
     }
 
     // the last buffer to Y
     const float* z = zbuf + (args.nf & 1) * bufsz;
     float* ys = Y + n0 * args.n_out;
+    const int slab_out = p * (args.n_out / args.P);
     if (args.vec_y) {
-        const int q = args.n_out / 4;
+        const int q = args.tout / 4;
         for (int i = t; i < nr * q; i += kThreads) {
             const int r = i / q, j = i - r * q;
             const floatx4_t v = *reinterpret_cast<const floatx4_t*>(z + r * pitch + 4 * j);
-            __builtin_nontemporal_store(v, reinterpret_cast<floatx4_t*>(ys + int64_t(r) * args.n_out + 4 * j));
+            __builtin_nontemporal_store(
+                v, reinterpret_cast<floatx4_t*>(ys + int64_t(r) * args.n_out +
+                                                tile_offset(4 * j, slab_out, args.Q, args.T, q0)));
         }
     } else {
-        for (int i = t; i < nr * args.n_out; i += kThreads) {
-            const int r = i / args.n_out, j = i - r * args.n_out;
-            ys[int64_t(r) * args.n_out + j] = z[r * pitch + j];
+        for (int i = t; i < nr * args.tout; i += kThreads) {
+            const int r = i / args.tout, j = i - r * args.tout;
+            ys[int64_t(r) * args.n_out + tile_offset(j, slab_out, args.Q, args.T, q0)] = z[r * pitch + j];
         }
     }
 }
 
-// Rows per workgroup: two row buffers in kLdsTarget bytes (at least two rows,
-// so that each weight block loaded serves more than one row).
-int chain_rows(int pitch) {
-    return std::max(2, std::min(16, kLdsTarget / (2 * 4 * pitch)));
+// Rows per workgroup: the row buffers (one when factors run in place, else
+// two) in kLdsTarget bytes, kTiledLdsTarget for tiles of rows too wide for LDS (a
+// tile's weights are read once per workgroup: more rows share them); at
+// least two rows, so that each weight block loaded serves more than one row.
+int chain_rows(int pitch, int nbuf, bool tiled) {
+    const int target = tiled ? kTiledLdsTarget : kLdsTarget;
+    return std::max(2, std::min(tiled ? kMaxRows : 16, target / (nbuf * 4 * pitch)));
 }
 
-int row_pitch(const Shape* s, int n) {
-    int64_t w = s[0].n_in;
-    for (int k = 0; k < n; ++k) w = std::max<int64_t>(w, s[k].n_out);
-    return static_cast<int>((w + 3) / 4 * 4);
+// Factors that can run in place: square blocks on the register path.
+bool runs_in_place(const Shape* s, int n) {
+    for (int k = 0; k < n; ++k)
+        if (s[k].b != s[k].c || s[k].b * s[k].c > kMaxBlock || (s[k].b != 1 && s[k].b != 2 && s[k].b != 4))
+            return false;
+    return true;
 }
+
+int64_t gcd64(int64_t x, int64_t y) {
+    while (y != 0) {
+        const int64_t r = x % y;
+        x = y;
+        y = r;
+    }
+    return x;
+}
+
+// The tile a workgroup keeps in LDS: whole rows when the widest row of the
+// run fits; else, with P = gcd of the a's, if one slab fits: consecutive
+// slabs, as many as stay within kSlabTarget values (one when a slab is
+// wider), a run of contiguous values; else one of the P slabs and T of its Q
+// classes (Q = gcd of the d's), the most classes within kClassWidth values
+// and at least kMinRun of them, so that X and Y move in runs of 64 bytes.
+// Narrow tiles leave room for more rows, and every row a workgroup holds
+// shares the weights it reads (measured on 65,536-, 16,384- and 8,192-point
+// radix-2 and radix-4 butterflies: tiles of 256-value slabs and of 1024
+// class values with up to 32 rows beat 4096-value tiles of 4 rows by up to
+// 1.6 times).
+struct RunTile {
+    int P, Q, T;
+    int64_t width;           // floats of the widest tile row
+};
+
+bool run_tile(const Shape* s, int n, RunTile* rt) {
+    int64_t w = s[0].n_in, P = 0, Q = 0;
+    for (int k = 0; k < n; ++k) {
+        w = std::max<int64_t>(w, s[k].n_out);
+        P = gcd64(P, s[k].a);
+        Q = gcd64(Q, s[k].d);
+    }
+    if (w <= kMaxWidth) {
+        *rt = RunTile{1, 1, 1, w};
+        return true;
+    }
+    if (w / P <= kMaxWidth) {
+        int64_t slabs = P;
+        for (int64_t f = 1; f <= P; ++f)
+            if (P % f == 0 && w / f <= kSlabTarget) {
+                slabs = f;
+                break;
+            }
+        *rt = RunTile{static_cast<int>(slabs), 1, 1, w / slabs};
+        return true;
+    }
+    const int64_t sub = w / (P * Q);
+    int64_t T = 0;
+    for (int64_t t = kClassWidth / sub; t >= kMinRun; --t)
+        if (Q % t == 0) {
+            T = t;
+            break;
+        }
+    if (T == 0) return false;
+    *rt = RunTile{static_cast<int>(P), static_cast<int>(Q), static_cast<int>(T), sub * T};
+    return true;
+}
+
+int row_pitch(const RunTile& rt) { return static_cast<int>((rt.width + 3) / 4 * 4); }
 
 }  // namespace
 
 bool row_chain_supports(const Shape* s, int n, int xt, int wt) {
     (void)xt;
     if (n < 2 || n > kMaxFactors) return false;
-    int64_t w = s[0].n_in;
+    RunTile rt;
+    if (!run_tile(s, n, &rt)) return false;
     for (int k = 0; k < n; ++k) {
         // small blocks only: with b * c = 64 the run measured no faster than one
         // launch per factor, with 128 2.4 times slower (VALU work and VGPRs)
         if (s[k].b * s[k].c > kMaxBlock) return false;
-        if (s[k].nnz * elem_bytes(wt) > kMaxWeightBytes) return false;
-        w = std::max<int64_t>(w, s[k].n_out);
+        // the blocks one workgroup reads for its tile
+        if (s[k].nnz / (int64_t(rt.P) * rt.Q) * rt.T * elem_bytes(wt) > kMaxWeightBytes) return false;
     }
-    return w <= kMaxWidth;
+    return true;
 }
 
 template <typename TX, typename TW>
@@ -263,32 +406,52 @@ ks_status_t launch_rc(int maxbc, dim3 grid, size_t lds, hipStream_t stream, cons
 ks_status_t launch_row_chain(const Shape* s, int n, int xt, int wt, const void* const* W, const void* X, float* Y,
                              int64_t batch, hipStream_t stream, int num_cus) {
     if (!row_chain_supports(s, n, xt, wt)) return KS_ERR_UNSUPPORTED;
-    if (resident_chain_supports(s, n, xt, wt) && resident_chain_aligned(X, Y))
+    RunTile rt;
+    run_tile(s, n, &rt);
+    const bool whole_rows = rt.P == 1 && rt.Q == 1;
+    if (whole_rows && resident_chain_supports(s, n, xt, wt) && resident_chain_aligned(X, Y))
         return launch_resident_chain(s, n, xt, wt, W, X, Y, batch, stream, num_cus);
-    if (digit_chain_supports(s, n, xt, wt)) return launch_digit_chain(s, n, xt, wt, W, X, Y, batch, stream);
+    if (whole_rows && digit_chain_supports(s, n, xt, wt))
+        return launch_digit_chain(s, n, xt, wt, W, X, Y, batch, stream);
     RowChainArgs args{};
     args.nf = n;
-    args.pitch = row_pitch(s, n);
-    args.rows = chain_rows(args.pitch);
+    args.pitch = row_pitch(rt);
+    args.inplace = runs_in_place(s, n) ? 1 : 0;
+    const int nbuf = args.inplace ? 1 : 2;
+    args.rows = chain_rows(args.pitch, nbuf, !whole_rows);
     args.n_in = static_cast<int>(s[0].n_in);
     args.n_out = static_cast<int>(s[n - 1].n_out);
     args.batch = batch;
+    args.P = rt.P;
+    args.Q = rt.Q;
+    args.T = rt.T;
+    args.ntiles = rt.P * (rt.Q / rt.T);
+    const int pq = rt.P * rt.Q;
+    args.tin = args.n_in / pq * rt.T;
+    args.tout = args.n_out / pq * rt.T;
+    // 4-element vectors: every tile row starts on a multiple of 4 elements and
+    // its runs are whole vectors (one run, the slab, when Q = 1; else runs of T)
     const uintptr_t xa = reinterpret_cast<uintptr_t>(X), ya = reinterpret_cast<uintptr_t>(Y);
     const int xvec_align = xt == kBF16 ? 8 : 16;
-    args.vec_x = (args.n_in % 4 == 0 && xa % xvec_align == 0) ? 1 : 0;
-    args.vec_y = (args.n_out % 4 == 0 && ya % 16 == 0) ? 1 : 0;
+    const bool runs4 = rt.T == rt.Q || rt.T % 4 == 0;
+    args.vec_x = (runs4 && args.n_in % 4 == 0 && (args.n_in / rt.P) % 4 == 0 && args.tin % 4 == 0 &&
+                  xa % xvec_align == 0) ? 1 : 0;
+    args.vec_y = (runs4 && args.n_out % 4 == 0 && (args.n_out / rt.P) % 4 == 0 && args.tout % 4 == 0 &&
+                  ya % 16 == 0) ? 1 : 0;
     int maxbc = 1;
     for (int k = 0; k < n; ++k) {
         args.pat[k][0] = s[k].a;
         args.pat[k][1] = s[k].b;
         args.pat[k][2] = s[k].c;
         args.pat[k][3] = s[k].d;
+        args.sub[k][0] = s[k].a / rt.P;
+        args.sub[k][1] = s[k].d / rt.Q * rt.T;
         args.w[k] = W[k];
         maxbc = std::max(maxbc, s[k].b * s[k].c);
     }
-    const int64_t blocks = (batch + args.rows - 1) / args.rows;
+    const int64_t blocks = (batch + args.rows - 1) / args.rows * args.ntiles;
     if (blocks > 0x7fffffff) return KS_ERR_UNSUPPORTED;
-    const size_t lds = size_t(2) * args.rows * args.pitch * 4;
+    const size_t lds = size_t(nbuf) * args.rows * args.pitch * 4;
     const dim3 grid(static_cast<unsigned>(blocks));
     if (xt == kF32 && wt == kF32) return launch_rc<float, float>(maxbc, grid, lds, stream, X, Y, args);
     if (xt == kBF16 && wt == kBF16) return launch_rc<bf16_t, bf16_t>(maxbc, grid, lds, stream, X, Y, args);
@@ -297,12 +460,28 @@ ks_status_t launch_row_chain(const Shape* s, int n, int xt, int wt, const void* 
 }
 
 int row_chain_describe(const Shape* s, int n, char* buf, size_t len) {
-    if (resident_chain_supports(s, n, kF32, kF32)) return resident_chain_describe(s, n, buf, len);
-    if (digit_chain_supports(s, n, kF32, kF32)) return digit_chain_describe(s, n, buf, len);
-    const int pitch = row_pitch(s, n);
-    const int rows = chain_rows(pitch);
-    return std::snprintf(buf, len, "row-resident chain: %d factors, rows/wg=%d, row pitch %d floats, lds=%d", n,
-                         rows, pitch, 2 * rows * pitch * 4);
+    RunTile rt;
+    if (!run_tile(s, n, &rt)) return std::snprintf(buf, len, "row-resident chain: unsupported");
+    const bool whole_rows = rt.P == 1 && rt.Q == 1;
+    if (whole_rows && resident_chain_supports(s, n, kF32, kF32)) return resident_chain_describe(s, n, buf, len);
+    if (whole_rows && digit_chain_supports(s, n, kF32, kF32)) return digit_chain_describe(s, n, buf, len);
+    const int pitch = row_pitch(rt);
+    const int nbuf = runs_in_place(s, n) ? 1 : 2;
+    const int rows = chain_rows(pitch, nbuf, !whole_rows);
+    if (whole_rows)
+        return std::snprintf(buf, len, "row-resident chain: %d factors, rows/wg=%d, row pitch %d floats, %s, lds=%d",
+                             n, rows, pitch, nbuf == 1 ? "in place" : "two buffers", nbuf * rows * pitch * 4);
+    if (rt.Q == 1)
+        return std::snprintf(buf, len,
+                             "tile-resident chain: %d factors, %d slabs of %d values, rows/wg=%d, tile pitch %d "
+                             "floats, %s, lds=%d",
+                             n, rt.P, static_cast<int>(rt.width), rows, pitch, nbuf == 1 ? "in place" : "two buffers",
+                             nbuf * rows * pitch * 4);
+    return std::snprintf(buf, len,
+                         "tile-resident chain: %d factors, %d slabs x %d classes, %d classes a tile, rows/wg=%d, "
+                         "tile pitch %d floats, %s, lds=%d",
+                         n, rt.P, rt.Q, rt.T, rows, pitch, nbuf == 1 ? "in place" : "two buffers",
+                         nbuf * rows * pitch * 4);
 }
 
 }  // namespace ks

@@ -124,6 +124,17 @@ def workloads() -> dict:
     w["radix8_n4096"] = Workload("radix8_n4096", [(8 ** k, 8, 8, 8 ** (3 - k)) for k in range(4)], 16384,
                                  [1.0 / np.sqrt(8.0)] * 4, 8,
                                  note="radix-8 butterfly, four factors at n = 4096")
+    # butterflies on rows wider than LDS holds: runs of factors cut by slab
+    # (common divisor of the a's) and index class (common divisor of the d's)
+    w["radix2_n65536"] = Workload("radix2_n65536", [(2 ** k, 2, 2, 2 ** (15 - k)) for k in range(16)], 4096,
+                                  [1.0 / np.sqrt(2.0)] * 16, 12,
+                                  note="radix-2 butterfly, sixteen factors at n = 65,536")
+    w["radix4_n65536"] = Workload("radix4_n65536", [(4 ** k, 4, 4, 4 ** (7 - k)) for k in range(8)], 4096,
+                                  [0.5] * 8, 13,
+                                  note="radix-4 butterfly, eight factors at n = 65,536")
+    w["radix2_n16384"] = Workload("radix2_n16384", [(2 ** k, 2, 2, 2 ** (13 - k)) for k in range(14)], 16384,
+                                  [1.0 / np.sqrt(2.0)] * 14, 14,
+                                  note="radix-2 butterfly, fourteen factors at n = 16,384")
     # a radix-16 pair the strided-pair kernel fuses (e = 4): (64, 16, 16, 64)
     # then (1024, 16, 16, 4) at n = 65,536 (not a configuration of the pages)
     w["strided_pair_e4"] = Workload("strided_pair_e4", [(64, 16, 16, 64), (1024, 16, 16, 4)], 4096, [0.25] * 2, 9,

@@ -516,6 +516,8 @@ ROW_CHAINS = {
     "digits_out_of_order_n64": ([(4, 2, 2, 8), (4, 4, 4, 4), (32, 2, 2, 1), (1, 4, 4, 16), (2, 2, 2, 16),
                                  (8, 2, 2, 4)], 515),
     "radix2_n16": (_radix(2, 4), 3001),
+    # square blocks off the power-of-two path: the general kernel, in place
+    "square_in_place_n72": ([(3, 2, 2, 12), (6, 2, 2, 6), (12, 2, 2, 3)], 333),
 }
 
 
@@ -612,6 +614,74 @@ def test_row_chain_unaligned_rows(bf16):
     libks.chain_matmul(Xo, [to_dev(W, bf16) for W in Ws], pats, out=Yo)
     torch.cuda.synchronize()
     chain_check(pats, X, Ws, Yo.cpu().numpy(), bf16)
+
+
+# Runs of small-block factors whose rows are wider than 4096 elements: one
+# launch per run of factors that share slabs (a divisor of every a) and
+# classes of indices (a divisor of every d), a workgroup holding one slab and
+# a group of classes. (patterns, rows, expected launch groups)
+TILED_CHAINS = {
+    # 65,536-point radix-2: 1024 classes in groups of 16, then 64 slabs of 1024
+    "radix2_n65536": (_radix(2, 16), 37, [list(range(6)), list(range(6, 16))]),
+    # 16,384-point radix-4: 256 classes in groups of 16, then 64 slabs of 256
+    "radix4_n16384": (_radix(4, 7), 21, [[0, 1, 2], [3, 4, 5, 6]]),
+    # three slabs (P = 3), each of 1024 classes taken 128 at a time
+    "slabs3_classes1024": ([(3, 2, 2, 4096), (6, 2, 2, 2048), (12, 2, 2, 1024)], 19, [[0, 1, 2]]),
+    # 1536 classes (not a power of two), 128 a tile
+    "classes1536": ([(1, 2, 2, 6144), (2, 2, 2, 3072), (4, 2, 2, 1536)], 23, [[0, 1, 2]]),
+    # 2050 classes, 205 a tile: runs that are not whole 4-element vectors
+    "classes2050_runs410": ([(1, 2, 2, 4100), (2, 2, 2, 2050)], 17, [[0, 1]]),
+    # five slabs of 1024 (a tile each: 5120 values do not fit)
+    "slabs5_whole": ([(5, 2, 2, 512), (10, 2, 2, 256), (20, 2, 2, 128)], 33, [[0, 1, 2]]),
+    # b != c: 8192 -> 16384 -> 8192 through 4 x 2 and 2 x 4 blocks
+    "expand_contract": ([(1, 4, 2, 4096), (4, 2, 4, 1024)], 29, [[0, 1]]),
+}
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("name", sorted(TILED_CHAINS))
+def test_tiled_row_chain(name, bf16):
+    """Chains on rows too wide for LDS, cut by their closure into slabs and
+    groups of index classes: the planned launch groups, all of Y against the
+    oracle, and the same chain one launch per factor."""
+    pats, batch, groups = TILED_CHAINS[name]
+    wl = datagen.Workload("tiled", pats, batch, [1.0 / np.sqrt(p[2]) for p in pats], 70 + len(pats) + batch)
+    dt = libks.DTYPE_BF16 if bf16 else libks.DTYPE_F32
+    assert libks.ks_chain_groups(pats, batch, dt) == groups
+    X, Ws = datagen.draw(wl)
+    Xt, Wts = to_dev(X, bf16), [to_dev(W, bf16) for W in Ws]
+    Y = libks.chain_matmul(Xt, Wts, pats)
+    Yu = libks.chain_matmul(Xt, Wts, pats, fuse=False)
+    torch.cuda.synchronize()
+    chain_check(pats, X, Ws, Y.cpu().numpy(), bf16)
+    chain_check(pats, X, Ws, Yu.cpu().numpy(), bf16)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_tiled_row_chain_unaligned(bf16):
+    """A tiled run with X and Y one element past a 16-byte boundary: the
+    element-wise load and store paths of the tiles."""
+    pats, batch = _radix(2, 13), 9
+    wl = datagen.Workload("tiled", pats, batch, [1.0 / np.sqrt(2.0)] * len(pats), 19)
+    X, Ws = datagen.draw(wl)
+    Xo = _offset_copy(to_dev(X, bf16), 1)
+    Yo = _offset_out(batch, 8192, 1)
+    libks.chain_matmul(Xo, [to_dev(W, bf16) for W in Ws], pats, out=Yo)
+    torch.cuda.synchronize()
+    chain_check(pats, X, Ws, Yo.cpu().numpy(), bf16)
+
+
+def test_tiled_hadamard_exact():
+    """The 16,384-point Walsh-Hadamard transform (fourteen radix-2 factors of
+    [[1, 1], [1, -1]] blocks) on small integers runs as two tiled launches
+    and is exact in fp32: bit for bit the oracle."""
+    pats = datagen.hadamard_patterns(14)
+    assert libks.ks_chain_groups(pats, 11, libks.DTYPE_F32) == [list(range(6)), list(range(6, 14))]
+    wl = datagen.Workload("hadamard16384", pats, 11, [1.0] * len(pats), 14, x_kind="int8range", w_kind="hadamard")
+    X, Ws = datagen.draw(wl)
+    Y = libks.chain_matmul(to_dev(X), [to_dev(W) for W in Ws], pats).cpu().numpy()
+    ref = oracle.ks_chain_matmul(pats, [host_values(W, False) for W in Ws], host_values(X, False))
+    assert np.array_equal(Y.astype(np.float64), ref)
 
 
 def _offset_copy(t: torch.Tensor, elems: int) -> torch.Tensor:
