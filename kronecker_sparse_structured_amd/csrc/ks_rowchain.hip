@@ -49,18 +49,18 @@ namespace {
 
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kMaxFactors = 16;              // factors per launch
 constexpr int kMaxWidth = 4096;              // widest row of the run (elements)
 constexpr int kLdsTarget = 32 * 1024;        // LDS of the two row buffers (rows of 4096: 2 rows)
-constexpr int kTiledLdsTarget = 64 * 1024;   // the same for tiles of rows too wide for LDS
+constexpr int kTiledLdsTarget = 48 * 1024;   // the same for tiles of rows too wide for LDS (three a CU)
 constexpr int kMaxRows = 32;                 // rows per workgroup of a tiled run (16 for whole rows)
 constexpr int64_t kSlabTarget = 256;         // slabs merged into tiles of at most this many values
-constexpr int64_t kClassWidth = 1024;        // widest tile made of index classes (16 rows in 64 KB)
+constexpr int64_t kClassWidth = 1024;        // widest tile made of index classes (12 rows in 48 KB)
 constexpr int64_t kMaxWeightBytes = 64 * 1024;
 constexpr int kMaxBlock = 16;                // b * c held in registers
 
-constexpr int kMinRun = 16;                  // elements per run of X / Y when tiles are class groups
+constexpr int kMinRun = 32;                  // elements per run of X / Y when tiles are class groups
 
 struct RowChainArgs {
     int nf;                  // factors in the run
@@ -241,9 +241,10 @@ __global__ __launch_bounds__(kThreads) void row_chain_kernel(const TX* __restric
     // buffers as offsets from the LDS array itself (a pointer picked from an
     // array of pointers would lose its address space: generic accesses)
     const int bufsz = args.inplace ? 0 : args.rows * pitch;
+    const unsigned wg = blockIdx.x;
     // workgroup: row block, then tile (slab p, classes q0 .. q0 + T - 1)
-    const int tile = static_cast<int>(blockIdx.x % static_cast<unsigned>(args.ntiles));
-    const int64_t n0 = int64_t(blockIdx.x / static_cast<unsigned>(args.ntiles)) * args.rows;
+    const int tile = static_cast<int>(wg % static_cast<unsigned>(args.ntiles));
+    const int64_t n0 = int64_t(wg / static_cast<unsigned>(args.ntiles)) * args.rows;
     const int groups_per_slab = args.Q / args.T;
     const int p = tile / groups_per_slab;
     const int q0 = (tile - p * groups_per_slab) * args.T;
@@ -332,12 +333,15 @@ int64_t gcd64(int64_t x, int64_t y) {
 // slabs, as many as stay within kSlabTarget values (one when a slab is
 // wider), a run of contiguous values; else one of the P slabs and T of its Q
 // classes (Q = gcd of the d's), the most classes within kClassWidth values
-// and at least kMinRun of them, so that X and Y move in runs of 64 bytes.
+// and at least kMinRun of them, so that fp32 X and Y move in runs of whole
+// 128-byte lines (runs of 64 bytes read 1.5 times the bytes of X and Y by
+// the HBM counters: each line fetched twice).
 // Narrow tiles leave room for more rows, and every row a workgroup holds
 // shares the weights it reads (measured on 65,536-, 16,384- and 8,192-point
 // radix-2 and radix-4 butterflies: tiles of 256-value slabs and of 1024
 // class values with up to 32 rows beat 4096-value tiles of 4 rows by up to
-// 1.6 times).
+// 1.6 times; 512 threads and 48 KB of LDS a workgroup beat 256 threads and
+// 64 KB by another 1.1 to 1.5 times, 1024 threads lost).
 struct RunTile {
     int P, Q, T;
     int64_t width;           // floats of the widest tile row

@@ -303,7 +303,7 @@ def test_chain_plan_row_resident_runs():
     assert libks.ks_chain_groups(radix2, 100, libks.DTYPE_F32) == [list(range(12))]
     assert libks.ks_chain_groups(radix2, 100, libks.DTYPE_F32, libks.CHAIN_NO_FUSE) == [[k] for k in range(12)]
     wide = [(2 ** k, 2, 2, 2 ** (12 - k)) for k in range(13)]          # n = 8192: two tiled runs
-    assert libks.ks_chain_groups(wide, 100, libks.DTYPE_F32) == [list(range(6)), list(range(6, 13))]
+    assert libks.ks_chain_groups(wide, 100, libks.DTYPE_F32) == [list(range(5)), list(range(5, 13))]
     mixed = [(64, 4, 4, 4), (1, 64, 16, 64), (256, 4, 4, 4), (256, 4, 4, 4)]
     assert libks.ks_chain_groups(mixed, 100, libks.DTYPE_F32) == [[0], [1], [2, 3]]
     big_blocks = [(1, 16, 8, 256), (16, 2, 2, 128), (32, 2, 2, 64)]    # 16 x 8 blocks first
@@ -317,28 +317,28 @@ def test_chain_plan_tiled_runs():
     into slabs (P divides every a) when one slab fits in 4096 values, as
     many consecutive slabs a tile as stay within 256 values; or else into one
     slab and groups of T of its Q index classes (Q divides every d), at most
-    1024 values of a row a tile, in runs of at least 16 elements; the run
-    ends where no such tile exists."""
+    1024 values of a row a tile, in runs of at least 32 elements (128-byte
+    lines of fp32); the run ends where no such tile exists."""
     f32 = libks.DTYPE_F32
     radix2 = [(2 ** k, 2, 2, 2 ** (15 - k)) for k in range(16)]      # n = 65,536
-    assert libks.ks_chain_groups(radix2, 4096, f32) == [list(range(6)), list(range(6, 16))]
+    assert libks.ks_chain_groups(radix2, 4096, f32) == [list(range(5)), list(range(5, 16))]
     desc = libks.ks_chain_describe(radix2, 4096, f32)
-    assert "1 slabs x 1024 classes, 16 classes a tile" in desc, desc
-    assert "64 slabs of 1024 values" in desc, desc
+    assert "1 slabs x 2048 classes, 32 classes a tile" in desc, desc
+    assert "32 slabs of 2048 values" in desc, desc
     radix4 = [(4 ** k, 4, 4, 4 ** (7 - k)) for k in range(8)]         # n = 65,536
-    assert libks.ks_chain_groups(radix4, 4096, f32) == [[0, 1, 2], [3, 4, 5, 6, 7]]
+    assert libks.ks_chain_groups(radix4, 4096, f32) == [[0, 1], [2, 3, 4, 5, 6, 7]]
     three_slabs = [(3, 2, 2, 4096), (6, 2, 2, 2048), (12, 2, 2, 1024)]
     assert "3 slabs x 1024 classes, 128 classes a tile" in libks.ks_chain_describe(three_slabs, 7, f32)
     assert "1 slabs x 2050 classes, 205 classes a tile" in libks.ks_chain_describe(
         [(1, 2, 2, 4100), (2, 2, 2, 2050)], 7, f32)
     assert "5 slabs of 1024 values" in libks.ks_chain_describe(
         [(5, 2, 2, 512), (10, 2, 2, 256), (20, 2, 2, 128)], 7, f32)
-    # radix-4 on n = 32,768: a fourth factor would leave 128 classes of 256
-    # values (runs of 4 in a 1024-value tile), so the run stops at three; the
-    # last three factors share 64 slabs of 512 values
+    # radix-4 on n = 32,768: a third factor would leave 512 classes of 64
+    # values (runs of 16 in a 1024-value tile), so the run stops at two; the
+    # last four factors share 16 slabs of 2048 values
     radix4_odd = [(4 ** k, 4, 4, 2 ** 13 // 4 ** k) for k in range(6)]
-    assert libks.ks_chain_groups(radix4_odd, 7, f32) == [[0, 1, 2], [3, 4, 5]]
-    assert "64 slabs of 512 values" in libks.ks_chain_describe(radix4_odd, 7, f32)
+    assert libks.ks_chain_groups(radix4_odd, 7, f32) == [[0, 1], [2, 3, 4, 5]]
+    assert "16 slabs of 2048 values" in libks.ks_chain_describe(radix4_odd, 7, f32)
 
 
 def test_chain_plan_fuses_known_pairs():
