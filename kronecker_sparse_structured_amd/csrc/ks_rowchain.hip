@@ -49,12 +49,14 @@ namespace {
 
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 512;
+constexpr int kThreads = 256;              // threads of a workgroup on whole rows
+constexpr int kTiledThreads = 512;         // and on tiles of rows too wide for LDS
 constexpr int kMaxFactors = 16;              // factors per launch
 constexpr int kMaxWidth = 4096;              // widest row of the run (elements)
 constexpr int kLdsTarget = 32 * 1024;        // LDS of the two row buffers (rows of 4096: 2 rows)
 constexpr int kTiledLdsTarget = 48 * 1024;   // the same for tiles of rows too wide for LDS (three a CU)
-constexpr int kMaxRows = 32;                 // rows per workgroup of a tiled run (16 for whole rows)
+constexpr int kMaxRows = 32;                 // rows per workgroup of a tiled run
+constexpr int kMaxWholeRows = 256;           // and of a run on whole rows (narrow rows: many a workgroup)
 constexpr int64_t kSlabTarget = 256;         // slabs merged into tiles of at most this many values
 constexpr int64_t kClassWidth = 1024;        // widest tile made of index classes (12 rows in 48 KB)
 constexpr int64_t kMaxWeightBytes = 64 * 1024;
@@ -83,6 +85,7 @@ struct RowChainArgs {
 struct BlockMap {
     int abase, d, Q, T, q0;
     __device__ __forceinline__ int64_t block(int alpha, int dext) const {
+        if (T == 1) return int64_t(abase + alpha) * d + dext * Q + q0;   // whole rows and slabs: no division
         const int dq = dext / T;
         return int64_t(abase + alpha) * d + dq * Q + q0 + (dext - dq * T);
     }
@@ -96,20 +99,21 @@ __device__ __forceinline__ int tile_offset(int l, int slab0, int Q, int T, int q
     return slab0 + e * Q + q0 + (l - e * T);
 }
 
-// Threads of one factor: with at least kThreads groups a thread takes
-// groups t, t + kThreads, ... over all rows; with fewer, the rows of a group
-// are dealt out to kThreads / groups threads.
+// Threads of one factor (NT in the workgroup): with at least NT groups a
+// thread takes groups t, t + NT, ... over all rows; with fewer, the rows of
+// a group are dealt out to NT / groups threads.
 struct ItemMap {
     int g0, gstep, r0, rstep;
 };
 
+template <int NT>
 __device__ __forceinline__ bool item_map(int groups, ItemMap* m) {
     const int t = threadIdx.x;
-    if (groups >= kThreads) {
-        *m = ItemMap{t, kThreads, 0, 1};
+    if (groups >= NT) {
+        *m = ItemMap{t, NT, 0, 1};
         return true;
     }
-    const int tpg = kThreads / groups;
+    const int tpg = NT / groups;
     *m = ItemMap{t % groups, groups, t / groups, tpg};
     return t / groups < tpg;
 }
@@ -118,14 +122,15 @@ __device__ __forceinline__ bool item_map(int groups, ItemMap* m) {
 // blocks: a thread holds the B * C weights of its (alpha, delta) group in
 // registers and applies them to each of its rows (C inputs read from LDS
 // once, B outputs written).
-template <int B, int C, typename TW>
+template <int NT, int B, int C, typename TW>
 __device__ __forceinline__ void apply_block(const float* src, float* dst, int pitch, int nr, int a, int d,
                                             const TW* __restrict__ K, const BlockMap& bm) {
-    // the blocks of NB groups are loaded together (one wait on the cache for
-    // NB groups, not one per group), at most 16 weights and 8 groups a thread
-    constexpr int NB = B * C >= 16 ? 1 : (16 / (B * C) > 8 ? 8 : 16 / (B * C));
+    // on tiles, the blocks of NB groups are loaded together (one wait on the
+    // cache for NB groups, not one per group), at most 16 weights and 8
+    // groups a thread; on whole rows one group at a time measured faster
+    constexpr int NB = (NT != kTiledThreads || B * C >= 16) ? 1 : (16 / (B * C) > 8 ? 8 : 16 / (B * C));
     ItemMap m;
-    if (!item_map(a * d, &m)) return;
+    if (!item_map<NT>(a * d, &m)) return;
     const int groups = a * d;
     for (int g0 = m.g0; g0 < groups; g0 += NB * m.gstep) {
         float w[NB][B][C];
@@ -169,11 +174,11 @@ __device__ __forceinline__ void apply_block(const float* src, float* dst, int pi
 }
 
 // Any b, c (up to 16): weights read from global memory (cached) per row.
-template <typename TW>
+template <int NT, typename TW>
 __device__ __forceinline__ void apply_any(const float* src, float* dst, int pitch, int nr, int a, int b, int c,
                                           int d, const TW* __restrict__ K, const BlockMap& bm) {
     ItemMap m;
-    if (!item_map(a * d, &m)) return;
+    if (!item_map<NT>(a * d, &m)) return;
     for (int g = m.g0; g < a * d; g += m.gstep) {
         const int alpha = g / d;
         const int delta = g - alpha * d;
@@ -193,48 +198,48 @@ __device__ __forceinline__ void apply_any(const float* src, float* dst, int pitc
 // B x C blocks up to MAXBC weights take the register path (a kernel's VGPR
 // count follows its largest block: MAXBC = 16 keeps it near 54 VGPRs, eight
 // waves per SIMD).
-template <int MAXBC, int B, int C, typename TW>
+template <int NT, int MAXBC, int B, int C, typename TW>
 __device__ __forceinline__ bool try_block(const float* src, float* dst, int pitch, int nr, int a, int d,
                                           const TW* __restrict__ K, const BlockMap& bm) {
     if constexpr (B * C <= MAXBC) {
-        apply_block<B, C>(src, dst, pitch, nr, a, d, K, bm);
+        apply_block<NT, B, C>(src, dst, pitch, nr, a, d, K, bm);
         return true;
     } else {
         return false;
     }
 }
 
-template <int MAXBC, int B, typename TW>
+template <int NT, int MAXBC, int B, typename TW>
 __device__ __forceinline__ void apply_b(const float* src, float* dst, int pitch, int nr, int a, int c, int d,
                                         const TW* __restrict__ K, const BlockMap& bm) {
     bool done = false;
     switch (c) {
-        case 1: done = try_block<MAXBC, B, 1>(src, dst, pitch, nr, a, d, K, bm); break;
-        case 2: done = try_block<MAXBC, B, 2>(src, dst, pitch, nr, a, d, K, bm); break;
-        case 4: done = try_block<MAXBC, B, 4>(src, dst, pitch, nr, a, d, K, bm); break;
-        case 8: done = try_block<MAXBC, B, 8>(src, dst, pitch, nr, a, d, K, bm); break;
-        case 16: done = try_block<MAXBC, B, 16>(src, dst, pitch, nr, a, d, K, bm); break;
+        case 1: done = try_block<NT, MAXBC, B, 1>(src, dst, pitch, nr, a, d, K, bm); break;
+        case 2: done = try_block<NT, MAXBC, B, 2>(src, dst, pitch, nr, a, d, K, bm); break;
+        case 4: done = try_block<NT, MAXBC, B, 4>(src, dst, pitch, nr, a, d, K, bm); break;
+        case 8: done = try_block<NT, MAXBC, B, 8>(src, dst, pitch, nr, a, d, K, bm); break;
+        case 16: done = try_block<NT, MAXBC, B, 16>(src, dst, pitch, nr, a, d, K, bm); break;
     }
-    if (!done) apply_any(src, dst, pitch, nr, a, B, c, d, K, bm);
+    if (!done) apply_any<NT>(src, dst, pitch, nr, a, B, c, d, K, bm);
 }
 
 // One factor on the tile: a and d are the tile's (a / P, (d / Q) T); bm
 // finds the blocks.
-template <int MAXBC, typename TW>
+template <int NT, int MAXBC, typename TW>
 __device__ __forceinline__ void apply_factor(const float* src, float* dst, int pitch, int nr, int a, int b, int c,
                                              int d, const TW* __restrict__ K, const BlockMap& bm) {
     switch (b) {
-        case 1: apply_b<MAXBC, 1>(src, dst, pitch, nr, a, c, d, K, bm); return;
-        case 2: apply_b<MAXBC, 2>(src, dst, pitch, nr, a, c, d, K, bm); return;
-        case 4: apply_b<MAXBC, 4>(src, dst, pitch, nr, a, c, d, K, bm); return;
-        case 8: apply_b<MAXBC, 8>(src, dst, pitch, nr, a, c, d, K, bm); return;
-        case 16: apply_b<MAXBC, 16>(src, dst, pitch, nr, a, c, d, K, bm); return;
+        case 1: apply_b<NT, MAXBC, 1>(src, dst, pitch, nr, a, c, d, K, bm); return;
+        case 2: apply_b<NT, MAXBC, 2>(src, dst, pitch, nr, a, c, d, K, bm); return;
+        case 4: apply_b<NT, MAXBC, 4>(src, dst, pitch, nr, a, c, d, K, bm); return;
+        case 8: apply_b<NT, MAXBC, 8>(src, dst, pitch, nr, a, c, d, K, bm); return;
+        case 16: apply_b<NT, MAXBC, 16>(src, dst, pitch, nr, a, c, d, K, bm); return;
     }
-    apply_any(src, dst, pitch, nr, a, b, c, d, K, bm);
+    apply_any<NT>(src, dst, pitch, nr, a, b, c, d, K, bm);
 }
 
-template <typename TX, typename TW, int MAXBC>
-__global__ __launch_bounds__(kThreads) void row_chain_kernel(const TX* __restrict__ X, float* __restrict__ Y,
+template <typename TX, typename TW, int MAXBC, int NT>
+__global__ __launch_bounds__(NT) void row_chain_kernel(const TX* __restrict__ X, float* __restrict__ Y,
                                                              RowChainArgs args) {
     extern __shared__ __align__(16) float zbuf[];
     const int pitch = args.pitch;
@@ -256,14 +261,14 @@ __global__ __launch_bounds__(kThreads) void row_chain_kernel(const TX* __restric
     const int slab_in = p * (args.n_in / args.P);
     if (args.vec_x) {
         const int q = args.tin / 4;
-        for (int i = t; i < nr * q; i += kThreads) {
+        for (int i = t; i < nr * q; i += NT) {
             const int r = i / q, j = i - r * q;
             float v[4];
             load4_f32(xs + int64_t(r) * args.n_in + tile_offset(4 * j, slab_in, args.Q, args.T, q0), v);
             *reinterpret_cast<floatx4_t*>(zbuf + r * pitch + 4 * j) = floatx4_t{v[0], v[1], v[2], v[3]};
         }
     } else {
-        for (int i = t; i < nr * args.tin; i += kThreads) {
+        for (int i = t; i < nr * args.tin; i += NT) {
             const int r = i / args.tin, j = i - r * args.tin;
             zbuf[r * pitch + j] = to_f32(xs[int64_t(r) * args.n_in + tile_offset(j, slab_in, args.Q, args.T, q0)]);
         }
@@ -277,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void row_chain_kernel(const TX* __restric
         const TW* K = static_cast<const TW*>(args.w[f]);
         const float* src = zbuf + (f & 1) * bufsz;
         float* dst = zbuf + ((f + 1) & 1) * bufsz;
-        apply_factor<MAXBC>(src, dst, pitch, nr, a, b, c, d, K, bm);
+        apply_factor<NT, MAXBC>(src, dst, pitch, nr, a, b, c, d, K, bm);
         __syncthreads();
     }
 
@@ -287,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void row_chain_kernel(const TX* __restric
     const int slab_out = p * (args.n_out / args.P);
     if (args.vec_y) {
         const int q = args.tout / 4;
-        for (int i = t; i < nr * q; i += kThreads) {
+        for (int i = t; i < nr * q; i += NT) {
             const int r = i / q, j = i - r * q;
             const floatx4_t v = *reinterpret_cast<const floatx4_t*>(z + r * pitch + 4 * j);
             __builtin_nontemporal_store(
@@ -295,7 +300,7 @@ __global__ __launch_bounds__(kThreads) void row_chain_kernel(const TX* __restric
                                                 tile_offset(4 * j, slab_out, args.Q, args.T, q0)));
         }
     } else {
-        for (int i = t; i < nr * args.tout; i += kThreads) {
+        for (int i = t; i < nr * args.tout; i += NT) {
             const int r = i / args.tout, j = i - r * args.tout;
             ys[int64_t(r) * args.n_out + tile_offset(j, slab_out, args.Q, args.T, q0)] = z[r * pitch + j];
         }
@@ -308,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void row_chain_kernel(const TX* __restric
 // least two rows, so that each weight block loaded serves more than one row.
 int chain_rows(int pitch, int nbuf, bool tiled) {
     const int target = tiled ? kTiledLdsTarget : kLdsTarget;
-    return std::max(2, std::min(tiled ? kMaxRows : 16, target / (nbuf * 4 * pitch)));
+    return std::max(2, std::min(tiled ? kMaxRows : kMaxWholeRows, target / (nbuf * 4 * pitch)));
 }
 
 // Factors that can run in place: square blocks on the register path.
@@ -400,11 +405,15 @@ bool row_chain_supports(const Shape* s, int n, int xt, int wt) {
 }
 
 template <typename TX, typename TW>
-ks_status_t launch_rc(int maxbc, dim3 grid, size_t lds, hipStream_t stream, const void* X, float* Y,
+ks_status_t launch_rc(int maxbc, bool tiled, dim3 grid, size_t lds, hipStream_t stream, const void* X, float* Y,
                       const RowChainArgs& args) {
     const TX* x = static_cast<const TX*>(X);
     if (maxbc > kMaxBlock) return KS_ERR_UNSUPPORTED;
-    return launch_kernel(row_chain_kernel<TX, TW, kMaxBlock>, grid, dim3(kThreads), lds, stream, x, Y, args);
+    if (tiled)
+        return launch_kernel(row_chain_kernel<TX, TW, kMaxBlock, kTiledThreads>, grid, dim3(kTiledThreads), lds,
+                             stream, x, Y, args);
+    return launch_kernel(row_chain_kernel<TX, TW, kMaxBlock, kThreads>, grid, dim3(kThreads), lds, stream, x, Y,
+                         args);
 }
 
 ks_status_t launch_row_chain(const Shape* s, int n, int xt, int wt, const void* const* W, const void* X, float* Y,
@@ -457,9 +466,9 @@ ks_status_t launch_row_chain(const Shape* s, int n, int xt, int wt, const void* 
     if (blocks > 0x7fffffff) return KS_ERR_UNSUPPORTED;
     const size_t lds = size_t(nbuf) * args.rows * args.pitch * 4;
     const dim3 grid(static_cast<unsigned>(blocks));
-    if (xt == kF32 && wt == kF32) return launch_rc<float, float>(maxbc, grid, lds, stream, X, Y, args);
-    if (xt == kBF16 && wt == kBF16) return launch_rc<bf16_t, bf16_t>(maxbc, grid, lds, stream, X, Y, args);
-    if (xt == kF32 && wt == kBF16) return launch_rc<float, bf16_t>(maxbc, grid, lds, stream, X, Y, args);
+    if (xt == kF32 && wt == kF32) return launch_rc<float, float>(maxbc, !whole_rows, grid, lds, stream, X, Y, args);
+    if (xt == kBF16 && wt == kBF16) return launch_rc<bf16_t, bf16_t>(maxbc, !whole_rows, grid, lds, stream, X, Y, args);
+    if (xt == kF32 && wt == kBF16) return launch_rc<float, bf16_t>(maxbc, !whole_rows, grid, lds, stream, X, Y, args);
     return KS_ERR_UNSUPPORTED;
 }
 
