@@ -658,6 +658,18 @@ def test_tiled_row_chain(name, bf16):
 
 
 @pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("name", ["radix2_n65536", "radix4_n65536", "radix2_n16384"])
+def test_tiled_chain_full_size(name, bf16):
+    """The wide butterflies at the size the benchmark times (4,096 rows of
+    65,536, 16,384 rows of 16,384), in its launch configuration (two tiled
+    launches whose last row blocks are ragged): every output."""
+    wl = datagen.get(name)
+    dt = libks.DTYPE_BF16 if bf16 else libks.DTYPE_F32
+    assert len(libks.ks_chain_groups(wl.patterns, wl.batch, dt)) == 2
+    _chain_workload(name, bf16, True)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
 def test_tiled_row_chain_unaligned(bf16):
     """A tiled run with X and Y one element past a 16-byte boundary: the
     element-wise load and store paths of the tiles."""
@@ -1008,3 +1020,22 @@ def test_kslinear_inference_row_chain(bf16):
           oracle.widen(w.detach().cpu().numpy(), "f32") for w in L.weights]
     ref = oracle.ks_chain_matmul(pats, Ks, host_values(x_np.reshape(-1, L.n_in), bf16))
     assert _rel(y.reshape(-1, L.n_out).cpu().numpy(), ref) <= FP32_REL_TOL
+
+
+def test_kslinear_inference_tiled_chain():
+    """The layer's inference path on rows wider than LDS holds: a radix-2
+    butterfly on n = 8192 runs as two tiled launches (X a view that starts
+    one row into its storage), against the oracle chain on the layer's
+    weights."""
+    from kronecker_sparse_structured_amd import layer
+    pats = _radix(2, 13)
+    assert libks.ks_chain_groups(pats, 21, libks.DTYPE_F32) == [list(range(5)), list(range(5, 13))]
+    L = layer.KSLinear(pats, device=DEV, seed=6)
+    x_np = np.random.default_rng(13).standard_normal((22, L.n_in), dtype=np.float32)
+    x = to_dev(x_np)[1:]
+    with torch.no_grad():
+        y = L(x)
+    torch.cuda.synchronize()
+    Ks = [oracle.widen(w.detach().cpu().numpy(), "f32") for w in L.weights]
+    ref = oracle.ks_chain_matmul(pats, Ks, host_values(x_np[1:], False))
+    assert _rel(y.cpu().numpy(), ref) <= FP32_REL_TOL
