@@ -247,11 +247,23 @@ ks_status_t plan_chain(const ks_pattern_t* p, int n, int64_t batch, int dt,
                 len = 2;
                 kind = 5;
             } else {
-                // the longest run from k whose rows fit on chip
+                // the longest run from k whose rows (or closure tiles) fit on chip
                 for (int m = n - k; m >= 2; --m) {
                     if (ks::row_chain_supports(&plan->shapes[k], m, xt, plan->wt)) {
                         len = m;
                         kind = 3;
+                        break;
+                    }
+                }
+                // but stop it earlier if that leaves the rest of the chain as one
+                // whole radix-2/4 butterfly on each slab: the register-resident
+                // kernel takes that (fp32 intermediates)
+                int slabs = 0;
+                for (int m = len - 1; kind == 3 && m >= 2 && k + len < n; --m) {
+                    if (n - k - m >= 2 &&
+                        ks::resident_slab_form(&plan->shapes[k + m], n - k - m, ks::kF32, plan->wt, &slabs) &&
+                        ks::row_chain_supports(&plan->shapes[k + m], n - k - m, ks::kF32, plan->wt)) {
+                        len = m;
                         break;
                     }
                 }

@@ -136,12 +136,18 @@ int digit_chain_describe(const Shape* s, int n, char* buf, size_t len);
 // Whole radix-2 or radix-4 butterflies on 1024- or 4096-wide rows, every
 // weight held in registers by one persistent workgroup a compute unit
 // (ks_resident.hip); needs X and Y 16-byte aligned. launch_row_chain takes
-// it first.
+// it first. The same on rows cut into slabs that each carry such a whole
+// butterfly with their own blocks (every a divisible by the slab count):
+// resident_slab_form finds the slab count, each workgroup keeps one slab's
+// weights.
 bool resident_chain_supports(const Shape* s, int n, int xt, int wt);
+bool resident_slab_form(const Shape* s, int n, int xt, int wt, int* slabs);
 bool resident_chain_aligned(const void* X, const float* Y);
 ks_status_t launch_resident_chain(const Shape* s, int n, int xt, int wt, const void* const* W, const void* X,
                                   float* Y, int64_t batch, hipStream_t stream, int num_cus);
-int resident_chain_describe(const Shape* s, int n, char* buf, size_t len);
+ks_status_t launch_resident_slabs(const Shape* s, int n, int slabs, int xt, int wt, const void* const* W,
+                                  const void* X, float* Y, int64_t batch, hipStream_t stream, int num_cus);
+int resident_chain_describe(const Shape* s, int n, int slabs, char* buf, size_t len);
 // The closure rule for fusing factor f then g (ks_closure.cpp): closed
 // components of the intermediate, with the largest component's sizes (in
 // values) and the shortest runs of consecutive indices its X reads and Y

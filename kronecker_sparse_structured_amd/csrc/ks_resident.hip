@@ -70,13 +70,17 @@ typedef uint32_t uint32x2 __attribute__((ext_vector_type(2)));
 enum PassKind : int { kRadix4 = 0, kLowFirst = 1, kHighFirst = 2 };
 
 struct ResArgs {
-    int lg;                          // log2 of the row width
+    int lg;                          // log2 of the row width (of a slab)
     int npass;
     int rows;                        // rows per block
-    int nblocks;
+    int nblocks;                     // row blocks (of each slab)
     int64_t batch;
+    int slabs;                       // slabs of a row, each its own butterfly; workgroups take one each
+    int64_t ldx, ldy;                // elements from one row of X / Y to the next
     const void* w0[kMaxPasses];      // the pass's (first) factor
     const void* w1[kMaxPasses];      // its second radix-2 factor
+    int64_t ws0[kMaxPasses];         // elements of w0 / w1 from one slab's blocks to the next
+    int64_t ws1[kMaxPasses];
 };
 
 // The column of thread t in a pass on digit bits p, p + 1 of an L-bit index:
@@ -186,21 +190,28 @@ __device__ __forceinline__ void dma_1k(const void* g, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
 }
 
-// Copy block `blk` of X into LDS at byte `dst`: each wave its share of 1 KB
-// chunks. Returns nothing; the wave's vmcnt covers its chunks.
+// Copy block `blk` of X (X points at the workgroup's slab of row 0) into
+// LDS at byte `dst`, rows packed: each wave its share of 1 KB chunks, chunk
+// c being 1 KB (c mod chunks-per-row) of row c / chunks-per-row. Returns
+// nothing; the wave's vmcnt covers its chunks.
 template <typename TX>
 __device__ __forceinline__ void issue_block(const TX* X, const ResArgs& a, int blk, uint32_t dst) {
     const int64_t row0 = int64_t(blk) * a.rows;
     const int nr = static_cast<int>(min(int64_t(a.rows), a.batch - row0));
-    const int64_t row_bytes = int64_t(sizeof(TX)) << a.lg;
-    const int chunks = static_cast<int>((nr * row_bytes) >> 10);
+    const int row_log = a.lg + (sizeof(TX) == 2 ? 1 : 2) - 10;      // log2 of 1 KB chunks a row (>= 1)
+    const int chunks = nr << row_log;
+    const int64_t ld_bytes = a.ldx * int64_t(sizeof(TX));
     constexpr int per_wave = (kBlockBytes * sizeof(TX) / 4) / 1024 / (kThreads / 64);
     const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-    const char* src = reinterpret_cast<const char*>(X) + row0 * row_bytes + (threadIdx.x & 63) * 16;
+    const char* src = reinterpret_cast<const char*>(X) + row0 * ld_bytes + (threadIdx.x & 63) * 16;
 #pragma unroll
     for (int j = 0; j < per_wave; ++j) {
         const int c = w * per_wave + j;
-        if (c < chunks) dma_1k(src + int64_t(c) * 1024, dst + c * 1024);
+        if (c < chunks) {
+            const int r = c >> row_log;
+            const int part = c - (r << row_log);
+            dma_1k(src + int64_t(r) * ld_bytes + part * 1024, dst + c * 1024);
+        }
     }
 }
 
@@ -235,7 +246,6 @@ template <typename TX, typename TW, int L, int B, int DESC>
 __global__ __launch_bounds__(kThreads) void resident_chain_kernel(const TX* __restrict__ X, float* __restrict__ Y,
                                                                   ResArgs args) {
     using C = Chain<L, B, DESC>;
-    constexpr int n = 1 << L;
     constexpr bool kWiden = sizeof(TX) == 2;
     extern __shared__ __align__(16) unsigned char lds[];
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
@@ -246,7 +256,14 @@ __global__ __launch_bounds__(kThreads) void resident_chain_kernel(const TX* __re
         return lds0 + (kWiden ? kBlockBytes + b * (kBlockBytes / 2) : b * kBlockBytes);
     };
 
-    int bi = blockIdx.x;
+    // workgroup: slab blockIdx.x % slabs (its weights), row blocks
+    // blockIdx.x / slabs, + gridDim.x / slabs, ... (the grid is a multiple of
+    // the slab count)
+    const int slab = static_cast<int>(blockIdx.x % static_cast<unsigned>(args.slabs));
+    const int bstep = static_cast<int>(gridDim.x / static_cast<unsigned>(args.slabs));
+    X += int64_t(slab) << L;
+    Y += int64_t(slab) << L;
+    int bi = static_cast<int>(blockIdx.x / static_cast<unsigned>(args.slabs));
     if (bi < args.nblocks) issue_block(X, args, bi, dma_dst(0));
 
     float wr[C::NP][16];
@@ -259,18 +276,18 @@ __global__ __launch_bounds__(kThreads) void resident_chain_kernel(const TX* __re
         column_of(p, L, t, base, r, g);
         addr[ps] = ((base | (r << p)) << 2) + (g << (L + 2));
         if (ps == C::NP - 1) base_last = base;
-        load_pass_weights<TW>(wr[ps], static_cast<const TW*>(args.w0[ps]), static_cast<const TW*>(args.w1[ps]),
-                              C::kind, p, base, r);
+        const TW* k0 = static_cast<const TW*>(args.w0[ps]) + slab * args.ws0[ps];
+        const TW* k1 = args.w1[ps] ? static_cast<const TW*>(args.w1[ps]) + slab * args.ws1[ps] : nullptr;
+        load_pass_weights<TW>(wr[ps], k0, k1, C::kind, p, base, r);
     }
     const int gq = __builtin_amdgcn_readfirstlane(g);
 
     int nst = 0;                                 // this wave's stores of the previous block
-    for (int it = 0; bi < args.nblocks; bi += gridDim.x, ++it) {
+    for (int it = 0; bi < args.nblocks; bi += bstep, ++it) {
         const int cur = it & 1;
         wait_stores(nst);                        // this wave's chunks of block bi have landed
         lds_barrier();                           // every wave's have; the previous block is done
-        if (bi + static_cast<int>(gridDim.x) < args.nblocks)
-            issue_block(X, args, bi + gridDim.x, dma_dst(cur ^ 1));
+        if (bi + bstep < args.nblocks) issue_block(X, args, bi + bstep, dma_dst(cur ^ 1));
         const int64_t row0 = int64_t(bi) * args.rows;
         const int nr = static_cast<int>(min(int64_t(args.rows), args.batch - row0));
         const uint32_t work = kWiden ? 0u : static_cast<uint32_t>(cur * kBlockBytes);
@@ -324,7 +341,7 @@ __global__ __launch_bounds__(kThreads) void resident_chain_kernel(const TX* __re
                         for (int e = 0; e < 4; ++e) *reinterpret_cast<float*>(lds + (wa ^ (e << (p + 2)))) = v[e];
                     }
                 } else if (gq + C::Q * j < nr) {
-                    float* yr = Y + (row0 + gq + C::Q * j) * n;
+                    float* yr = Y + (row0 + gq + C::Q * j) * args.ldy;
                     if (p == 0) {
                         __builtin_nontemporal_store(floatx4{v[0], v[1], v[2], v[3]},
                                                     reinterpret_cast<floatx4*>(yr + base_last));
@@ -345,7 +362,6 @@ int log2i(int64_t v) {
     while ((int64_t(1) << l) < v) ++l;
     return l;
 }
-bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 
 // The run as a whole butterfly on 2^lg-wide rows: every factor (a, b, b, d)
 // of one radix b in {2, 4}, digits covering the index bits once each, in
@@ -353,9 +369,10 @@ bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 struct Form {
     int lg, radix, desc;
 };
-bool form_of(const Shape* s, int n, Form* f) {
-    if (n < 2 || n > kMaxRun) return false;
-    const int64_t w = s[0].n_in;
+bool form_of(const Shape* s, int n, int slabs, Form* f) {
+    if (n < 2 || n > kMaxRun || slabs < 1) return false;
+    if (s[0].n_in % slabs != 0) return false;
+    const int64_t w = s[0].n_in / slabs;         // each slab's width
     if (!(w == 1024 || w == 4096)) return false;
     const int b = s[0].b;
     if (!(b == 2 || b == 4)) return false;
@@ -363,12 +380,12 @@ bool form_of(const Shape* s, int n, Form* f) {
     f->radix = b;
     const int q = log2i(b);
     if (n * q != f->lg) return false;
-    if (n < 2) return false;
     f->desc = s[0].d > s[1].d ? 1 : 0;
     for (int k = 0; k < n; ++k) {
-        if (s[k].b != b || s[k].c != b || s[k].n_in != w || s[k].n_out != w) return false;
+        if (s[k].a % slabs != 0) return false;
+        if (s[k].b != b || s[k].c != b || s[k].n_in != w * slabs || s[k].n_out != w * slabs) return false;
         const int64_t d = int64_t(1) << (f->desc ? f->lg - q * (k + 1) : q * k);
-        if (s[k].d != d || int64_t(s[k].a) * b * d != w) return false;
+        if (s[k].d != d || int64_t(s[k].a / slabs) * b * d != w) return false;
     }
     return true;
 }
@@ -393,49 +410,82 @@ ks_status_t launch_typed(const ResArgs& a, int grid, int radix, int desc, const 
 
 }  // namespace
 
+bool resident_types(int xt, int wt) {
+    return (xt == kF32 || xt == kBF16) && (wt == kF32 || wt == kBF16) && !(xt == kBF16 && wt == kF32);
+}
+
 bool resident_chain_supports(const Shape* s, int n, int xt, int wt) {
     Form f{};
-    if (!form_of(s, n, &f)) return false;
-    return (xt == kF32 || xt == kBF16) && (wt == kF32 || wt == kBF16) && !(xt == kBF16 && wt == kF32);
+    return form_of(s, n, 1, &f) && resident_types(xt, wt);
+}
+
+bool resident_slab_form(const Shape* s, int n, int xt, int wt, int* slabs) {
+    Form f{};
+    if (n < 2 || !resident_types(xt, wt)) return false;
+    for (int64_t w : {int64_t(4096), int64_t(1024)}) {
+        if (s[0].n_in % w != 0 || s[0].n_in / w > 0x7fffffff) continue;
+        const int p = static_cast<int>(s[0].n_in / w);
+        if (form_of(s, n, p, &f)) {
+            *slabs = p;
+            return true;
+        }
+    }
+    return false;
 }
 
 bool resident_chain_aligned(const void* X, const float* Y) {
     return reinterpret_cast<uintptr_t>(X) % 16 == 0 && reinterpret_cast<uintptr_t>(Y) % 16 == 0;
 }
 
-ks_status_t launch_resident_chain(const Shape* s, int n, int xt, int wt, const void* const* W, const void* X,
-                                  float* Y, int64_t batch, hipStream_t stream, int num_cus) {
+ks_status_t launch_resident_slabs(const Shape* s, int n, int slabs, int xt, int wt, const void* const* W,
+                                  const void* X, float* Y, int64_t batch, hipStream_t stream, int num_cus) {
     Form f{};
-    if (!resident_chain_supports(s, n, xt, wt) || !resident_chain_aligned(X, Y)) return KS_ERR_UNSUPPORTED;
-    form_of(s, n, &f);
+    if (!form_of(s, n, slabs, &f) || !resident_types(xt, wt) || !resident_chain_aligned(X, Y))
+        return KS_ERR_UNSUPPORTED;
     if (batch == 0) return KS_OK;
     ResArgs a{};
     a.lg = f.lg;
     a.npass = f.lg / 2;
     for (int ps = 0; ps < a.npass; ++ps) {
         // radix 4: one factor a pass; radix 2: two, applied in run order
-        a.w0[ps] = W[f.radix == 4 ? ps : 2 * ps];
-        a.w1[ps] = f.radix == 4 ? nullptr : W[2 * ps + 1];
+        const int k0 = f.radix == 4 ? ps : 2 * ps;
+        a.w0[ps] = W[k0];
+        a.ws0[ps] = s[k0].nnz / slabs;
+        a.w1[ps] = f.radix == 4 ? nullptr : W[k0 + 1];
+        a.ws1[ps] = f.radix == 4 ? 0 : s[k0 + 1].nnz / slabs;
     }
     a.rows = kBlockBytes / (4 << a.lg);
     a.batch = batch;
+    a.slabs = slabs;
+    a.ldx = s[0].n_in;
+    a.ldy = s[n - 1].n_out;
     const int64_t blocks = (batch + a.rows - 1) / a.rows;
     if (blocks > 0x7fffffff) return KS_ERR_UNSUPPORTED;
     a.nblocks = static_cast<int>(blocks);
-    const int grid = static_cast<int>(std::min<int64_t>(blocks, std::max(1, num_cus)));
+    // one persistent workgroup a compute unit, the same number on every slab
+    const int64_t per_slab = std::max<int64_t>(1, std::min<int64_t>(blocks, std::max(1, num_cus) / slabs));
+    if (per_slab * slabs > 0x7fffffff) return KS_ERR_UNSUPPORTED;
+    const int grid = static_cast<int>(per_slab * slabs);
     if (xt == kF32 && wt == kF32) return launch_typed<float, float>(a, grid, f.radix, f.desc, X, Y, stream);
     if (xt == kF32 && wt == kBF16) return launch_typed<float, bf16_t>(a, grid, f.radix, f.desc, X, Y, stream);
     return launch_typed<bf16_t, bf16_t>(a, grid, f.radix, f.desc, X, Y, stream);
 }
 
-int resident_chain_describe(const Shape* s, int n, char* buf, size_t len) {
+ks_status_t launch_resident_chain(const Shape* s, int n, int xt, int wt, const void* const* W, const void* X,
+                                  float* Y, int64_t batch, hipStream_t stream, int num_cus) {
+    return launch_resident_slabs(s, n, 1, xt, wt, W, X, Y, batch, stream, num_cus);
+}
+
+int resident_chain_describe(const Shape* s, int n, int slabs, char* buf, size_t len) {
     Form f{};
-    if (!form_of(s, n, &f)) return -1;
+    if (!form_of(s, n, slabs, &f)) return -1;
+    char where[64] = "";
+    if (slabs > 1) std::snprintf(where, sizeof(where), " on each of %d slabs of %d values", slabs, 1 << f.lg);
     std::snprintf(buf, len,
-                  "register-resident butterfly: %d radix-%d factors in %d passes (%s), weights in registers, "
+                  "register-resident butterfly%s: %d radix-%d factors in %d passes (%s), weights in registers, "
                   "rows/block=%d, lds=%d, one persistent workgroup of %d threads per CU",
-                  n, f.radix, f.lg / 2, f.desc ? "descending" : "ascending", kBlockBytes / (4 << f.lg), kLdsBytes,
-                  kThreads);
+                  where, n, f.radix, f.lg / 2, f.desc ? "descending" : "ascending", kBlockBytes / (4 << f.lg),
+                  kLdsBytes, kThreads);
     return 0;
 }
 

@@ -424,6 +424,10 @@ ks_status_t launch_row_chain(const Shape* s, int n, int xt, int wt, const void* 
     const bool whole_rows = rt.P == 1 && rt.Q == 1;
     if (whole_rows && resident_chain_supports(s, n, xt, wt) && resident_chain_aligned(X, Y))
         return launch_resident_chain(s, n, xt, wt, W, X, Y, batch, stream, num_cus);
+    // slabs that each carry a whole radix-2/4 butterfly of 1024 or 4096 values
+    int rslabs = 0;
+    if (!whole_rows && rt.Q == 1 && resident_slab_form(s, n, xt, wt, &rslabs) && resident_chain_aligned(X, Y))
+        return launch_resident_slabs(s, n, rslabs, xt, wt, W, X, Y, batch, stream, num_cus);
     if (whole_rows && digit_chain_supports(s, n, xt, wt))
         return launch_digit_chain(s, n, xt, wt, W, X, Y, batch, stream);
     RowChainArgs args{};
@@ -476,7 +480,10 @@ int row_chain_describe(const Shape* s, int n, char* buf, size_t len) {
     RunTile rt;
     if (!run_tile(s, n, &rt)) return std::snprintf(buf, len, "row-resident chain: unsupported");
     const bool whole_rows = rt.P == 1 && rt.Q == 1;
-    if (whole_rows && resident_chain_supports(s, n, kF32, kF32)) return resident_chain_describe(s, n, buf, len);
+    if (whole_rows && resident_chain_supports(s, n, kF32, kF32)) return resident_chain_describe(s, n, 1, buf, len);
+    int rslabs = 0;
+    if (!whole_rows && rt.Q == 1 && resident_slab_form(s, n, kF32, kF32, &rslabs))
+        return resident_chain_describe(s, n, rslabs, buf, len);
     if (whole_rows && digit_chain_supports(s, n, kF32, kF32)) return digit_chain_describe(s, n, buf, len);
     const int pitch = row_pitch(rt);
     const int nbuf = runs_in_place(s, n) ? 1 : 2;

@@ -303,7 +303,7 @@ def test_chain_plan_row_resident_runs():
     assert libks.ks_chain_groups(radix2, 100, libks.DTYPE_F32) == [list(range(12))]
     assert libks.ks_chain_groups(radix2, 100, libks.DTYPE_F32, libks.CHAIN_NO_FUSE) == [[k] for k in range(12)]
     wide = [(2 ** k, 2, 2, 2 ** (12 - k)) for k in range(13)]          # n = 8192: two tiled runs
-    assert libks.ks_chain_groups(wide, 100, libks.DTYPE_F32) == [list(range(5)), list(range(5, 13))]
+    assert libks.ks_chain_groups(wide, 100, libks.DTYPE_F32) == [list(range(3)), list(range(3, 13))]
     mixed = [(64, 4, 4, 4), (1, 64, 16, 64), (256, 4, 4, 4), (256, 4, 4, 4)]
     assert libks.ks_chain_groups(mixed, 100, libks.DTYPE_F32) == [[0], [1], [2, 3]]
     big_blocks = [(1, 16, 8, 256), (16, 2, 2, 128), (32, 2, 2, 64)]    # 16 x 8 blocks first
@@ -318,13 +318,18 @@ def test_chain_plan_tiled_runs():
     many consecutive slabs a tile as stay within 256 values; or else into one
     slab and groups of T of its Q index classes (Q divides every d), at most
     1024 values of a row a tile, in runs of at least 32 elements (128-byte
-    lines of fp32); the run ends where no such tile exists."""
+    lines of fp32); the run ends where no such tile exists, or earlier when
+    the rest of the chain is a whole radix-2/4 butterfly on every slab of
+    1024 or 4096 values (the register-resident kernel, one slab's weights a
+    workgroup)."""
     f32 = libks.DTYPE_F32
     radix2 = [(2 ** k, 2, 2, 2 ** (15 - k)) for k in range(16)]      # n = 65,536
-    assert libks.ks_chain_groups(radix2, 4096, f32) == [list(range(5)), list(range(5, 16))]
+    assert libks.ks_chain_groups(radix2, 4096, f32) == [list(range(4)), list(range(4, 16))]
     desc = libks.ks_chain_describe(radix2, 4096, f32)
-    assert "1 slabs x 2048 classes, 32 classes a tile" in desc, desc
-    assert "32 slabs of 2048 values" in desc, desc
+    assert "1 slabs x 4096 classes, 64 classes a tile" in desc, desc
+    assert "register-resident butterfly on each of 16 slabs of 4096 values" in desc, desc
+    # reversed: the resident run first, then the class tile
+    assert libks.ks_chain_groups(radix2[::-1], 4096, f32) == [list(range(12)), list(range(12, 16))]
     radix4 = [(4 ** k, 4, 4, 4 ** (7 - k)) for k in range(8)]         # n = 65,536
     assert libks.ks_chain_groups(radix4, 4096, f32) == [[0, 1], [2, 3, 4, 5, 6, 7]]
     three_slabs = [(3, 2, 2, 4096), (6, 2, 2, 2048), (12, 2, 2, 1024)]

@@ -621,9 +621,15 @@ def test_row_chain_unaligned_rows(bf16):
 # classes of indices (a divisor of every d), a workgroup holding one slab and
 # a group of classes. (patterns, rows, expected launch groups)
 TILED_CHAINS = {
-    # 65,536-point radix-2: 2048 classes in groups of 32, then 32 slabs of 2048
-    "radix2_n65536": (_radix(2, 16), 37, [list(range(5)), list(range(5, 16))]),
-    # 16,384-point radix-4: 1024 classes in groups of 64, then 16 slabs of 1024
+    # 65,536-point radix-2: 4096 classes in groups of 64, then a whole
+    # 4096-point butterfly on each of 16 slabs (register-resident kernel)
+    "radix2_n65536": (_radix(2, 16), 37, [list(range(4)), list(range(4, 16))]),
+    # reversed: the resident slabs first (bf16 X staged), then the classes
+    "radix2_n65536_reversed": (_radix(2, 16)[::-1], 37, [list(range(12)), list(range(12, 16))]),
+    # 16-point butterflies on 1024-value slabs, reading X at 16 slabs
+    "radix2_n16384": (_radix(2, 14), 29, [list(range(4)), list(range(4, 14))]),
+    # 16,384-point radix-4: 1024 classes in groups of 64, then a whole
+    # radix-4 butterfly on each of 16 slabs of 1024
     "radix4_n16384": (_radix(4, 7), 21, [[0, 1], [2, 3, 4, 5, 6]]),
     # three slabs (P = 3), each of 1024 classes taken 128 at a time
     "slabs3_classes1024": ([(3, 2, 2, 4096), (6, 2, 2, 2048), (12, 2, 2, 1024)], 19, [[0, 1, 2]]),
@@ -688,7 +694,7 @@ def test_tiled_hadamard_exact():
     [[1, 1], [1, -1]] blocks) on small integers runs as two tiled launches
     and is exact in fp32: bit for bit the oracle."""
     pats = datagen.hadamard_patterns(14)
-    assert libks.ks_chain_groups(pats, 11, libks.DTYPE_F32) == [list(range(5)), list(range(5, 14))]
+    assert libks.ks_chain_groups(pats, 11, libks.DTYPE_F32) == [list(range(4)), list(range(4, 14))]
     wl = datagen.Workload("hadamard16384", pats, 11, [1.0] * len(pats), 14, x_kind="int8range", w_kind="hadamard")
     X, Ws = datagen.draw(wl)
     Y = libks.chain_matmul(to_dev(X), [to_dev(W) for W in Ws], pats).cpu().numpy()
@@ -1029,7 +1035,7 @@ def test_kslinear_inference_tiled_chain():
     weights."""
     from kronecker_sparse_structured_amd import layer
     pats = _radix(2, 13)
-    assert libks.ks_chain_groups(pats, 21, libks.DTYPE_F32) == [list(range(5)), list(range(5, 13))]
+    assert libks.ks_chain_groups(pats, 21, libks.DTYPE_F32) == [list(range(3)), list(range(3, 13))]
     L = layer.KSLinear(pats, device=DEV, seed=6)
     x_np = np.random.default_rng(13).standard_normal((22, L.n_in), dtype=np.float32)
     x = to_dev(x_np)[1:]
