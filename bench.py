@@ -68,9 +68,9 @@ WORKLOAD_SOURCES = {
     "monarch_n1024": ("ks_monarch.hip",),
     "radix4_n4096": ("ks_resident.hip", "ks_rowchain.hip", "ks_digitchain.hip"),
     "radix2_n1024": ("ks_resident.hip", "ks_rowchain.hip", "ks_digitchain.hip"),
-    "radix2_n65536": ("ks_rowchain.hip",),
-    "radix4_n65536": ("ks_rowchain.hip",),
-    "radix2_n16384": ("ks_rowchain.hip",),
+    "radix2_n65536": ("ks_rowchain.hip", "ks_resident.hip"),
+    "radix4_n65536": ("ks_rowchain.hip", "ks_resident.hip"),
+    "radix2_n16384": ("ks_rowchain.hip", "ks_resident.hip"),
 }
 
 
