@@ -34,7 +34,9 @@ Printed: one JSON line with
   other_configs  (default run only; --headline-only skips it) the other
              configurations timed the same way and summarised: the ViT
              factor, the GPT-2 chain fused and one launch per factor, the
-             butterfly with bf16 inputs, and the 51-pattern square sweep.
+             butterfly with bf16 inputs, the 65,536-point radix-2 and
+             radix-4 butterflies (fused and one launch per factor), and
+             the 51-pattern square sweep.
 """
 from __future__ import annotations
 
@@ -576,7 +578,8 @@ def other_configs(lib, sp, stream, torch, np, datagen, libks) -> dict:
     """The other configurations of the KS workloads, each timed like the
     headline (rotated inputs, back-to-back calls, HIP events), summarised:
     the ViT factor, the GPT-2 chain fused and one launch per factor, the
-    65,536-point butterfly with bf16 inputs and weights, and the 51-pattern
+    65,536-point butterfly with bf16 inputs and weights, the 65,536-point
+    radix-2 and radix-4 butterflies fused and one launch per factor, and the 51-pattern
     square sweep (roofline fraction of each pattern: bytes over 8 TB/s or
     flops over the fp32 matrix peak, whichever takes longer)."""
     out = {}
@@ -602,6 +605,16 @@ def other_configs(lib, sp, stream, torch, np, datagen, libks) -> dict:
                                   "GB/s": round(r["bytes_run"] / r["ms"] / 1e6, 1),
                                   "frac_as_run": frac(r["bytes_run"], r["ms"]),
                                   "frac_vs_fused_minimum": frac(r["bytes_min"], r["ms"])}
+    # butterflies on rows wider than LDS: closure tiles and register-resident slabs
+    for name in ("radix2_n65536", "radix4_n65536"):
+        w = {}
+        for key, flags in (("fused", libks.CHAIN_AUTO), ("one_launch_per_factor", libks.CHAIN_NO_FUSE)):
+            r = time_workload(datagen.get(name), False, flags, lib, sp, stream, torch, np, datagen, libks,
+                              reps=10)
+            w[key] = {"ms": round(r["ms"], 5), "launches": r["launches"],
+                      "frac_as_run": frac(r["bytes_run"], r["ms"]),
+                      "frac_vs_fused_minimum": frac(r["bytes_min"], r["ms"])}
+        out[name] = {"dtype": "f32", **w}
     fr, small, big = [], [], []
     for p in datagen.square_sweep_patterns():
         wl = datagen.get("square_%d_%d_%d_%d" % p)
