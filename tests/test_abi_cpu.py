@@ -330,6 +330,10 @@ def test_chain_plan_tiled_runs():
     assert "register-resident butterfly on each of 16 slabs of 4096 values" in desc, desc
     # reversed: the resident run first, then the class tile
     assert libks.ks_chain_groups(radix2[::-1], 4096, f32) == [list(range(12)), list(range(12, 16))]
+    # the longest resident rest: 12 factors on 4096-value slabs after two, not
+    # 10 on 1024-value slabs after four
+    radix2_16k = [(2 ** k, 2, 2, 2 ** (13 - k)) for k in range(14)]
+    assert libks.ks_chain_groups(radix2_16k, 16384, f32) == [[0, 1], list(range(2, 14))]
     radix4 = [(4 ** k, 4, 4, 4 ** (7 - k)) for k in range(8)]         # n = 65,536
     assert libks.ks_chain_groups(radix4, 4096, f32) == [[0, 1], [2, 3, 4, 5, 6, 7]]
     three_slabs = [(3, 2, 2, 4096), (6, 2, 2, 2048), (12, 2, 2, 1024)]

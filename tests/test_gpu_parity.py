@@ -626,8 +626,9 @@ TILED_CHAINS = {
     "radix2_n65536": (_radix(2, 16), 37, [list(range(4)), list(range(4, 16))]),
     # reversed: the resident slabs first (bf16 X staged), then the classes
     "radix2_n65536_reversed": (_radix(2, 16)[::-1], 37, [list(range(12)), list(range(12, 16))]),
-    # 16-point butterflies on 1024-value slabs, reading X at 16 slabs
-    "radix2_n16384": (_radix(2, 14), 29, [list(range(4)), list(range(4, 14))]),
+    # 16,384-point radix-2: 4096 classes in groups of 256, then a whole
+    # 4096-point butterfly on each of 4 slabs
+    "radix2_n16384": (_radix(2, 14), 29, [[0, 1], list(range(2, 14))]),
     # 16,384-point radix-4: 1024 classes in groups of 64, then a whole
     # radix-4 butterfly on each of 16 slabs of 1024
     "radix4_n16384": (_radix(4, 7), 21, [[0, 1], [2, 3, 4, 5, 6]]),
@@ -694,7 +695,7 @@ def test_tiled_hadamard_exact():
     [[1, 1], [1, -1]] blocks) on small integers runs as two tiled launches
     and is exact in fp32: bit for bit the oracle."""
     pats = datagen.hadamard_patterns(14)
-    assert libks.ks_chain_groups(pats, 11, libks.DTYPE_F32) == [list(range(4)), list(range(4, 14))]
+    assert libks.ks_chain_groups(pats, 11, libks.DTYPE_F32) == [[0, 1], list(range(2, 14))]
     wl = datagen.Workload("hadamard16384", pats, 11, [1.0] * len(pats), 14, x_kind="int8range", w_kind="hadamard")
     X, Ws = datagen.draw(wl)
     Y = libks.chain_matmul(to_dev(X), [to_dev(W) for W in Ws], pats).cpu().numpy()
