@@ -238,25 +238,12 @@ __device__ __forceinline__ void apply_factor(const float* src, float* dst, int p
     apply_any<NT>(src, dst, pitch, nr, a, b, c, d, K, bm);
 }
 
-template <typename TX, typename TW, int MAXBC, int NT>
-__global__ __launch_bounds__(NT) void row_chain_kernel(const TX* __restrict__ X, float* __restrict__ Y,
-                                                             RowChainArgs args) {
-    extern __shared__ __align__(16) float zbuf[];
-    const int pitch = args.pitch;
-    // buffers as offsets from the LDS array itself (a pointer picked from an
-    // array of pointers would lose its address space: generic accesses)
-    const int bufsz = args.inplace ? 0 : args.rows * pitch;
-    const unsigned wg = blockIdx.x;
-    // workgroup: row block, then tile (slab p, classes q0 .. q0 + T - 1)
-    const int tile = static_cast<int>(wg % static_cast<unsigned>(args.ntiles));
-    const int64_t n0 = int64_t(wg / static_cast<unsigned>(args.ntiles)) * args.rows;
-    const int groups_per_slab = args.Q / args.T;
-    const int p = tile / groups_per_slab;
-    const int q0 = (tile - p * groups_per_slab) * args.T;
-    const int nr = static_cast<int>(min(int64_t(args.rows), args.batch - n0));
+// The X tile of rows [n0, n0 + nr) into LDS at z (bf16 widened exactly).
+template <int NT, typename TX>
+__device__ __forceinline__ void load_tile(const TX* __restrict__ X, float* z, const RowChainArgs& args, int64_t n0,
+                                          int nr, int p, int q0) {
     const int t = threadIdx.x;
-
-    // X tile rows into buffer 0 (bf16 widened exactly)
+    const int pitch = args.pitch;
     const TX* xs = X + n0 * args.n_in;
     const int slab_in = p * (args.n_in / args.P);
     if (args.vec_x) {
@@ -265,29 +252,22 @@ __global__ __launch_bounds__(NT) void row_chain_kernel(const TX* __restrict__ X,
             const int r = i / q, j = i - r * q;
             float v[4];
             load4_f32(xs + int64_t(r) * args.n_in + tile_offset(4 * j, slab_in, args.Q, args.T, q0), v);
-            *reinterpret_cast<floatx4_t*>(zbuf + r * pitch + 4 * j) = floatx4_t{v[0], v[1], v[2], v[3]};
+            *reinterpret_cast<floatx4_t*>(z + r * pitch + 4 * j) = floatx4_t{v[0], v[1], v[2], v[3]};
         }
     } else {
         for (int i = t; i < nr * args.tin; i += NT) {
             const int r = i / args.tin, j = i - r * args.tin;
-            zbuf[r * pitch + j] = to_f32(xs[int64_t(r) * args.n_in + tile_offset(j, slab_in, args.Q, args.T, q0)]);
+            z[r * pitch + j] = to_f32(xs[int64_t(r) * args.n_in + tile_offset(j, slab_in, args.Q, args.T, q0)]);
         }
     }
-    __syncthreads();
+}
 
-    for (int f = 0; f < args.nf; ++f) {
-        const int b = args.pat[f][1], c = args.pat[f][2];
-        const int a = args.sub[f][0], d = args.sub[f][1];
-        const BlockMap bm{p * a, args.pat[f][3], args.Q, args.T, q0};
-        const TW* K = static_cast<const TW*>(args.w[f]);
-        const float* src = zbuf + (f & 1) * bufsz;
-        float* dst = zbuf + ((f + 1) & 1) * bufsz;
-        apply_factor<NT, MAXBC>(src, dst, pitch, nr, a, b, c, d, K, bm);
-        __syncthreads();
-    }
-
-    // the last buffer to Y
-    const float* z = zbuf + (args.nf & 1) * bufsz;
+// The Y tile of rows [n0, n0 + nr) from LDS at z.
+template <int NT>
+__device__ __forceinline__ void store_tile(float* __restrict__ Y, const float* z, const RowChainArgs& args,
+                                           int64_t n0, int nr, int p, int q0) {
+    const int t = threadIdx.x;
+    const int pitch = args.pitch;
     float* ys = Y + n0 * args.n_out;
     const int slab_out = p * (args.n_out / args.P);
     if (args.vec_y) {
@@ -304,6 +284,125 @@ __global__ __launch_bounds__(NT) void row_chain_kernel(const TX* __restrict__ X,
             const int r = i / args.tout, j = i - r * args.tout;
             ys[int64_t(r) * args.n_out + tile_offset(j, slab_out, args.Q, args.T, q0)] = z[r * pitch + j];
         }
+    }
+}
+
+template <typename TX, typename TW, int MAXBC, int NT>
+__global__ __launch_bounds__(NT) void row_chain_kernel(const TX* __restrict__ X, float* __restrict__ Y,
+                                                             RowChainArgs args) {
+    extern __shared__ __align__(16) float zbuf[];
+    const int pitch = args.pitch;
+    // buffers as offsets from the LDS array itself (a pointer picked from an
+    // array of pointers would lose its address space: generic accesses)
+    const int bufsz = args.inplace ? 0 : args.rows * pitch;
+    const unsigned wg = blockIdx.x;
+    // workgroup: row block, then tile (slab p, classes q0 .. q0 + T - 1)
+    const int tile = static_cast<int>(wg % static_cast<unsigned>(args.ntiles));
+    const int64_t n0 = int64_t(wg / static_cast<unsigned>(args.ntiles)) * args.rows;
+    const int groups_per_slab = args.Q / args.T;
+    const int p = tile / groups_per_slab;
+    const int q0 = (tile - p * groups_per_slab) * args.T;
+    const int nr = static_cast<int>(min(int64_t(args.rows), args.batch - n0));
+
+    load_tile<NT>(X, zbuf, args, n0, nr, p, q0);
+    __syncthreads();
+
+    for (int f = 0; f < args.nf; ++f) {
+        const int b = args.pat[f][1], c = args.pat[f][2];
+        const int a = args.sub[f][0], d = args.sub[f][1];
+        const BlockMap bm{p * a, args.pat[f][3], args.Q, args.T, q0};
+        const TW* K = static_cast<const TW*>(args.w[f]);
+        const float* src = zbuf + (f & 1) * bufsz;
+        float* dst = zbuf + ((f + 1) & 1) * bufsz;
+        apply_factor<NT, MAXBC>(src, dst, pitch, nr, a, b, c, d, K, bm);
+        __syncthreads();
+    }
+
+    // the last buffer to Y
+    store_tile<NT>(Y, zbuf + (args.nf & 1) * bufsz, args, n0, nr, p, q0);
+}
+
+// Tiles of index classes of a run of square radix-B factors (at most NF of
+// them), when no factor has more (alpha, delta) groups on the
+// tile than the workgroup has threads: a persistent workgroup keeps one
+// tile and walks its row blocks (blockIdx / tiles, + gridDim / tiles, ...),
+// holding the blocks of its group in every factor in registers for the
+// whole launch instead of reading them again for every row block. Factors
+// run in place.
+template <typename TX, typename TW, int B, int NF>
+__global__ __launch_bounds__(kTiledThreads) void tile_chain_persistent_kernel(const TX* __restrict__ X,
+                                                                              float* __restrict__ Y,
+                                                                              RowChainArgs args, int row_blocks) {
+    constexpr int NT = kTiledThreads;
+    extern __shared__ __align__(16) float zbuf[];
+    const int pitch = args.pitch;
+    const int tile = static_cast<int>(blockIdx.x % static_cast<unsigned>(args.ntiles));
+    const int first = static_cast<int>(blockIdx.x / static_cast<unsigned>(args.ntiles));
+    const int step = static_cast<int>(gridDim.x / static_cast<unsigned>(args.ntiles));
+    const int groups_per_slab = args.Q / args.T;
+    const int p = tile / groups_per_slab;
+    const int q0 = (tile - p * groups_per_slab) * args.T;
+
+    // this thread's group in each factor (at most one: groups <= NT), its
+    // rows (all, or every rstep-th when the groups are fewer than threads)
+    // and the group's B x B block
+    float w[NF][B][B];
+    int off[NF], r0[NF], rstep[NF];
+    bool has[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+        has[f] = false;
+        off[f] = 0;
+        r0[f] = 0;
+        rstep[f] = 1;
+        if (f < args.nf) {
+            const int a = args.sub[f][0], d = args.sub[f][1];
+            ItemMap m;
+            if (item_map<NT>(a * d, &m) && m.g0 < a * d) {
+                const int alpha = m.g0 / d, delta = m.g0 - alpha * d;
+                const BlockMap bm{p * a, args.pat[f][3], args.Q, args.T, q0};
+                const TW* kp = static_cast<const TW*>(args.w[f]) + bm.block(alpha, delta) * (B * B);
+#pragma unroll
+                for (int be = 0; be < B; ++be)
+#pragma unroll
+                    for (int gm = 0; gm < B; ++gm) w[f][be][gm] = to_f32(kp[be * B + gm]);
+                has[f] = true;
+                off[f] = alpha * B * d + delta;
+                r0[f] = m.r0;
+                rstep[f] = m.rstep;
+            }
+        }
+    }
+
+    for (int rb = first; rb < row_blocks; rb += step) {
+        const int64_t n0 = int64_t(rb) * args.rows;
+        const int nr = static_cast<int>(min(int64_t(args.rows), args.batch - n0));
+        __syncthreads();                          // the previous block's stores have read the tile
+        load_tile<NT>(X, zbuf, args, n0, nr, p, q0);
+        __syncthreads();
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            if (f < args.nf) {
+                if (has[f]) {
+                    const int d = args.sub[f][1];
+                    float* z = zbuf + off[f];
+                    for (int r = r0[f]; r < nr; r += rstep[f]) {
+                        float x[B];
+#pragma unroll
+                        for (int gm = 0; gm < B; ++gm) x[gm] = z[r * pitch + gm * d];
+#pragma unroll
+                        for (int be = 0; be < B; ++be) {
+                            float acc = 0.0f;
+#pragma unroll
+                            for (int gm = 0; gm < B; ++gm) acc = fmaf(w[f][be][gm], x[gm], acc);
+                            z[r * pitch + be * d] = acc;
+                        }
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        store_tile<NT>(Y, zbuf, args, n0, nr, p, q0);
     }
 }
 
@@ -404,6 +503,32 @@ bool row_chain_supports(const Shape* s, int n, int xt, int wt) {
     return true;
 }
 
+// The persistent form takes class tiles of runs of at most 6 square radix-2
+// factors with no more groups per factor on the tile than threads. Measured
+// (4,096 rows of 65,536, 16,384 of 16,384): radix-2 class launches 0.53 ->
+// 0.43 ms and 0.41 -> 0.37 ms; a radix-4 one (two factors) 0.45 -> 0.52 ms,
+// so radix-4 keeps the per-block form.
+constexpr int kPersistentFactors = 6;
+
+bool persistent_tiles(const Shape* s, int n, const RunTile& rt) {
+    if (rt.Q == 1) return false;          // whole rows and slabs
+    if (n > kPersistentFactors) return false;
+    for (int k = 0; k < n; ++k) {
+        if (s[k].b != 2 || s[k].c != 2) return false;
+        const int64_t groups = int64_t(s[k].a / rt.P) * (s[k].d / rt.Q * rt.T);
+        if (groups > kTiledThreads) return false;
+    }
+    return true;
+}
+
+template <typename TX, typename TW>
+ks_status_t launch_pt(dim3 grid, size_t lds, hipStream_t stream, const void* X, float* Y, const RowChainArgs& args,
+                      int row_blocks) {
+    const TX* x = static_cast<const TX*>(X);
+    return launch_kernel(tile_chain_persistent_kernel<TX, TW, 2, kPersistentFactors>, grid, dim3(kTiledThreads), lds,
+                         stream, x, Y, args, row_blocks);
+}
+
 template <typename TX, typename TW>
 ks_status_t launch_rc(int maxbc, bool tiled, dim3 grid, size_t lds, hipStream_t stream, const void* X, float* Y,
                       const RowChainArgs& args) {
@@ -469,6 +594,18 @@ ks_status_t launch_row_chain(const Shape* s, int n, int xt, int wt, const void* 
     const int64_t blocks = (batch + args.rows - 1) / args.rows * args.ntiles;
     if (blocks > 0x7fffffff) return KS_ERR_UNSUPPORTED;
     const size_t lds = size_t(nbuf) * args.rows * args.pitch * 4;
+    if (persistent_tiles(s, n, rt)) {
+        // three workgroups a compute unit (48 KB of LDS each), the same number on every tile
+        const int row_blocks = static_cast<int>((batch + args.rows - 1) / args.rows);
+        const int64_t per_tile =
+            std::max<int64_t>(1, std::min<int64_t>(row_blocks, int64_t(3) * std::max(1, num_cus) / args.ntiles));
+        const dim3 pgrid(static_cast<unsigned>(per_tile * args.ntiles));
+        if (xt == kF32 && wt == kF32) return launch_pt<float, float>(pgrid, lds, stream, X, Y, args, row_blocks);
+        if (xt == kBF16 && wt == kBF16)
+            return launch_pt<bf16_t, bf16_t>(pgrid, lds, stream, X, Y, args, row_blocks);
+        if (xt == kF32 && wt == kBF16) return launch_pt<float, bf16_t>(pgrid, lds, stream, X, Y, args, row_blocks);
+        return KS_ERR_UNSUPPORTED;
+    }
     const dim3 grid(static_cast<unsigned>(blocks));
     if (xt == kF32 && wt == kF32) return launch_rc<float, float>(maxbc, !whole_rows, grid, lds, stream, X, Y, args);
     if (xt == kBF16 && wt == kBF16) return launch_rc<bf16_t, bf16_t>(maxbc, !whole_rows, grid, lds, stream, X, Y, args);
@@ -499,8 +636,9 @@ int row_chain_describe(const Shape* s, int n, char* buf, size_t len) {
                              nbuf * rows * pitch * 4);
     return std::snprintf(buf, len,
                          "tile-resident chain: %d factors, %d slabs x %d classes, %d classes a tile, rows/wg=%d, "
-                         "tile pitch %d floats, %s, lds=%d",
+                         "tile pitch %d floats, %s%s, lds=%d",
                          n, rt.P, rt.Q, rt.T, rows, pitch, nbuf == 1 ? "in place" : "two buffers",
+                         persistent_tiles(s, n, rt) ? ", persistent (weights in registers)" : "",
                          nbuf * rows * pitch * 4);
 }
 
