@@ -76,10 +76,16 @@ WORKLOAD_SOURCES = {
 }
 
 
+# single factors of the square sweep: the kernels the planner picks among
+SQUARE_SOURCES = ("ks_mfma.hip", "ks_valu.hip", "ks_col.hip", "ks_generic.hip")
+
+
 def kernel_source_hash(workload: str = "", no_fuse: bool = False) -> str:
     csrc = os.path.join(ROOT, "kronecker_sparse_structured_amd", "csrc")
     names = sorted(os.listdir(csrc))
     used = WORKLOAD_SOURCES.get(workload + (":nofuse" if no_fuse else ""), WORKLOAD_SOURCES.get(workload))
+    if used is None and workload.startswith("square_"):
+        used = SQUARE_SOURCES
     if used is not None:
         names = [n for n in names if n.endswith(".h") or n == "ks_api.cpp" or n in used]
     h = hashlib.sha256()
