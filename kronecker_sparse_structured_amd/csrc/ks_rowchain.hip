@@ -18,8 +18,8 @@
 // * Z[r][alpha][gamma][delta] to the other buffer. Consecutive threads take
 // consecutive delta, so LDS reads and writes of a wave are consecutive words
 // when d >= 64 (strided by c or b words when d is small). A factor's
-// weights (at most 64 KB here) are read once per workgroup, from the L2
-// cache after the first. fp32 accumulation; intermediates are fp32 (bf16 X
+// weights (at most 64 KB a workgroup) are read once per workgroup, from the
+// L2 cache after the first. fp32 accumulation; intermediates are fp32 (bf16 X
 // and weights are widened exactly).
 //
 // Rows wider than the LDS allows are cut by the closure of the run. Factor
@@ -34,9 +34,18 @@
 // tile element e*T + t is slab element e*Q + q0 + t, so on the tile each
 // factor is again a KS factor, (a/P, b, c, (d/Q)*T), whose block
 // (alpha', delta'') is K[p*(a/P) + alpha'][(delta''/T)*Q + q0 + delta''%T].
-// X and Y move in runs of T elements. When whole slabs fit, a tile is the
-// fewest consecutive slabs that do (P taken as a smaller divisor, Q = T = 1):
-// one contiguous run, on which each factor is (a/P, b, c, d).
+// X and Y move in runs of T elements. When a whole slab fits, a tile is
+// instead consecutive slabs, as many as stay within a small width (P taken
+// as a smaller divisor, Q = T = 1): one contiguous run, on which each factor
+// is (a/P, b, c, d). The tile choice is run_tile below.
+//
+// Square factors run in place in one LDS buffer. Class tiles of short
+// radix-2 runs take a persistent form that keeps each thread's blocks in
+// registers across row blocks (tile_chain_persistent_kernel). Runs that are
+// a whole radix-2/4 butterfly on every slab of 1024 or 4096 values, and
+// whole-row butterflies, go to the register-resident kernel
+// (ks_resident.hip), and other whole-row power-of-two runs to the
+// digit-pass kernel (ks_digitchain.hip).
 
 #include <algorithm>
 #include <cstdio>
